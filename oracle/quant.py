@@ -1,0 +1,230 @@
+"""Oracle: latent-cache quantisers and page layouts.  Test infrastructure only.
+
+[Report] §3.2 compares quantisation schemes for the 512-wide latent and the
+64-wide RoPE key; §4.1 keeps two of them: INT8 with one scale per 32-element
+block, and asymmetric INT4 with a scale and a zero point per 32-element block.
+The RoPE key is kept as INT8 in 8-element blocks.  The page does not fix the
+arithmetic; the readings taken here (each one quantises a single appended token
+by itself, so append can be done token by token) are:
+
+  INT8 (symmetric, group of g consecutive channels of one token):
+      amax  = max |x|                       (float32; exact from bf16)
+      scale = amax / 127                    (IEEE float32 division, RNE)
+      code  = clamp(rint(x / scale), -127, 127), rint = round half to even
+      amax == 0  ->  scale = 0, codes 0;    dequant: code * scale (float32)
+  INT4 (asymmetric, group of 32):
+      mn, mx = min x, max x
+      scale = (mx - mn) / 15                (float32)
+      zero  = mn
+      q     = clamp(rint((x - mn) / scale), 0, 15);  scale == 0 -> q = 0
+      dequant: q * scale + zero (float32, two roundings)
+      byte j of a token holds element 2j in bits 0-3 and 2j+1 in bits 4-7.
+
+Every step is evaluated in numpy float32 with float32 constants, so the codes and
+scales are defined bit for bit; the GPU's quantise-on-append must reproduce them
+exactly.
+
+Page layouts (64 tokens a page, bytes):
+  bf16 : [64][576] bf16 (latent 0..511 then RoPE key 512..575)        73,728
+  int8 : [64][576] int8 codes | [64][16] f32 latent scales
+         | [64][8] f32 RoPE-key scales                                 43,008
+  int4 : [64][256] packed latent nibbles | [64][64] int8 RoPE-key codes
+         | [64][16] f32 scales | [64][16] f32 zeros
+         | [64][8] f32 RoPE-key scales                                 30,720
+
+Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
+INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
+unclamped element is at most half a step; zero groups round-trip exactly;
+the rounding rule is checked on hand-made ties; page bytes round-trip through
+unpack_page.  The page's own error figures need the real latents and are not
+reproduced ("parity unpinned" for those numbers).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 64
+D_C = 512
+D_R = 64
+G_C = 32      # latent channels per group
+G_R = 8       # RoPE-key channels per group
+
+CACHE_BF16, CACHE_INT8, CACHE_INT4 = 0, 1, 2
+_F127 = np.float32(127.0)
+_F15 = np.float32(15.0)
+
+
+def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def quant_int8_sym(x_bits: np.ndarray, group: int):
+    """Symmetric INT8 per group of `group` consecutive channels of each row.
+
+    x_bits [..., C] bf16 bits -> codes int8 [..., C], scales float32 [..., C/group]
+    """
+    x = _bf16_to_f32(x_bits)
+    shp = x.shape
+    xg = x.reshape(shp[:-1] + (shp[-1] // group, group))
+    amax = np.max(np.abs(xg), axis=-1)                         # float32
+    scale = (amax / _F127).astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    q = np.rint((xg / safe[..., None]).astype(np.float32))
+    q = np.clip(q, -127, 127)
+    q = np.where(scale[..., None] == 0, 0, q)
+    return q.astype(np.int8).reshape(shp), scale
+
+
+def dequant_int8(codes: np.ndarray, scales: np.ndarray, group: int) -> np.ndarray:
+    shp = codes.shape
+    cg = codes.astype(np.float32).reshape(shp[:-1] + (shp[-1] // group, group))
+    return (cg * scales[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
+
+
+def quant_int4_asym(x_bits: np.ndarray, group: int = G_C):
+    """Asymmetric INT4 per group: returns q uint8 [..., C] (0..15), scale, zero float32."""
+    x = _bf16_to_f32(x_bits)
+    shp = x.shape
+    xg = x.reshape(shp[:-1] + (shp[-1] // group, group))
+    mn = np.min(xg, axis=-1)
+    mx = np.max(xg, axis=-1)
+    scale = (mx - mn).astype(np.float32) / _F15
+    scale = scale.astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    d = (xg - mn[..., None]).astype(np.float32)
+    q = np.rint((d / safe[..., None]).astype(np.float32))
+    q = np.clip(q, 0, 15)
+    q = np.where(scale[..., None] == 0, 0, q)
+    return q.astype(np.uint8).reshape(shp), scale, mn.astype(np.float32)
+
+
+def dequant_int4(q: np.ndarray, scale: np.ndarray, zero: np.ndarray, group: int = G_C) -> np.ndarray:
+    shp = q.shape
+    qg = q.astype(np.float32).reshape(shp[:-1] + (shp[-1] // group, group))
+    prod = (qg * scale[..., None].astype(np.float32)).astype(np.float32)
+    return (prod + zero[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """[..., 2n] values 0..15 -> [..., n] bytes: element 2j low nibble, 2j+1 high."""
+    q = q.astype(np.uint8)
+    return (q[..., 0::2] | (q[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = b & np.uint8(0x0F)
+    out[..., 1::2] = b >> np.uint8(4)
+    return out
+
+
+def token_bytes(dtype: int) -> int:
+    """Cache bytes per token including scales and zero points."""
+    return {CACHE_BF16: 576 * 2,
+            CACHE_INT8: 576 + (D_C // G_C) * 4 + (D_R // G_R) * 4,
+            CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4}[dtype]
+
+
+def page_bytes(dtype: int) -> int:
+    return BLOCK * token_bytes(dtype)
+
+
+def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
+    """Quantise (or copy) n token rows into their per-field arrays."""
+    if dtype == CACHE_BF16:
+        return {"rows": np.concatenate([c_bits, r_bits], axis=-1).astype(np.uint16)}
+    rc, rs = quant_int8_sym(r_bits, G_R)
+    if dtype == CACHE_INT8:
+        cc, cs = quant_int8_sym(c_bits, G_C)
+        return {"codes": np.concatenate([cc, rc], axis=-1), "c_scale": cs, "r_scale": rs}
+    q, s, z = quant_int4_asym(c_bits, G_C)
+    return {"nib": pack_nibbles(q), "r_codes": rc, "c_scale": s, "c_zero": z, "r_scale": rs}
+
+
+def pack_page(dtype: int, fields: dict) -> np.ndarray:
+    """Lay out the fields of up to 64 tokens as one page (uint8 [page_bytes]).
+
+    Slots beyond the tokens given are zero.
+    """
+    out = np.zeros(page_bytes(dtype), np.uint8)
+
+    def put(off, arr, width):
+        a = np.ascontiguousarray(arr).view(np.uint8).reshape(-1, width)
+        out[off: off + a.size] = a.reshape(-1)
+        return off + BLOCK * width
+
+    if dtype == CACHE_BF16:
+        put(0, fields["rows"], 1152)
+    elif dtype == CACHE_INT8:
+        off = put(0, fields["codes"], 576)
+        off = put(off, fields["c_scale"], 64)
+        put(off, fields["r_scale"], 32)
+    else:
+        off = put(0, fields["nib"], 256)
+        off = put(off, fields["r_codes"], 64)
+        off = put(off, fields["c_scale"], 64)
+        off = put(off, fields["c_zero"], 64)
+        put(off, fields["r_scale"], 32)
+    return out
+
+
+def unpack_page(dtype: int, page: np.ndarray) -> dict:
+    """Inverse of pack_page for all 64 slots."""
+    page = np.asarray(page, np.uint8)
+
+    def get(off, width, dt, cols):
+        raw = page[off: off + BLOCK * width].copy()
+        return raw.view(dt).reshape(BLOCK, cols), off + BLOCK * width
+
+    if dtype == CACHE_BF16:
+        rows, _ = get(0, 1152, np.uint16, 576)
+        return {"rows": rows}
+    if dtype == CACHE_INT8:
+        codes, off = get(0, 576, np.int8, 576)
+        cs, off = get(off, 64, np.float32, 16)
+        rs, _ = get(off, 32, np.float32, 8)
+        return {"codes": codes, "c_scale": cs, "r_scale": rs}
+    nib, off = get(0, 256, np.uint8, 256)
+    rc, off = get(off, 64, np.int8, 64)
+    cs, off = get(off, 64, np.float32, 16)
+    cz, off = get(off, 64, np.float32, 16)
+    rs, _ = get(off, 32, np.float32, 8)
+    return {"nib": nib, "r_codes": rc, "c_scale": cs, "c_zero": cz, "r_scale": rs}
+
+
+def dequant_fields(dtype: int, f: dict):
+    """Fields of n tokens -> (c [n,512], r [n,64]) float32 values the decode reads."""
+    if dtype == CACHE_BF16:
+        rows = _bf16_to_f32(f["rows"])
+        return rows[..., :D_C], rows[..., D_C:]
+    if dtype == CACHE_INT8:
+        c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C)
+        r = dequant_int8(f["codes"][..., D_C:], f["r_scale"], G_R)
+        return c, r
+    c = dequant_int4(unpack_nibbles(f["nib"]), f["c_scale"], f["c_zero"], G_C)
+    r = dequant_int8(f["r_codes"], f["r_scale"], G_R)
+    return c, r
+
+
+def pack_pool(dtype: int, num_pages: int, seqs) -> np.ndarray:
+    """Build a whole pool from (c_bits [L,512], r_bits [L,64], block_table_row) triples."""
+    pool = np.zeros((num_pages, page_bytes(dtype)), np.uint8)
+    for c_bits, r_bits, bt_row in seqs:
+        L = c_bits.shape[0]
+        for p0 in range(0, L, BLOCK):
+            n = min(BLOCK, L - p0)
+            f = encode_tokens(dtype, c_bits[p0:p0 + n], r_bits[p0:p0 + n])
+            pool[int(bt_row[p0 // BLOCK])] = pack_page(dtype, f)
+    return pool
+
+
+def dequant_pool_seq(dtype: int, pool: np.ndarray, bt_row: np.ndarray, L: int):
+    """Read one sequence back from a packed pool: (c [L,512], r [L,64]) float64."""
+    cs, rs = [], []
+    for p0 in range(0, L, BLOCK):
+        n = min(BLOCK, L - p0)
+        f = unpack_page(dtype, pool[int(bt_row[p0 // BLOCK])])
+        c, r = dequant_fields(dtype, f)
+        cs.append(c[:n])
+        rs.append(r[:n])
+    return (np.concatenate(cs).astype(np.float64), np.concatenate(rs).astype(np.float64))
