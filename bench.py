@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Absorbed-latent MLA decode benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload v3_decode] [--cache-dtype bf16]
+
+One step = one pass of the whole decode hot path over one batch, all inputs
+already resident in HBM: append the batch's new tokens (quantising if the cache
+is quantised), absorb W_UK into the queries, split-KV attention over the paged
+latent cache, log-sum-exp combine, W_UV expansion.  Inputs are seeded synthetic
+data with the workload's shapes (no checkpoint or dataset is read).
+
+Prints ONE JSON line.  `value` is the latent-cache bytes the step attends over
+divided by the step time (GB/s).  `roofline` is for the dominant kernel,
+mla_decode_attn, timed alone with HIP events on the stream it runs on;
+`cpu_baseline` times the CPU oracle (fp64, as it stands) on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS_16 = 2500.0   # MI355X dense fp16/bf16 matrix peak, vendor figure
+
+WORKLOADS = {
+    # name: (generator, description)
+    "v3_decode": ("v3_decode", "DeepSeek-V3-shaped absorbed decode: H=128, B=64, 8192 tokens/seq, paged bf16 "
+                               "cache, 64-token pages, shuffled block table"),
+    "v2lite_decode": ("v2lite_decode", "V2-Lite-shaped decode attention: H=16, B=32, 4096 tokens/seq, contiguous"),
+    "v3_ragged": ("v3_ragged", "V3-shaped ragged decode: H=128, B=128, log-uniform lengths in [128, 65536]"),
+    "v2lite_quant": ("v2lite_quant", "quantised latent cache, V2-Lite shapes: H=16, B=64, 16384 tokens/seq"),
+}
+DTYPES = {"bf16": 0, "int8": 1, "int4": 2}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, cache_dtype, budget_s=15.0):
+    """Time the oracle's absorbed decode (fp64 numpy) on whole sequences of the
+    workload until ~budget_s of CPU work; report GB/s of latent cache read."""
+    from oracle import mla_ref, quant
+    wk = mla_ref.bf16_to_f64(case.w_uk)
+    wv = mla_ref.bf16_to_f64(case.w_uv)
+    bpt = quant.token_bytes(cache_dtype)
+    done_tokens, t_total, seqs = 0, 0.0, 0
+    for b in range(case.B):
+        c_bits, r_bits = case.seq_cache(b)
+        if cache_dtype == 0:
+            c, r = mla_ref.bf16_to_f64(c_bits), mla_ref.bf16_to_f64(r_bits)
+            t0 = time.perf_counter()
+        else:
+            t0 = time.perf_counter()
+            f = quant.encode_tokens(cache_dtype, c_bits, r_bits)
+            c32, r32 = quant.dequant_fields(cache_dtype, f)
+            c, r = c32.astype(np.float64), r32.astype(np.float64)
+        mla_ref.absorbed_decode(mla_ref.bf16_to_f64(case.q_nope[b]), mla_ref.bf16_to_f64(case.q_pe[b]),
+                                c, r, wk, wv, case.softmax_scale)
+        t_total += time.perf_counter() - t0
+        done_tokens += int(case.seq_lens[b])
+        seqs += 1
+        if t_total >= budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(done_tokens * bpt / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of %d sequences (%d tokens), fp64 numpy absorbed decode incl. W_UK/W_UV, %.1f s"
+                      % (seqs, case.B, done_tokens, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--cache-dtype", default="bf16", choices=sorted(DTYPES))
+    ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by sequence "
+              "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_synth
+    from mla_absorbed_latent_amd import api
+    from mla_absorbed_latent_amd.runner import DecodeRunner
+
+    gen, desc = WORKLOADS[args.workload]
+    case = getattr(mla_synth, gen)()
+    cache_dtype = DTYPES[args.cache_dtype]
+    dev = torch.device("cuda:0")
+    cfg = api.config(case.H, cache_dtype, case.softmax_scale)
+    run = DecodeRunner(cfg, case.B, case.num_pages, dev)
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- fill the cache through the library (bulk append), then the step's inputs
+    t0 = time.time()
+    last_c, last_r, last_s = [], [], []
+    pend = ([], [], [])
+    n_pend = 0
+    for b in range(case.B):
+        c, r = case.seq_cache(b)
+        s = case.slots_of(b)
+        pend[0].append(c)
+        pend[1].append(r)
+        pend[2].append(s)
+        n_pend += len(s)
+        last_c.append(c[-1])
+        last_r.append(r[-1])
+        last_s.append(s[-1])
+        if n_pend >= (1 << 19) or b == case.B - 1:
+            run.append(bits(np.concatenate(pend[0])), bits(np.concatenate(pend[1])),
+                       torch.from_numpy(np.concatenate(pend[2])).to(dev))
+            pend = ([], [], [])
+            n_pend = 0
+    new_c = bits(np.stack(last_c))
+    new_r = bits(np.stack(last_r))
+    new_s = torch.from_numpy(np.array(last_s, np.int64)).to(dev)
+    q_nope, q_pe = bits(case.q_nope), bits(case.q_pe)
+    w_uk, w_uv = bits(case.w_uk), bits(case.w_uv)
+    block_table = torch.from_numpy(case.block_table).to(dev)
+    seq_lens = torch.from_numpy(case.seq_lens.astype(np.int32)).to(dev)
+    n_items = run.plan(case.seq_lens, chunk_pages=args.chunk_pages)
+    torch.cuda.synchronize()
+    log("setup %.1f s: %s, %d tokens, %d work items" % (time.time() - t0, desc, case.total_tokens, n_items))
+
+    def step():
+        run.step(q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c, new_r, new_s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- the dominant kernel alone: mla_decode_attn, events on its own stream
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    run.absorb(q_nope, q_pe, w_uk)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        run.attend(block_table, seq_lens)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    # combine alone (for t_attn = decode_attn + combine)
+    ev0.record()
+    for _ in range(args.steps):
+        run.combine()
+    ev1.record()
+    torch.cuda.synchronize()
+    comb_ms = ev0.elapsed_time(ev1) / args.steps
+
+    bpt = api.cache_bytes_per_token(cfg)
+    latent_bytes = case.total_tokens * bpt
+    flops = 2176.0 * case.H * case.total_tokens
+    attn_gbs = latent_bytes / (attn_ms * 1e-3) / 1e9
+    step_gbs = latent_bytes / (ms_step * 1e-3) / 1e9
+    t_attn_ms = attn_ms + comb_ms
+    roof_t = max(latent_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS_16 * 1e12))
+
+    line = {
+        "metric": "MLA absorbed decode: latent-cache GB/s, TFLOP/s, % roofline (H=128, B=64)",
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if cache_dtype == 0 else ("i8/f16" if cache_dtype == 1 else "i4/f16"),
+        "data": "synthetic (seeded; shapes and distributions of the workload, no checkpoint)",
+        "config": {"workload": args.workload, "description": desc, "batch": case.B, "heads": case.H,
+                   "cached_tokens": case.total_tokens, "cache_dtype": args.cache_dtype,
+                   "work_items": n_items, "page_tokens": 64},
+        "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "tokens_per_s": round(case.B / (ms_step * 1e-3), 1),
+        "t_attn_ms": round(t_attn_ms, 5),
+        "attn_gbs": round(latent_bytes / (t_attn_ms * 1e-3) / 1e9, 2),
+        "attn_tflops": round(flops / (t_attn_ms * 1e-3) / 1e12, 2),
+        "pct_roofline_attn": round(100.0 * roof_t / (t_attn_ms * 1e-3), 2),
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_attn", "achieved": round(attn_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_ms": round(attn_ms, 5),
+                     "bytes_per_launch": latent_bytes,
+                     "mfma_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline(case, cache_dtype)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

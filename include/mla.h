@@ -1,0 +1,224 @@
+/*
+ * mla.h -- C ABI of the absorbed-latent MLA decode library for AMD MI355X (gfx950).
+ *
+ * Multi-head Latent Attention caches, per token and layer, a 512-wide latent
+ * c_kv and a 64-wide decoupled RoPE key k_pe (576 elements, 1,152 B in bf16).
+ * Decode folds each head's W_UK into its query, attends to the shared latent as
+ * one "KV head" of width 576 (scores) / 512 (values), merges split partials with
+ * a log-sum-exp combine, and expands the 512-wide result through W_UV.
+ *
+ * Sources cited below by key:
+ *   [Audit]    "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界"
+ *   [Report]   "DeepSeek-V2-Lite MLA 吸收式 KV 缓存优化 — 完整实验报告"
+ *   [Tutorial] "手搓 MLA:从 MHA 到 weight absorption,看懂 DeepSeek 的 KV 压缩"
+ *   [Budget]   "kv_budget.py" (TileLang tutorial, "算子实战 IV：MoE 与 MLA")
+ *
+ * Conventions shared by every call
+ *   - All tensors are caller-owned device memory, passed as raw pointers; the
+ *     library never allocates, frees or copies on the host's behalf, and never
+ *     synchronises the stream.  Every call is asynchronous on `stream`
+ *     (a hipStream_t; NULL is the default stream).  Inputs are never modified.
+ *   - bf16 and fp16 tensors are passed as uint16_t bit patterns.
+ *   - Device pointers must be 16-byte aligned (MLA_ERR_ALIGN otherwise).
+ *   - Host-visible arguments are validated before anything is launched, so a
+ *     call that returns an error has had no effect.  A failed launch returns
+ *     MLA_ERR_HIP; mla_last_hip_error() then holds the hipError_t (per thread).
+ *   - The first call that launches work checks that the current device is
+ *     gfx950 and returns MLA_ERR_UNSUPPORTED otherwise.
+ *   - Device-resident indices (slot_mapping, block_table, work items) cannot be
+ *     checked on the host without a sync; kernels bounds-check them and skip
+ *     what is out of range instead of faulting.
+ *   - Calls on one stream are ordered; the library keeps no state between calls
+ *     except the per-thread last HIP error and a per-device architecture flag.
+ */
+#ifndef MLA_ABSORBED_LATENT_H
+#define MLA_ABSORBED_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MLA_ERR_SHAPE = 2,       /* unsupported head count / widths / block size        */
+  MLA_ERR_VALUE = 3,       /* a size or scalar argument is out of range           */
+  MLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned             */
+  MLA_ERR_WORKSPACE = 5,   /* a caller buffer is too small (planner capacity)     */
+  MLA_ERR_UNSUPPORTED = 6, /* the current device is not gfx950                    */
+  MLA_ERR_HIP = 7          /* a HIP call or launch failed                         */
+} mla_status;
+
+/* Latent-cache formats ([Report] §3.2 and §4.1). */
+typedef enum {
+  MLA_CACHE_BF16 = 0,  /* c_kv and k_pe in bf16                                       */
+  MLA_CACHE_INT8 = 1,  /* c_kv INT8, one fp32 scale per 32 channels; k_pe INT8 per 8   */
+  MLA_CACHE_INT4 = 2   /* c_kv asymmetric INT4, fp32 scale + zero per 32; k_pe INT8    */
+} mla_cache_dtype;
+
+/* Shape of one MLA layer.  Supported: num_heads in {16, 128}, qk_nope_dim = 128,
+ * kv_lora_rank = 512, rope_dim = 64, v_head_dim = 128, block_size = 64; any
+ * other value gives MLA_ERR_SHAPE.  softmax_scale must be finite and > 0
+ * (1/sqrt(qk_nope_dim + rope_dim) for DeepSeek shapes). */
+typedef struct {
+  int32_t num_heads;
+  int32_t qk_nope_dim;
+  int32_t kv_lora_rank;
+  int32_t rope_dim;
+  int32_t v_head_dim;
+  int32_t block_size;
+  int32_t cache_dtype;   /* mla_cache_dtype */
+  float softmax_scale;
+} mla_config;
+
+/* One unit of split-KV work: pages [first_page, first_page + n_pages) of
+ * sequence `seq` (logical page numbers, i.e. indices into its block-table row);
+ * the partial result is written to row `out_row` of o_part / lse_part. */
+typedef struct {
+  int32_t seq;
+  int32_t first_page;
+  int32_t n_pages;
+  int32_t out_row;
+} mla_work_item;
+
+/* ------------------------------------------------------------------ sizes
+ * Pure host functions; they return 0 for an invalid config.
+ * Bytes per token include every scale and zero point the decode reads:
+ *   bf16 1,152 ([Audit] §2.4: 576 elements x 2 B), INT8 672, INT4 480.
+ * Page layouts (64 tokens, row = token):
+ *   bf16: [64][576] bf16, latent in 0..511 then RoPE key in 512..575  (73,728 B)
+ *   INT8: [64][576] int8 codes | [64][16] f32 latent scales
+ *         | [64][8] f32 RoPE-key scales                               (43,008 B)
+ *   INT4: [64][256] latent nibbles (element 2j in bits 0-3 of byte j, 2j+1 in
+ *         bits 4-7) | [64][64] int8 RoPE-key codes | [64][16] f32 scales
+ *         | [64][16] f32 zeros | [64][8] f32 RoPE-key scales          (30,720 B)
+ * A pool of N pages is N * mla_cache_page_bytes() contiguous bytes.          */
+mla_status mla_config_check(const mla_config* cfg);
+size_t mla_cache_bytes_per_token(const mla_config* cfg);
+size_t mla_cache_page_bytes(const mla_config* cfg);
+/* o_part (n_items x H x 512 f32) plus lse_part (n_items x H f32), in bytes. */
+size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
+
+/* ------------------------------------------------------------------ a-1
+ * mla_cache_append: write n_tokens new cache rows into their pool slots.
+ * [Audit] §2.4 and §4.1 (only the latent and the RoPE key are cached);
+ * quantise-on-append for the INT8 / INT4 formats of [Report] §3.2.
+ *   pool          device, num_pages * page_bytes, written
+ *   c_kv          device [n_tokens][512] bf16 (post-RMSNorm latent)
+ *   k_pe          device [n_tokens][64] bf16 (post-RoPE key)
+ *   slot_mapping  device [n_tokens] int64, slot = page * 64 + offset; negative
+ *                 or >= num_pages * 64 slots are skipped
+ * INT8: per token, each group of 32 latent channels (8 for k_pe) gets
+ *   scale = max|x| / 127 (IEEE fp32 division) and codes clamp(rint(x/scale),
+ *   -127, 127) (round half to even); max|x| = 0 gives scale 0 and codes 0.
+ * INT4: per group of 32 latent channels, zero = min, scale = (max-min)/15,
+ *   q = clamp(rint((x-min)/scale), 0, 15); scale 0 gives q = 0.
+ * Codes and scales are bit-exact with that definition.
+ * n_tokens == 0 is a no-op; n_tokens < 0 is MLA_ERR_VALUE.                  */
+mla_status mla_cache_append(const mla_config* cfg, void* pool, int64_t num_pages,
+                            const uint16_t* c_kv, const uint16_t* k_pe,
+                            const int64_t* slot_mapping, int32_t n_tokens,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------ a-2
+ * mla_absorb_q: fold W_UK into the query ([Audit] §2.2; [Tutorial] §四,
+ * einsum "thd,hdc->thc"):  q_abs[b,h,0:512] = sum_d q_nope[b,h,d] W_UK[h,d,:],
+ * q_abs[b,h,512:576] = q_pe[b,h,:].
+ *   q_nope  device [batch][H][128] bf16
+ *   q_pe    device [batch][H][64]  bf16 (post-RoPE)
+ *   w_uk    device [H][128][512]   bf16 (index order "hdc")
+ *   q_abs   device [batch][H][576] fp16, written (fp32 accumulation, rounded
+ *           to nearest even)
+ * batch == 0 is a no-op.                                                   */
+mla_status mla_absorb_q(const mla_config* cfg, const uint16_t* q_nope, const uint16_t* q_pe,
+                        const uint16_t* w_uk, uint16_t* q_abs, int32_t batch,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------ planner
+ * mla_plan_splits: host-only, synchronous.  Cuts every sequence's pages into
+ * contiguous runs of about `chunk_pages` pages (chunk_pages <= 0: chosen so the
+ * whole batch makes at least ~num_cus work items), one work item per run.
+ * A sequence with no tokens gets one empty item.  Items are ordered longest
+ * first; out_row = split_offsets[seq] + (index of the run within its sequence).
+ *   seq_lens_host      host [batch] int32, tokens per sequence (>= 0)
+ *   items_host         host [max_items], written
+ *   n_items            host, written
+ *   split_offsets_host host [batch + 1], written (rows of sequence b are
+ *                      split_offsets[b] .. split_offsets[b+1]-1)
+ * MLA_ERR_WORKSPACE when max_items is too small (n_items then holds the
+ * number needed).                                                          */
+mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch,
+                           int32_t num_cus, int32_t chunk_pages, mla_work_item* items_host,
+                           int32_t max_items, int32_t* n_items, int32_t* split_offsets_host);
+
+/* ------------------------------------------------------------------ a-3
+ * mla_decode_attn: split-KV absorbed attention, MQA over the latent
+ * ([Audit] §6.1: key width 576, value width 512; [Tutorial] §四).  For every
+ * work item and head:
+ *   s_t   = softmax_scale * (q_abs[b,h,0:512] . c_t + q_abs[b,h,512:576] . k_pe_t)
+ *   o_j   = sum_t exp(s_t - m) c_t / sum_t exp(s_t - m),  m = max_t s_t
+ *   lse_j = m + ln sum_t exp(s_t - m)             (natural log)
+ * over the item's tokens t (a range of the sequence's first seq_lens[b] tokens).
+ * An empty item gives lse_j = -inf and o_j = 0.  Quantised caches are
+ * dequantised in registers (code * scale; q * scale + zero).
+ *   q_abs        device [batch][H][576] fp16 (from mla_absorb_q)
+ *   pool         device, num_pages pages in the config's format
+ *   block_table  device [batch][max_pages_per_seq] int32 physical page ids;
+ *                ids outside [0, num_pages) make their tokens contribute nothing
+ *   seq_lens     device [batch] int32
+ *   items        device [n_items] (from mla_plan_splits, uploaded by the caller)
+ *   o_part       device [n_items][H][512] f32, lse_part device [n_items][H] f32
+ *                (mla_decode_workspace_bytes(n_items) bytes in all); an item whose
+ *                seq or out_row is out of range is skipped
+ * Numerics: scores and probabilities use fp16 operands on the matrix cores
+ * with fp32 accumulation; the bf16 latent is widened to fp16 exactly (values
+ * beyond +-65504 are not supported); softmax state is fp32.                */
+mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const void* pool,
+                           int64_t num_pages, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* seq_lens,
+                           const mla_work_item* items, int32_t n_items,
+                           float* o_part, float* lse_part, int32_t batch,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------ a-4
+ * mla_decode_combine: exact log-sum-exp merge of each sequence's partials:
+ *   lse = ln sum_j exp(lse_j);  o_lat = sum_j exp(lse_j - lse) o_j.
+ * A sequence whose partials are all empty gets o_lat = 0, lse = -inf.
+ *   split_offsets  device [batch + 1] int32 (from mla_plan_splits)
+ *   o_lat          device [batch][H][512] f32, written
+ *   lse            device [batch][H] f32, written (may be NULL)            */
+mla_status mla_decode_combine(const mla_config* cfg, const float* o_part, const float* lse_part,
+                              const int32_t* split_offsets, float* o_lat, float* lse,
+                              int32_t batch, hipStream_t stream);
+
+/* ------------------------------------------------------------------ a-5
+ * mla_out_proj: expand the latent result through W_UV ([Audit] §2.3;
+ * [Tutorial] §四, einsum "thc,hdc->thd"):
+ *   out[b,h,d] = sum_c W_UV[h,d,c] o_lat[b,h,c]            -> bf16
+ * and optionally the layer output y[b,:] = W_O . concat_h(out[b,h,:]) -> bf16.
+ *   o_lat      device [batch][H][512] f32
+ *   w_uv       device [H][128][512] bf16 ("hdc")
+ *   out        device [batch][H][128] bf16, written
+ *   w_o        device [hidden][H*128] bf16 or NULL (then hidden, y and
+ *              out_f32 are ignored)
+ *   y          device [batch][hidden] bf16, written when w_o != NULL
+ *   out_f32    device [batch][H][128] f32 workspace, required when w_o != NULL:
+ *              receives `out` before its bf16 rounding; y is computed from it
+ * The 512-wide operand is rounded to fp16 for the matrix cores (fp32 sums).  */
+mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const uint16_t* w_uv,
+                        uint16_t* out, const uint16_t* w_o, int32_t hidden, uint16_t* y,
+                        float* out_f32, int32_t batch, hipStream_t stream);
+
+/* ------------------------------------------------------------------ errors */
+const char* mla_status_string(mla_status s);
+int32_t mla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_ABSORBED_LATENT_H */

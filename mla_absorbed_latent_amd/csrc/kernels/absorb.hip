@@ -1,0 +1,95 @@
+// absorb.hip -- fold W_UK into the query ("DeepSeek MLA 吸收式缓存：真实权重执行与
+// FlashMLA 架构边界" §2.2; "手搓 MLA:从 MHA 到 weight absorption" §四, einsum
+// "thd,hdc->thc"):
+//     q_abs[b,h,c]       = sum_d q_nope[b,h,d] * W_UK[h,d,c]     c < 512
+//     q_abs[b,h,512 + r] = q_pe[b,h,r]
+//
+// Per head this is a [B x 128] x [128 x 512] product.  It runs transposed on the
+// bf16 matrix cores (bf16 x bf16 products are exact in the fp32 accumulator):
+//     q_abs^T[c][b] = W_UK[h]^T[c][d] . q_nope^T[d][b]      (mfma 32x32x16 bf16)
+// A work-group owns one head and 128 latent columns.  W_UK[h][:, c0:c0+128] is
+// staged row-major in LDS and read transposed (ds_read_b64_tr_b16), so every
+// lane gets 8 consecutive d for its column c; q_nope rows come straight from
+// HBM as 16-byte loads.  The result is rounded to fp16 (round to nearest even)
+// and stored 4 consecutive columns at a time.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kSlab = 128;                       // latent columns per work-group
+constexpr int kWRow = kSlab * 2;                 // 256 B per LDS row (one d)
+
+__global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
+                                                       const uint16_t* __restrict__ q_pe,
+                                                       const uint16_t* __restrict__ w_uk,
+                                                       uint16_t* __restrict__ q_abs, int H, int B) {
+  __shared__ __attribute__((aligned(16))) char lds[kDn * kWRow];     // 32 KB
+  const int h = blockIdx.x / (kDc / kSlab);
+  const int c0 = (blockIdx.x % (kDc / kSlab)) * kSlab;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // Stage W_UK[h][0:128][c0:c0+128]: 128 rows x 16 chunks of 16 B.
+  const uint16_t* wsrc = w_uk + (int64_t)h * kDn * kDc + c0;
+  for (int i = threadIdx.x; i < kDn * 16; i += 256) {
+    const int d = i >> 4, ch = i & 15;
+    *reinterpret_cast<u32x4*>(lds + d * kWRow + 16 * (ch ^ (d & 7))) = ld16(wsrc + (int64_t)d * kDc + 8 * ch);
+  }
+  // q_pe passthrough (bf16 -> fp16 is exact in range), done by the first slab.
+  if (c0 == 0) {
+    for (int i = threadIdx.x; i < B * 8; i += 256) {
+      const int b = i >> 3, ch = i & 7;
+      const u32x4 v = ld16(q_pe + ((int64_t)b * H + h) * kDr + 8 * ch);
+      st16(q_abs + ((int64_t)b * H + h) * kDk + kDc + 8 * ch, bf16x8_to_f16x8(v));
+    }
+  }
+  __syncthreads();
+
+  const int g = lane >> 5, grp = lane >> 4, gi = lane & 15;
+  // Transposed read: group lane gi addresses row (d) d0 + (gi >> 2), columns
+  // 16 (grp & 1) + 4 (gi & 3) of this wave's 32-column block.
+  const int cw = 32 * wave;                            // wave's columns within the slab
+  const int colh = cw + 16 * (grp & 1) + 4 * (gi & 3);  // in halves
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    const int b = b0 + (lane & 31);
+    const bool bok = b < B;
+    floatx16 acc = floatx16{};
+    const uint16_t* qrow = q_nope + ((int64_t)(bok ? b : 0) * H + h) * kDn + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) {
+      u32x4 qv = bok ? ld16(qrow + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+      const int d = 16 * ks + 8 * g + (gi >> 2);
+      const int ch = colh >> 3;
+      const uint32_t off_lo = d * kWRow + 16 * (ch ^ (d & 7)) + 2 * (colh & 7);
+      const int d4 = d + 4;
+      const uint32_t off_hi = d4 * kWRow + 16 * (ch ^ (d4 & 7)) + 2 * (colh & 7);
+      const half4 lo = lds_read_tr(lds, off_lo);
+      const half4 hi = lds_read_tr(lds, off_hi);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = mfma32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qv), acc);
+    }
+    if (bok) {
+      uint16_t* dst = q_abs + ((int64_t)b * H + h) * kDk + c0 + cw + 4 * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 v;
+        v[0] = (uint32_t)f32_to_f16_bits(acc[4 * rr]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 1]) << 16);
+        v[1] = (uint32_t)f32_to_f16_bits(acc[4 * rr + 2]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 3]) << 16);
+        *reinterpret_cast<u32x2*>(dst + 8 * rr) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_absorb_q(int num_heads, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk,
+                           uint16_t* q_abs, int batch, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(num_heads * (kDc / kSlab)), dim3(256), 0, stream, q_nope, q_pe, w_uk,
+                     q_abs, num_heads, batch);
+  return hipGetLastError();
+}
+
+}  // namespace mla

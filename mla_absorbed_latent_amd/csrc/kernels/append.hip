@@ -1,0 +1,169 @@
+// append.hip -- write new tokens' latent rows into the paged cache, quantising
+// on the way in for the INT8 / INT4 formats.
+//
+// Only the 512-wide latent and the 64-wide RoPE key are cached
+// ("DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界" §2.4, §4.1).  The quantised
+// formats follow "DeepSeek-V2-Lite MLA 吸收式 KV 缓存优化 — 完整实验报告" §3.2 / §4.1
+// (INT8 with 32-element blocks, asymmetric INT4 with 32-element blocks, RoPE key
+// INT8 with 8-element blocks).  Each block is one token's consecutive channels,
+// so a token is quantised by itself.  Arithmetic is IEEE fp32 with correctly
+// rounded division and round-half-even, so codes and scales are reproducible
+// bit for bit:
+//   INT8: scale = amax / 127, code = clamp(rint(x / scale), -127, 127); amax 0 -> 0.
+//   INT4: zero = min, scale = (max - min) / 15, q = clamp(rint((x - min) / scale), 0, 15);
+//         scale 0 -> q 0; two codes a byte, element 2j in the low nibble.
+//
+// One thread per 16-byte chunk (bf16) or per quantisation group; slots outside
+// [0, num_pages * 64) are skipped.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kPageBf16 = kBlock * kRowBytesBf16;        // 73,728
+constexpr int kPageInt8 = kBlock * 672;                  // 43,008
+constexpr int kPageInt4 = kBlock * 480;                  // 30,720
+
+__device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_pages) {
+  return slot >= 0 && slot < num_pages * kBlock;
+}
+
+__global__ __launch_bounds__(256) void append_bf16(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                   const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = gid / 72;
+  const int chunk = (int)(gid % 72);
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  const uint16_t* src = chunk < 64 ? c_kv + tok * kDc + chunk * 8 : k_pe + tok * kDr + (chunk - 64) * 8;
+  uint8_t* dst = pool + (slot / kBlock) * kPageBf16 + (slot % kBlock) * kRowBytesBf16 + chunk * 16;
+  st16(dst, ld16(src));
+}
+
+// Symmetric INT8 of `kG` consecutive bf16 values.
+template <int kG>
+__device__ __forceinline__ float quant_sym8(const uint16_t* x, int8_t* codes) {
+  float v[kG];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    v[i] = bf16_to_f32(x[i]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const float scale = __fdiv_rn(amax, 127.0f);
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    float q = 0.f;
+    if (scale != 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(v[i], scale)), -127.f), 127.f);
+    codes[i] = (int8_t)(int)q;
+  }
+  return scale;
+}
+
+// 24 groups a token: 16 latent groups of 32, then 8 RoPE-key groups of 8.
+__global__ __launch_bounds__(256) void append_int8(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                   const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = gid / 24;
+  const int grp = (int)(gid % 24);
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * kPageInt8;
+  const int off = (int)(slot % kBlock);
+  if (grp < 16) {
+    int8_t codes[32];
+    const float s = quant_sym8<32>(c_kv + tok * kDc + grp * 32, codes);
+    int8_t* dst = reinterpret_cast<int8_t*>(page + off * 576 + grp * 32);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dst[i] = codes[i];
+    reinterpret_cast<float*>(page + 64 * 576)[off * 16 + grp] = s;
+  } else {
+    const int j = grp - 16;
+    int8_t codes[8];
+    const float s = quant_sym8<8>(k_pe + tok * kDr + j * 8, codes);
+    int8_t* dst = reinterpret_cast<int8_t*>(page + off * 576 + 512 + j * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = codes[i];
+    reinterpret_cast<float*>(page + 64 * 576 + 64 * 64)[off * 8 + j] = s;
+  }
+}
+
+// 24 groups a token: 16 asymmetric INT4 latent groups of 32, then 8 INT8 RoPE-key groups.
+__global__ __launch_bounds__(256) void append_int4(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                   const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = gid / 24;
+  const int grp = (int)(gid % 24);
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * kPageInt4;
+  const int off = (int)(slot % kBlock);
+  // page regions: nibbles [64][256] | rope codes [64][64] | scales [64][16] | zeros [64][16] | rope scales [64][8]
+  uint8_t* nib = page;
+  int8_t* rcodes = reinterpret_cast<int8_t*>(page + 64 * 256);
+  float* scales = reinterpret_cast<float*>(page + 64 * 256 + 64 * 64);
+  float* zeros = scales + 64 * 16;
+  float* rscales = zeros + 64 * 16;
+  if (grp < 16) {
+    const uint16_t* x = c_kv + tok * kDc + grp * 32;
+    float v[32];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_to_f32(x[i]);
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+    const float scale = __fdiv_rn(mx - mn, 15.0f);
+    uint8_t bytes[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t q0 = 0, q1 = 0;
+      if (scale != 0.f) {
+        q0 = (uint32_t)(int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * j] - mn, scale)), 0.f), 15.f);
+        q1 = (uint32_t)(int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * j + 1] - mn, scale)), 0.f), 15.f);
+      }
+      bytes[j] = (uint8_t)(q0 | (q1 << 4));
+    }
+    uint8_t* dst = nib + off * 256 + grp * 16;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[j] = bytes[j];
+    scales[off * 16 + grp] = scale;
+    zeros[off * 16 + grp] = mn;
+  } else {
+    const int j = grp - 16;
+    int8_t codes[8];
+    const float s = quant_sym8<8>(k_pe + tok * kDr + j * 8, codes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rcodes[off * 64 + j * 8 + i] = codes[i];
+    rscales[off * 8 + j] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
+                         const uint16_t* k_pe, const int64_t* slots, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  uint8_t* p = static_cast<uint8_t*>(pool);
+  if (cache_dtype == 0) {
+    const int64_t work = (int64_t)n * 72;
+    hipLaunchKernelGGL(append_bf16, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
+                       c_kv, k_pe, slots, n);
+  } else {
+    const int64_t work = (int64_t)n * 24;
+    const dim3 grid((unsigned)((work + 255) / 256));
+    if (cache_dtype == 1)
+      hipLaunchKernelGGL(append_int8, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+    else
+      hipLaunchKernelGGL(append_int4, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,83 @@
+"""DecodeRunner: the five C-ABI calls of one decode step over caller-owned
+torch buffers.
+
+Allocation happens here, with torch, outside the library (which never
+allocates).  The split plan is computed on the host once per set of sequence
+lengths and uploaded; the timed step itself is five asynchronous launches on
+the current stream and no host synchronisation.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import api
+
+
+class DecodeRunner:
+    def __init__(self, cfg: api.Config, batch: int, num_pages: int, device="cuda:0"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.B = batch
+        self.H = cfg.num_heads
+        self.device = torch.device(device)
+        self.num_pages = num_pages
+        self.page_bytes = api.cache_page_bytes(cfg)
+        self.pool = torch.zeros(num_pages * self.page_bytes, dtype=torch.uint8, device=self.device)
+        self.q_abs = torch.empty(batch, self.H, 576, dtype=torch.float16, device=self.device)
+        self.o_lat = torch.empty(batch, self.H, 512, dtype=torch.float32, device=self.device)
+        self.lse = torch.empty(batch, self.H, dtype=torch.float32, device=self.device)
+        self.out = torch.empty(batch, self.H, 128, dtype=torch.bfloat16, device=self.device)
+        self.items = None
+        self.offsets = None
+        self.o_part = None
+        self.lse_part = None
+        self.n_items = 0
+
+    # ---------------------------------------------------------------- planning
+    def plan(self, seq_lens: Sequence[int], num_cus: Optional[int] = None, chunk_pages: int = 0) -> int:
+        torch = self.torch
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        items, offs = api.plan_splits(self.cfg, seq_lens, num_cus, chunk_pages)
+        self.n_items = int(items.shape[0])
+        rows = max(int(offs[-1]), 1)
+        arr = items if self.n_items else np.zeros((1, 4), np.int32)
+        self.items = torch.from_numpy(np.ascontiguousarray(arr)).to(self.device)
+        self.offsets = torch.from_numpy(offs).to(self.device)
+        if self.o_part is None or self.o_part.shape[0] < rows:
+            self.o_part = torch.empty(rows, self.H, 512, dtype=torch.float32, device=self.device)
+            self.lse_part = torch.empty(rows, self.H, dtype=torch.float32, device=self.device)
+        return self.n_items
+
+    # ---------------------------------------------------------------- the step
+    def append(self, c_kv, k_pe, slots) -> None:
+        api.cache_append(self.cfg, self.pool, c_kv, k_pe, slots)
+
+    def absorb(self, q_nope, q_pe, w_uk) -> None:
+        api.absorb_q(self.cfg, q_nope, q_pe, w_uk, self.q_abs)
+
+    def attend(self, block_table, seq_lens) -> None:
+        if self.n_items == 0:
+            return
+        api.decode_attn(self.cfg, self.q_abs, self.pool, block_table, seq_lens, self.items[: self.n_items],
+                        self.o_part, self.lse_part)
+
+    def combine(self) -> None:
+        api.decode_combine(self.cfg, self.o_part, self.lse_part, self.offsets, self.o_lat, self.lse)
+
+    def project(self, w_uv, w_o=None, y=None, out_f32=None) -> None:
+        api.out_proj(self.cfg, self.o_lat, w_uv, self.out, w_o, y, out_f32)
+
+    def step(self, q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c_kv=None, new_k_pe=None,
+             new_slots=None, w_o=None, y=None, out_f32=None):
+        """One decode step: append the new tokens, absorb, attend, merge, expand."""
+        if new_c_kv is not None:
+            self.append(new_c_kv, new_k_pe, new_slots)
+        self.absorb(q_nope, q_pe, w_uk)
+        self.attend(block_table, seq_lens)
+        self.combine()
+        self.project(w_uv, w_o, y, out_f32)
+        return self.out

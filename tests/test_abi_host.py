@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/mla.h
+declares, and its host-only paths (sizes, validation, planner) behave as
+documented.  No call here launches a kernel: every argument error is rejected
+on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_synth
+from mla_absorbed_latent_amd import _lib as L
+from mla_absorbed_latent_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("library not built: run __graft_entry__.build() first")
+    return L.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|const char\*|int32_t)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in L.SIGNATURES, "binding lacks " + s
+
+
+def test_sizes(lib):
+    for dt, tok, page in ((0, 1152, 73728), (1, 672, 43008), (2, 480, 30720)):
+        cfg = api.config(128, dt)
+        assert api.cache_bytes_per_token(cfg) == tok
+        assert api.cache_page_bytes(cfg) == page
+    cfg = api.config(128)
+    assert api.decode_workspace_bytes(cfg, 10) == 10 * 128 * 513 * 4
+    assert api.cache_bytes_per_token(api.config(8)) == 0       # invalid config -> 0
+
+
+def test_config_check(lib):
+    ok = api.config(16)
+    assert lib.mla_config_check(C.byref(ok)) == L.MLA_OK
+    assert lib.mla_config_check(None) == L.MLA_ERR_NULL
+    for field, val, st in (("num_heads", 64, L.MLA_ERR_SHAPE), ("kv_lora_rank", 256, L.MLA_ERR_SHAPE),
+                           ("block_size", 16, L.MLA_ERR_SHAPE), ("cache_dtype", 3, L.MLA_ERR_VALUE),
+                           ("softmax_scale", 0.0, L.MLA_ERR_VALUE), ("softmax_scale", float("inf"), L.MLA_ERR_VALUE)):
+        c = api.config(16)
+        setattr(c, field, val)
+        assert lib.mla_config_check(C.byref(c)) == st, field
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert len(api.status_string(s)) > 0
+    assert "unknown" in api.status_string(99)
+
+
+def test_argument_errors_are_rejected_before_any_launch(lib):
+    cfg = api.config(16)
+    fake = C.c_void_p(0x1000)      # aligned, never dereferenced: validation fails first
+    odd = C.c_void_p(0x1001)
+    assert lib.mla_cache_append(C.byref(cfg), None, 4, fake, fake, fake, 3, None) == L.MLA_ERR_NULL
+    assert lib.mla_cache_append(C.byref(cfg), odd, 4, fake, fake, fake, 3, None) == L.MLA_ERR_ALIGN
+    assert lib.mla_cache_append(C.byref(cfg), fake, 4, fake, fake, fake, -1, None) == L.MLA_ERR_VALUE
+    assert lib.mla_cache_append(C.byref(cfg), None, 4, None, None, None, 0, None) == L.MLA_OK   # no-op
+    assert lib.mla_absorb_q(C.byref(cfg), fake, fake, None, fake, 2, None) == L.MLA_ERR_NULL
+    assert lib.mla_absorb_q(C.byref(cfg), fake, fake, fake, fake, -2, None) == L.MLA_ERR_VALUE
+    assert lib.mla_decode_attn(C.byref(cfg), fake, fake, 4, fake, 2, fake, fake, -1, fake, fake, 1,
+                               None) == L.MLA_ERR_VALUE
+    assert lib.mla_decode_attn(C.byref(cfg), fake, fake, 4, fake, 2, fake, None, 3, fake, fake, 1,
+                               None) == L.MLA_ERR_NULL
+    assert lib.mla_decode_attn(C.byref(cfg), fake, fake, 4, fake, 2, fake, fake, 0, fake, fake, 1,
+                               None) == L.MLA_OK                                        # no items: no-op
+    assert lib.mla_decode_combine(C.byref(cfg), fake, fake, fake, odd, None, 2, None) == L.MLA_ERR_ALIGN
+    assert lib.mla_out_proj(C.byref(cfg), fake, fake, fake, fake, 0, fake, fake, 2, None) == L.MLA_ERR_VALUE
+    assert lib.mla_out_proj(C.byref(cfg), fake, fake, fake, fake, 2048, None, fake, 2, None) == L.MLA_ERR_NULL
+    bad = api.config(64)
+    assert lib.mla_absorb_q(C.byref(bad), fake, fake, fake, fake, 2, None) == L.MLA_ERR_SHAPE
+
+
+def _check_plan(items, offs, lens, block=64):
+    B = len(lens)
+    assert offs[0] == 0 and offs[-1] == len(items)
+    seen = {}
+    for seq, first, n, row in items:
+        assert offs[seq] <= row < offs[seq + 1]
+        seen.setdefault(seq, []).append((first, n, row))
+    for b in range(B):
+        runs = sorted(seen[b])
+        pages = (lens[b] + block - 1) // block
+        cur = 0
+        for first, n, _ in runs:
+            assert first == cur
+            cur += n
+        assert cur == pages
+        assert sorted(r for _, _, r in runs) == list(range(offs[b], offs[b + 1]))
+    ns = [it[2] for it in items]
+    assert ns == sorted(ns, reverse=True)         # longest first
+
+
+def test_planner_uniform_batch(lib):
+    cfg = api.config(128)
+    items, offs = api.plan_splits(cfg, [8192] * 64, 256)
+    assert len(items) == 256 and set(items[:, 2]) == {32}
+    _check_plan(items, offs, [8192] * 64)
+
+
+def test_planner_ragged_and_edges(lib):
+    cfg = api.config(128)
+    lens = mla_synth.log_uniform_lengths(4, 128)
+    items, offs = api.plan_splits(cfg, lens, 256)
+    _check_plan(items, offs, list(lens))
+    assert len(items) >= 256
+    lens = [0, 1, 63, 64, 65, 65536]
+    items, offs = api.plan_splits(cfg, lens, 256, chunk_pages=7)
+    _check_plan(items, offs, lens)
+    assert [n for s, _, n, _ in items if s == 0] == [0]          # empty sequence: one empty item
+    items, offs = api.plan_splits(cfg, [], 256)
+    assert len(items) == 0 and list(offs) == [0]
+
+
+def test_planner_capacity_error(lib):
+    cfg = api.config(16)
+    lens = (C.c_int32 * 2)(640, 640)
+    n = C.c_int32(0)
+    offs = (C.c_int32 * 3)()
+    items = (L.WorkItem * 1)()
+    st = lib.mla_plan_splits(C.byref(cfg), lens, 2, 256, 1, items, 1, C.byref(n), offs)
+    assert st == L.MLA_ERR_WORKSPACE and n.value == 20
+    lens[0] = -1
+    assert lib.mla_plan_splits(C.byref(cfg), lens, 2, 256, 1, items, 1, C.byref(n), offs) == L.MLA_ERR_VALUE
+
+
+def test_binding_rejects_bad_shapes_before_the_library():
+    import torch
+    cfg = api.config(16)
+    with pytest.raises(ValueError):
+        api.absorb_q(cfg, torch.zeros(2, 16, 64, dtype=torch.bfloat16), torch.zeros(2, 16, 64, dtype=torch.bfloat16),
+                     torch.zeros(16, 128, 512, dtype=torch.bfloat16), torch.zeros(2, 16, 576, dtype=torch.float16))
+
+
+def test_product_never_touches_the_oracle():
+    """The HIP path and its binding must not import or reference the oracle."""
+    pkg = os.path.join(ROOT, "mla_absorbed_latent_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"\boracle\b", text.replace("no CPU fallback", "")), f
