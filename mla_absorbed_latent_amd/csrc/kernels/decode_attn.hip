@@ -6,44 +6,48 @@
 // shared "KV head" of width 576 for scores and 512 for values.  Per work item
 // (a run of a sequence's pages) and head:
 //   s_t = scale * q_abs . row_t,  o = sum_t e^{s_t-m} c_t / l,  lse = m + ln l.
+// Quantised caches ("DeepSeek-V2-Lite MLA 吸收式 KV 缓存优化 — 完整实验报告" §3.2/§4.1)
+// are dequantised once per tile into the same fp16 tile layout.
 //
 // gfx950 design
-//   * One work-group (4 wave64s, 256 threads) per work item; the item's tokens
-//     are streamed through LDS in tiles.  All 256 threads load a tile from HBM
-//     with coalesced 16-byte loads into registers one tile ahead, widen bf16 to
-//     fp16 (exact), and store it row-major in LDS (double buffered).
-//   * H = 128: wave w owns heads 32w..32w+31 and the whole 32-token tile.
-//       scores S^T[32 tok x 32 head] = K[32 x 576] . Q^T       (36 x mfma 32x32x16;
-//         K from LDS, Q resident in VGPRs)
-//       O^T[512 x 32 head] += V^T[512 x 32 tok] . P^T           (32 x mfma 32x32x16;
-//         V^T read straight from the row-major tile with ds_read_b64_tr_b16,
-//         P^T is the score accumulator's own lane layout, rounded to fp16)
-//     so every head of the sequence shares each LDS read of the latent.
+//   * One work-group (4 wave64s) per work item; the item's tokens stream through
+//     LDS in tiles of fp16 rows (1,152 B, 16-byte chunks XOR-swizzled by row).
+//   * H = 128: wave w owns heads 32w..32w+31 and the whole 32-token tile:
+//       S^T[32 tok x 32 head] = K[32 x 576] . Q^T    36 x mfma 32x32x16 (K from LDS,
+//                                                     Q resident in VGPRs)
+//       O^T[512 x 32 head] += V^T . P^T               32 x mfma 32x32x16 (V^T read from
+//                                                     the same row-major tile with
+//                                                     ds_read_b64_tr_b16; P^T is the
+//                                                     score accumulator's own layout)
+//     so all 128 heads share each LDS read of the latent.  bf16 tiles arrive by
+//     direct global->LDS loads (no VGPRs) into a 4-tile ring and are widened to
+//     fp16 in place by the lane that loaded them; two tiles stay in flight.
 //   * H = 16: each wave takes 16 tokens of a 64-token page for all 16 heads
-//     (mfma 16x16x32 for scores, 16x16x16 for values); the four waves' running
-//     (max, sum, O) are merged through LDS at the end.
-//   * Online softmax in the log2 domain with a lazy running max: O and l are
-//     only rescaled when a tile's max exceeds the reference max by more than
-//     kTau (so P <= 2^kTau stays far inside fp16), which is exact after the
-//     final division by l.
-//   * Tokens past the item's end, or on pages whose id is outside the pool,
-//     are zero-filled in LDS and masked to -inf.
+//     (mfma 16x16x32 scores, 16x16x16 values); the four waves' (max, sum, O) are
+//     merged through LDS at the end.
+//   * Quantised tiles, and H = 16, use register prefetch one tile ahead and a
+//     2-tile LDS ring.
+//   * Softmax in the log2 domain.  H = 128 fixes each head's reference max at its
+//     first non-empty tile and never rescales O inside the loop (P <= 2^15 fits
+//     fp16); if a later tile exceeds that by more than 2^15 the item is redone
+//     against exact maxima (one scores-only pass, one accumulate pass).  H = 16
+//     rescales lazily (only when the max grows by more than 2^8).
+//   * Tokens past the item's end, or on pages whose id is outside the pool, are
+//     zero-filled in LDS and masked to -inf.
+#include <type_traits>
+
 #include "common.h"
 #include "decode_attn.h"
 
 namespace mla {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units), H = 16
-constexpr float kTauFixed = 15.0f;  // fixed-reference headroom (log2 units), H = 128: P <= 2^15
+constexpr float kTau = 8.0f;         // lazy-rescale threshold (log2 units), H = 16
+constexpr float kTauFixed = 15.0f;   // fixed-reference headroom (log2 units), H = 128: P <= 2^15
 
-// LDS tile layout: fp16 rows of 576 (1,152 B = 72 chunks of 16 B), no padding;
-// the 16-byte chunk index of row r is XORed with (r & 7) so that the eight rows
-// read together by an MFMA operand fetch land in different banks.
-constexpr int kRowLds = kDk * 2;                    // 1,152 B
-constexpr int kChunksPerRow = kRowBytesBf16 / 16;   // 72 x 16 B per token row
+constexpr int kRowLds = kDk * 2;                    // 1,152 B: one fp16 token row in LDS
 
+// Byte offset of 16-byte chunk `chunk` of LDS row `row` (XOR swizzle on the low 3 bits).
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return (uint32_t)(row * kRowLds + 16 * (chunk ^ (row & 7)));
 }
@@ -77,18 +81,18 @@ __device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int t) {
   return (p >= 0 && p < a.num_pages) ? p : -1;
 }
 
-// ---------------------------------------------------------------------------
-// Tile loader, bf16 pool: kTok tokens (a multiple of 32 dividing 64) starting
-// at token t0 -> registers (one tile ahead) -> fp16 rows in LDS.  Thread tid
-// owns token (tid >> 3) of every 32-token pass and the 16-byte columns
-// (tid & 7) + 8k, k = 0..8, so both the global and the LDS offsets are affine
-// in k; a wave's load covers 8 tokens x 128 contiguous bytes.
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// Register-prefetch tile loaders: issue() loads a tile into registers, commit()
+// writes it as fp16 rows into an LDS buffer.  kTok tokens (32 or 64), starting
+// at a multiple of kTok within a page.  Thread tid owns token (tid >> 3) of each
+// 32-token pass and the 16-byte output chunks (tid & 7) + 8k, k = 0..8 (k = 8 is
+// the RoPE key), so all offsets are affine in k.  Rows past t_end and pages out
+// of range become zeros.
+// ===========================================================================
 template <int kTok>
-struct LoaderBf16 {
+struct LoaderBf16Reg {
   static constexpr int kPass = kTok / 32;
-  static constexpr int kPer = 9 * kPass;          // 16-byte chunks per thread
-  u32x4 r[kPer];
+  u32x4 r[9 * kPass];
 
   __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
     const int64_t page = page_of(a, b, t0);
@@ -114,29 +118,227 @@ struct LoaderBf16 {
   }
 };
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Four int8 codes -> four fp16 values code * s (s already fp16).  0x6400 | (code ^ 0x80)
+// is the fp16 number 1024 + code + 128, exactly; subtracting 1152 leaves the code.
+__device__ __forceinline__ u32x2 int8x4_to_f16(uint32_t c, half2v s) {
+  const uint32_t u = c ^ 0x80808080u;
+  const uint32_t h0 = 0x64006400u | (u & 0xffu) | ((u & 0xff00u) << 8);
+  const uint32_t h1 = 0x64006400u | ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u);
+  const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  return u32x2{__builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h0) + bias) * s),
+               __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h1) + bias) * s)};
+}
+
+// INT8 page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key scales.
+template <int kTok>
+struct LoaderInt8Reg {
+  static constexpr int kPass = kTok / 32;
+  static constexpr int kPage = kBlock * 672;
+  u32x2 c[9 * kPass];
+  float s[9 * kPass];
+
+  __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
+    const int64_t page = page_of(a, b, t0);
+    const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
+    const uint8_t* pg = a.pool + (page < 0 ? 0 : page) * (int64_t)kPage;
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int row = (t0 % kBlock) + 32 * p + tok;
+      const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const uint8_t* codes = pg + row * 576 + 8 * c8;
+      const float* cs = reinterpret_cast<const float*>(pg + 64 * 576) + row * 16 + (c8 >> 2);
+      const float* ks = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64) + row * 8 + c8;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        c[9 * p + k] = ok ? *reinterpret_cast<const u32x2*>(codes + 64 * k) : u32x2{0u, 0u};
+        s[9 * p + k] = ok ? (k < 8 ? cs[2 * k] : ks[0]) : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) const {
+    const int tok = threadIdx.x >> 3;
+    char* dst = lds_buf + swz(tok, threadIdx.x & 7);
+#pragma unroll
+    for (int p = 0; p < kPass; ++p)
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const _Float16 sh = (_Float16)s[9 * p + k];
+        const half2v s2 = {sh, sh};
+        const u32x2 lo = int8x4_to_f16(c[9 * p + k][0], s2), hi = int8x4_to_f16(c[9 * p + k][1], s2);
+        *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+  }
+};
+
+// INT4 page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32 scales
+//            | [64][16] f32 zeros | [64][8] f32 key scales.
+template <int kTok>
+struct LoaderInt4Reg {
+  static constexpr int kPass = kTok / 32;
+  static constexpr int kPage = kBlock * 480;
+  uint32_t n[8 * kPass];     // 8 nibbles (latent chunk k) per dword
+  u32x2 kc[kPass];           // 8 key codes (chunk 8)
+  float s[9 * kPass];        // scale per chunk (k = 8: key scale)
+  float z[8 * kPass];        // zero point per latent chunk
+
+  __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
+    const int64_t page = page_of(a, b, t0);
+    const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
+    const uint8_t* pg = a.pool + (page < 0 ? 0 : page) * (int64_t)kPage;
+    const float* scales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
+    const float* zeros = scales + 64 * 16;
+    const float* kscales = zeros + 64 * 16;
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int row = (t0 % kBlock) + 32 * p + tok;
+      const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const uint8_t* nib = pg + row * 256 + 4 * c8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        n[8 * p + k] = ok ? *reinterpret_cast<const uint32_t*>(nib + 32 * k) : 0u;
+        s[9 * p + k] = ok ? scales[row * 16 + 2 * k + (c8 >> 2)] : 0.f;
+        z[8 * p + k] = ok ? zeros[row * 16 + 2 * k + (c8 >> 2)] : 0.f;
+      }
+      kc[p] = ok ? *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8) : u32x2{0u, 0u};
+      s[9 * p + 8] = ok ? kscales[row * 8 + c8] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) const {
+    const int tok = threadIdx.x >> 3;
+    char* dst = lds_buf + swz(tok, threadIdx.x & 7);
+    const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const _Float16 sh = (_Float16)s[9 * p + k], zh = (_Float16)z[8 * p + k];
+        const half2v s2 = {sh, sh}, z2 = {zh, zh};
+        const uint32_t w = n[8 * p + k];
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t byte = (w >> (8 * j)) & 0xffu;
+          // (element 2j, element 2j+1) = (low nibble, high nibble) as fp16 1024 + q
+          const uint32_t h = 0x64006400u | (byte & 0xfu) | ((byte >> 4) << 16);
+          const half2v qv = __builtin_bit_cast(half2v, h) + bias;
+          v[j] = __builtin_bit_cast(uint32_t, qv * s2 + z2);
+        }
+        *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = v;
+      }
+      const _Float16 kh = (_Float16)s[9 * p + 8];
+      const half2v k2 = {kh, kh};
+      const u32x2 lo = int8x4_to_f16(kc[p][0], k2), hi = int8x4_to_f16(kc[p][1], k2);
+      *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+};
+
 // ===========================================================================
 // H = 128
 // ===========================================================================
 constexpr int kTile128 = 32;
 constexpr int kBuf128 = kTile128 * kRowLds;        // 36,864 B
 
-// One pass over the item's tiles.  kMode 0: accumulate with a per-head
-// reference max fixed at the head's first non-empty tile, flagging `overflow`
-// if a later tile's max exceeds it by more than kTauFixed; kMode 1: scores only,
-// returning the exact per-head max in m_ref; kMode 2: accumulate with the exact
-// max already in m_ref (no overflow possible).
-template <int kMode>
-__device__ __forceinline__ void h128_pass(const DecodeArgs& a, const ItemRange& it, char* lds,
-                                          const half8 (&q)[kDk / 16], floatx16 (&o)[16],
-                                          float& m_ref, float& l_sum, bool& overflow,
-                                          const uint32_t (&qk_off)[4], const uint32_t (&pv_off)[2]) {
+struct H128Lane {
+  uint32_t qk_off[4];     // score operand: row hl, chunk 2 ks + g
+  uint32_t pv_off[2];     // transposed value read: row 4 g + (gi >> 2) (+16 j, +8)
+  int g;
+};
+
+__device__ __forceinline__ H128Lane h128_lane() {
+  H128Lane L;
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
+  const int hl = lane & 31, g = lane >> 5, grp = lane >> 4, gi = lane & 15;
+  L.g = g;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) L.qk_off[k4] = swz(hl, 2 * k4 + g);
+  const int pv_row = 4 * g + (gi >> 2);
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    L.pv_off[par] = swz(pv_row, 4 * par + 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  return L;
+}
+
+// One 32-token tile of work for one wave.  kMode 0: accumulate with a per-head
+// reference max fixed at the head's first non-empty tile (sets `overflow` when a
+// later tile exceeds it by more than kTauFixed); kMode 1: scores only, m_ref
+// becomes the exact max; kMode 2: accumulate against the exact max in m_ref.
+template <int kMode>
+__device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, const half8 (&q)[kDk / 16],
+                                          floatx16 (&o)[16], float& m_ref, float& l_sum, bool& overflow,
+                                          int t0, int t_end, bool page_ok, float scale_log2) {
+  auto kread = [&](int ks) -> half8 {
+    return *reinterpret_cast<const half8*>(buf + L.qk_off[ks & 3] + 128 * (ks >> 2));
+  };
+  floatx16 sacc = floatx16{};
+  half8 k0 = kread(0), k1 = kread(1), k2 = kread(2);
+#pragma unroll
+  for (int ks = 0; ks < kDk / 16; ++ks) {
+    const half8 kn = (ks + 3 < kDk / 16) ? kread(ks + 3) : k2;
+    sacc = mfma32x32x16(k0, q[ks], sacc);
+    k0 = k1;
+    k1 = k2;
+    k2 = kn;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tt = t0 + 8 * (r >> 2) + 4 * L.g + (r & 3);
+    float v = sacc[r] * scale_log2;
+    if (!page_ok || tt >= t_end) v = -INFINITY;
+    sacc[r] = v;
+    mx = fmaxf(mx, v);
+  }
+  mx = wave_max_xor(mx, 32);               // lanes l and l^32 hold the same head
+  if (kMode == 1) {
+    m_ref = fmaxf(m_ref, mx);
+    return;
+  }
+  if (kMode == 0) {
+    if (m_ref == -INFINITY) m_ref = mx;    // first non-empty tile: nothing accumulated yet
+    overflow |= mx > m_ref + kTauFixed;
+  }
+  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  half8 p[2];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
+    psum += e;
+    p[r >> 3][r & 7] = (_Float16)e;
+  }
+  l_sum += psum;
+  // O^T += V^T . P^T: step i covers tokens 16 (i / 16) .. +15 and features
+  // 32 (i % 16) .. +31; the transposed reads run two steps ahead of the MFMAs.
+  auto vread = [&](int i) -> half8 {
+    const int j = i >> 4, tile = i & 15;
+    const uint32_t off = L.pv_off[tile & 1] + 16 * j * kRowLds + 128 * (tile >> 1);
+    const half4 lo = lds_read_tr(buf, off);
+    const half4 hi = lds_read_tr(buf, off + 8 * kRowLds);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  half8 v0 = vread(0), v1 = vread(1);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const half8 vn = (i + 2 < 32) ? vread(i + 2) : v1;
+    o[i & 15] = mfma32x32x16(v0, p[i >> 4], o[i & 15]);
+    v0 = v1;
+    v1 = vn;
+  }
+}
+
+// ---- pipeline A: register prefetch, 2-tile ring (quantised formats) ----------
+template <class Loader, int kMode>
+__device__ __forceinline__ void h128_pass_reg(const DecodeArgs& a, const ItemRange& it, char* lds,
+                                              const H128Lane& L, const half8 (&q)[kDk / 16], floatx16 (&o)[16],
+                                              float& m_ref, float& l_sum, bool& overflow) {
   const int n_tiles = (it.t_end - it.t_begin + kTile128 - 1) / kTile128;
-  LoaderBf16<kTile128> ld;
+  Loader ld;
   if (n_tiles > 0) {
     ld.issue(a, it.b, it.t_begin, it.t_end);
-    __syncthreads();                       // previous users of the buffers are done
+    __syncthreads();                       // earlier users of the buffers are done
     ld.commit(lds);
     if (n_tiles > 1) ld.issue(a, it.b, it.t_begin + kTile128, it.t_end);
   }
@@ -146,70 +348,140 @@ __device__ __forceinline__ void h128_pass(const DecodeArgs& a, const ItemRange& 
       ld.commit(lds + ((s + 1) & 1) * kBuf128);
       if (s + 2 < n_tiles) ld.issue(a, it.b, it.t_begin + (s + 2) * kTile128, it.t_end);
     }
-    const char* buf = lds + (s & 1) * kBuf128;
     const int t0 = it.t_begin + s * kTile128;
-    const bool page_ok = page_of(a, it.b, t0) >= 0;
-
-    // ---- scores S^T (token x head) ----
-    floatx16 sacc = floatx16{};
-#pragma unroll
-    for (int ks = 0; ks < kDk / 16; ++ks) {
-      const half8 kv = *reinterpret_cast<const half8*>(buf + qk_off[ks & 3] + 128 * (ks >> 2));
-      sacc = mfma32x32x16(kv, q[ks], sacc);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tt = t0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      float v = sacc[r] * a.scale_log2;
-      if (!page_ok || tt >= it.t_end) v = -INFINITY;
-      sacc[r] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = wave_max_xor(mx, 32);             // lanes l and l^32 hold the same head
-    if (kMode == 1) {
-      m_ref = fmaxf(m_ref, mx);
-      continue;
-    }
-    if (kMode == 0) {
-      if (m_ref == -INFINITY) m_ref = mx;  // first non-empty tile: nothing accumulated yet
-      overflow |= mx > m_ref + kTauFixed;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    half8 p[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
-      psum += e;
-      p[r >> 3][r & 7] = (_Float16)e;
-    }
-    l_sum += psum;
-
-    // ---- O^T += V^T . P^T ----
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int tile = 0; tile < 16; ++tile) {
-        const uint32_t off = pv_off[tile & 1] + 16 * j * kRowLds + 128 * (tile >> 1);
-        const half4 lo = lds_read_tr(buf, off);
-        const half4 hi = lds_read_tr(buf, off + 8 * kRowLds);
-        const half8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[tile] = mfma32x32x16(av, p[j], o[tile]);
-      }
-    }
+    h128_tile<kMode>(lds + (s & 1) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, it.t_end,
+                     page_of(a, it.b, t0) >= 0, a.scale_log2);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void decode_h128_bf16(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBuf128];
+// ---- pipeline B: direct global->LDS loads, 4-tile ring (bf16) ----------------
+// Wave w fills LDS bytes [9216 w, 9216 w + 9216) of a tile with 9 loads of
+// 64 lanes x 16 B; the lane writing LDS offset o carries the global chunk
+// (row = o / 1152, logical chunk = physical chunk ^ (row & 7)).  After its own
+// loads have landed, each lane widens exactly those 16 bytes to fp16 in place
+// (or zeroes them for rows past the end / bad pages), so no other lane's data
+// is touched before the next barrier.
+struct DmaBf16Tile {
+  uint32_t loff;          // LDS byte offset of this lane's chunk 0 within a tile
+  int wave;
+
+  __device__ __forceinline__ void init() {
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    loff = 9216 * wave + 16 * (threadIdx.x & 63);
+  }
+  // Byte offset, from the tile's first cache row, of the chunk lane-slot k carries.
+  __device__ __forceinline__ uint32_t goff(int k) const {
+    const uint32_t o = loff + 1024 * k;
+    const uint32_t row = o / kRowLds;
+    const uint32_t pc = (o - row * kRowLds) >> 4;
+    return row * kRowBytesBf16 + 16 * (pc ^ (row & 7));
+  }
+  // The load is issued through inline assembly so that the compiler does not
+  // track it: otherwise it waits for every outstanding direct load before any
+  // LDS read it cannot prove disjoint, which would serialise the ring.  The
+  // waits are placed explicitly (wait_vm_tiles) instead.
+  __device__ __forceinline__ void issue(const uint8_t* src, char* lds_tile) const {
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds_tile + 9216 * wave);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const uint8_t* g = src + goff(k);
+      asm volatile(
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %0, off"
+          :
+          : "v"(g), "s"(lds_base + 1024 * k)
+          : "memory", "m0");
+    }
+  }
+  __device__ __forceinline__ void convert(char* lds_tile, int valid_rows) const {
+    u32x4 v[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) v[k] = *reinterpret_cast<const u32x4*>(lds_tile + loff + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const uint32_t o = loff + 1024 * k;
+      const int row = (int)(o / kRowLds);
+      *reinterpret_cast<u32x4*>(lds_tile + o) = row < valid_rows ? bf16x8_to_f16x8(v[k]) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 |
+// lgkmcnt[11:8] = 15 | vmcnt[5:4] in bits [15:14]).
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((kN & 15) | (7 << 4) | (15 << 8) | ((kN >> 4) << 14));
+}
+// Wait until this wave's loads for a tile have landed while `tiles_after` later
+// tiles (9 loads each) may still be in flight.
+__device__ __forceinline__ void wait_vm_tiles(int tiles_after) {
+  if (tiles_after >= 2) wait_vm<18>();
+  else if (tiles_after == 1) wait_vm<9>();
+  else wait_vm<0>();
+}
+
+// The pages of an item are looked up from an LDS copy of its block-table slice,
+// refreshed every kSegPages pages while no direct load is in flight, so the only
+// vector-memory operations inside the pipeline are the tile loads themselves
+// (the vmcnt accounting above relies on that).
+constexpr int kSegPages = 2048;
+
+template <int kMode>
+__device__ __forceinline__ void h128_pass_dma(const DecodeArgs& a, const ItemRange& it, char* lds, int32_t* ptab,
+                                              const H128Lane& L, const DmaBf16Tile& D, const half8 (&q)[kDk / 16],
+                                              floatx16 (&o)[16], float& m_ref, float& l_sum, bool& overflow) {
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+    const int n_pages = (seg1 - seg0 + kBlock - 1) / kBlock;
+    __syncthreads();                       // earlier users of the ring and the table are done
+    for (int i = threadIdx.x; i < n_pages; i += 256) ptab[i] = (int32_t)page_of(a, it.b, seg0 + i * kBlock);
+    __syncthreads();
+    const int n_tiles = (seg1 - seg0 + kTile128 - 1) / kTile128;
+    auto page_at = [&](int t) -> int { return ptab[(t * kTile128) / kBlock]; };
+    auto tile_src = [&](int t) -> const uint8_t* {
+      const int page = page_at(t);
+      return a.pool + (int64_t)(page < 0 ? 0 : page) * (kBlock * kRowBytesBf16) +
+             (int64_t)(((seg0 + t * kTile128) % kBlock) * kRowBytesBf16);
+    };
+    auto valid_rows = [&](int t) -> int {
+      return page_at(t) >= 0 ? min(kTile128, seg1 - (seg0 + t * kTile128)) : 0;
+    };
+    const bool any_pages = a.num_pages > 0;
+    if (any_pages) {
+      for (int t = 0; t < min(3, n_tiles); ++t) D.issue(tile_src(t), lds + t * kBuf128);
+    }
+    wait_vm_tiles(any_pages ? min(2, n_tiles - 1) : 0);
+    D.convert(lds, valid_rows(0));
+    for (int s = 0; s < n_tiles; ++s) {
+      __syncthreads();                     // tile s converted by all; tile s-1 no longer read
+      if (s + 3 < n_tiles && any_pages) D.issue(tile_src(s + 3), lds + ((s + 3) & 3) * kBuf128);
+      if (s + 1 < n_tiles) {
+        wait_vm_tiles(any_pages ? min(2, n_tiles - 1 - (s + 1)) : 0);
+        D.convert(lds + ((s + 1) & 3) * kBuf128, valid_rows(s + 1));
+      }
+      const int t0 = seg0 + s * kTile128;
+      h128_tile<kMode>(lds + (s & 3) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, seg1, page_at(s) >= 0,
+                       a.scale_log2);
+    }
+    wait_vm<0>();
+  }
+}
+
+template <int kCache>
+__global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
+  constexpr int kRing = (kCache == 0) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) char lds[kRing * kBuf128];
+  __shared__ int32_t ptab[kCache == 0 ? kSegPages : 1];
   const ItemRange it = item_range(a);
   if (!it.ok) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int hl = lane & 31;           // head within the wave / MFMA column
-  const int g = lane >> 5;            // k-half of the MFMA operands
+  const int hl = lane & 31;
+  const int g = lane >> 5;
   const int h = wave * 32 + hl;
+  const H128Lane L = h128_lane();
 
   // Q^T as the B operand: lane holds q_abs[b][h][16 ks + 8 g .. +7].
   half8 q[kDk / 16];
@@ -218,35 +490,40 @@ __global__ __launch_bounds__(256, 1) void decode_h128_bf16(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 16 * ks));
   }
-
-  // Per-lane LDS offsets (swizzled chunks; see swz()).  Score operand: row hl,
-  // chunk 2 ks + g.  Transposed value read: row 16 j + 4 g + (gi >> 2) (+8),
-  // chunk 4 tile + 2 (grp & 1) + ((gi & 3) >> 1), 8 bytes in when gi is odd.
-  const int grp = lane >> 4, gi = lane & 15;
-  uint32_t qk_off[4];
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) qk_off[k4] = swz(hl, 2 * k4 + g);
-  const int pv_row = 4 * g + (gi >> 2);
-  uint32_t pv_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-    pv_off[par] = swz(pv_row, 4 * par + 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
-
   floatx16 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = floatx16{};
   float m_ref = -INFINITY, l_sum = 0.f;
   bool overflow = false;
-  h128_pass<0>(a, it, lds, q, o, m_ref, l_sum, overflow, qk_off, pv_off);
-  if (__syncthreads_or(overflow)) {
-    // Rare: some head's scores grew by more than 2^kTauFixed after its first
-    // tile.  Find the exact maxima, then redo the item against them.
-    m_ref = -INFINITY;
-    h128_pass<1>(a, it, lds, q, o, m_ref, l_sum, overflow, qk_off, pv_off);
+
+  if constexpr (kCache == 0) {
+    // Retire the Q loads before the first direct load: the compiler cannot see
+    // the direct loads, so its own vmcnt waits for Q inside the loop would
+    // otherwise also stall on tile loads.
+    wait_vm<0>();
+    DmaBf16Tile D;
+    D.init();
+    h128_pass_dma<0>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
+    if (__syncthreads_or(overflow)) {
+      // Rare: some head's scores grew by more than 2^15 after its first tile.
+      m_ref = -INFINITY;
+      h128_pass_dma<1>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = floatx16{};
-    l_sum = 0.f;
-    h128_pass<2>(a, it, lds, q, o, m_ref, l_sum, overflow, qk_off, pv_off);
+      for (int i = 0; i < 16; ++i) o[i] = floatx16{};
+      l_sum = 0.f;
+      h128_pass_dma<2>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
+    }
+  } else {
+    using Loader = typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128>, LoaderInt4Reg<kTile128>>::type;
+    h128_pass_reg<Loader, 0>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
+    if (__syncthreads_or(overflow)) {
+      m_ref = -INFINITY;
+      h128_pass_reg<Loader, 1>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = floatx16{};
+      l_sum = 0.f;
+      h128_pass_reg<Loader, 2>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
+    }
   }
 
   // ---- normalise and write the partial ----
@@ -271,7 +548,8 @@ __global__ __launch_bounds__(256, 1) void decode_h128_bf16(DecodeArgs a) {
 constexpr int kTile16 = 64;
 constexpr int kBuf16 = kTile16 * kRowLds;          // 73,728 B
 
-__global__ __launch_bounds__(256, 1) void decode_h16_bf16(DecodeArgs a) {
+template <class Loader>
+__global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kBuf16];
   const ItemRange it = item_range(a);
   if (!it.ok) return;
@@ -294,7 +572,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_bf16(DecodeArgs a) {
   float m_run = -INFINITY;
   float l_sum = 0.f;
 
-  LoaderBf16<kTile16> ld;
+  Loader ld;
   if (n_tiles > 0) {
     ld.issue(a, it.b, it.t_begin, it.t_end);
     ld.commit(lds);
@@ -416,13 +694,19 @@ __global__ __launch_bounds__(256, 1) void decode_h16_bf16(DecodeArgs a) {
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid(a.n_items), block(256);
-  if (cache_dtype != 0) return hipErrorInvalidValue;
-  if (num_heads == 128)
-    hipLaunchKernelGGL(decode_h128_bf16, grid, block, 0, stream, a);
-  else if (num_heads == 16)
-    hipLaunchKernelGGL(decode_h16_bf16, grid, block, 0, stream, a);
-  else
+  if (num_heads == 128) {
+    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h128<0>, grid, block, 0, stream, a);
+    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h128<1>, grid, block, 0, stream, a);
+    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+  } else if (num_heads == 16) {
+    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<LoaderBf16Reg<kTile16>>, grid, block, 0, stream, a);
+    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<LoaderInt8Reg<kTile16>>, grid, block, 0, stream, a);
+    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<LoaderInt4Reg<kTile16>>, grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

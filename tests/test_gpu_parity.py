@@ -90,7 +90,7 @@ def test_decode_small(H, lens, chunk, paging):
         assert np.max(np.abs(lse[b] - ref_lse)) <= 1e-2 * max(1.0, np.max(np.abs(ref_lse)))
 
 
-QUANT_DECODE_READY = False
+QUANT_DECODE_READY = True
 needs_quant = pytest.mark.skipif(not QUANT_DECODE_READY, reason="quantised decode kernels not built yet")
 
 
