@@ -77,6 +77,27 @@ def cpu_baseline(case, cache_dtype, budget_s=15.0):
                       % (seqs, case.B, done_tokens, t_total)}
 
 
+def recorded_traffic(workload, cache_dtype):
+    """HBM bytes per launch of mla_decode_attn measured with rocprofv3 FETCH_SIZE /
+    WRITE_SIZE (scaled by a plain-copy calibration), as recorded in
+    profiles/decode_attn_<workload>.md -- or None when that record is missing or
+    was taken on a different version of the kernel source."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_attn_%s.md" % workload)
+    src = os.path.join(ROOT, "mla_absorbed_latent_amd", "csrc", "kernels", "decode_attn.hip")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path, encoding="utf-8").read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha or rec.get("cache_dtype") != cache_dtype:
+        return None
+    return rec.get("traffic_bytes")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,7 +107,18 @@ def main():
     ap.add_argument("--cache-dtype", default="bf16", choices=sorted(DTYPES))
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by sequence "
               "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -204,7 +236,7 @@ def main():
         "pct_roofline_attn": round(100.0 * roof_t / (t_attn_ms * 1e-3), 2),
         "roofline": {"bound": "hbm", "kernel": "mla_decode_attn", "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "launch_ms": round(attn_ms, 5),
+                     "traffic": recorded_traffic(args.workload, args.cache_dtype), "launch_ms": round(attn_ms, 5),
                      "bytes_per_launch": latent_bytes,
                      "mfma_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16, 4)},

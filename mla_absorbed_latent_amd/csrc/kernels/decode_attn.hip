@@ -47,9 +47,23 @@ constexpr float kTauFixed = 15.0f;   // fixed-reference headroom (log2 units), H
 
 constexpr int kRowLds = kDk * 2;                    // 1,152 B: one fp16 token row in LDS
 
-// Byte offset of 16-byte chunk `chunk` of LDS row `row` (XOR swizzle on the low 3 bits).
+// LDS tile layout: fp16 rows of 1,152 B (72 chunks of 16 B).  The 16-byte chunk
+// index is XORed (within its aligned group of 8) with a function of row bits 1..3,
+// chosen per kernel so that the MFMA operand fetches of that kernel are free of
+// bank conflicts on the 64-bank LDS: the row stride is 32 banks, so rows r and
+// r ^ 1 never collide and the XOR only has to separate rows that share parity.
+//   kSwz128: for 16 consecutive rows reading one chunk (score operand) and for
+//            4 rows x 32 B transposed reads (value operand).
+//   kSwz16:  the same two patterns at the 16-head shapes.
+constexpr int kSwz128 = 0, kSwz16 = 1;
+template <int kSwz>
+__device__ __forceinline__ int swz_key(int row) {
+  const int m = (row >> 1) & 7;
+  return kSwz == kSwz128 ? (((m & 1) << 2) | (m >> 1)) : (((m & 3) << 1) | (m >> 2));
+}
+template <int kSwz>
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-  return (uint32_t)(row * kRowLds + 16 * (chunk ^ (row & 7)));
+  return (uint32_t)(row * kRowLds + 16 * (chunk ^ swz_key<kSwz>(row)));
 }
 
 struct ItemRange {
@@ -89,7 +103,7 @@ __device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int t) {
 // the RoPE key), so all offsets are affine in k.  Rows past t_end and pages out
 // of range become zeros.
 // ===========================================================================
-template <int kTok>
+template <int kTok, int kSwz>
 struct LoaderBf16Reg {
   static constexpr int kPass = kTok / 32;
   u32x4 r[9 * kPass];
@@ -109,7 +123,7 @@ struct LoaderBf16Reg {
   }
   __device__ __forceinline__ void commit(char* lds_buf) const {
     const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz(tok, threadIdx.x & 7);
+    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -132,7 +146,7 @@ __device__ __forceinline__ u32x2 int8x4_to_f16(uint32_t c, half2v s) {
 }
 
 // INT8 page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key scales.
-template <int kTok>
+template <int kTok, int kSwz>
 struct LoaderInt8Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kPage = kBlock * 672;
@@ -159,7 +173,7 @@ struct LoaderInt8Reg {
   }
   __device__ __forceinline__ void commit(char* lds_buf) const {
     const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz(tok, threadIdx.x & 7);
+    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -174,7 +188,7 @@ struct LoaderInt8Reg {
 
 // INT4 page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32 scales
 //            | [64][16] f32 zeros | [64][8] f32 key scales.
-template <int kTok>
+template <int kTok, int kSwz>
 struct LoaderInt4Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kPage = kBlock * 480;
@@ -207,7 +221,7 @@ struct LoaderInt4Reg {
   }
   __device__ __forceinline__ void commit(char* lds_buf) const {
     const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz(tok, threadIdx.x & 7);
+    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
     const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
@@ -243,7 +257,7 @@ constexpr int kBuf128 = kTile128 * kRowLds;        // 36,864 B
 
 struct H128Lane {
   uint32_t qk_off[4];     // score operand: row hl, chunk 2 ks + g
-  uint32_t pv_off[2];     // transposed value read: row 4 g + (gi >> 2) (+16 j, +8)
+  uint32_t pv_off[4];     // transposed value read: row 4 g + (gi >> 2) + 8 hi (+16 j); [2 hi + parity]
   int g;
 };
 
@@ -253,11 +267,14 @@ __device__ __forceinline__ H128Lane h128_lane() {
   const int hl = lane & 31, g = lane >> 5, grp = lane >> 4, gi = lane & 15;
   L.g = g;
 #pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) L.qk_off[k4] = swz(hl, 2 * k4 + g);
-  const int pv_row = 4 * g + (gi >> 2);
+  for (int k4 = 0; k4 < 4; ++k4) L.qk_off[k4] = swz<kSwz128>(hl, 2 * k4 + g);
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    L.pv_off[par] = swz(pv_row, 4 * par + 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  for (int hi = 0; hi < 2; ++hi) {
+    const int pv_row = 4 * g + (gi >> 2) + 8 * hi;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      L.pv_off[2 * hi + par] = swz<kSwz128>(pv_row, 4 * par + 2 * (grp & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  }
   return L;
 }
 
@@ -282,15 +299,18 @@ __device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, co
     k1 = k2;
     k2 = kn;
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sacc[r] *= scale_log2;
+  if (!page_ok || t0 + kTile128 > t_end) {          // partial tile: mask the missing rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = t0 + 8 * (r >> 2) + 4 * L.g + (r & 3);
+      if (!page_ok || tt >= t_end) sacc[r] = -INFINITY;
+    }
+  }
   float mx = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tt = t0 + 8 * (r >> 2) + 4 * L.g + (r & 3);
-    float v = sacc[r] * scale_log2;
-    if (!page_ok || tt >= t_end) v = -INFINITY;
-    sacc[r] = v;
-    mx = fmaxf(mx, v);
-  }
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
   mx = wave_max_xor(mx, 32);               // lanes l and l^32 hold the same head
   if (kMode == 1) {
     m_ref = fmaxf(m_ref, mx);
@@ -314,9 +334,9 @@ __device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, co
   // 32 (i % 16) .. +31; the transposed reads run two steps ahead of the MFMAs.
   auto vread = [&](int i) -> half8 {
     const int j = i >> 4, tile = i & 15;
-    const uint32_t off = L.pv_off[tile & 1] + 16 * j * kRowLds + 128 * (tile >> 1);
-    const half4 lo = lds_read_tr(buf, off);
-    const half4 hi = lds_read_tr(buf, off + 8 * kRowLds);
+    const uint32_t off = 16 * j * kRowLds + 128 * (tile >> 1);
+    const half4 lo = lds_read_tr(buf, L.pv_off[tile & 1] + off);
+    const half4 hi = lds_read_tr(buf, L.pv_off[2 + (tile & 1)] + off);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   half8 v0 = vread(0), v1 = vread(1);
@@ -374,7 +394,7 @@ struct DmaBf16Tile {
     const uint32_t o = loff + 1024 * k;
     const uint32_t row = o / kRowLds;
     const uint32_t pc = (o - row * kRowLds) >> 4;
-    return row * kRowBytesBf16 + 16 * (pc ^ (row & 7));
+    return row * kRowBytesBf16 + 16 * (pc ^ swz_key<kSwz128>((int)row));
   }
   // The load is issued through inline assembly so that the compiler does not
   // track it: otherwise it waits for every outstanding direct load before any
@@ -457,13 +477,14 @@ __device__ __forceinline__ void h128_pass_dma(const DecodeArgs& a, const ItemRan
     for (int s = 0; s < n_tiles; ++s) {
       __syncthreads();                     // tile s converted by all; tile s-1 no longer read
       if (s + 3 < n_tiles && any_pages) D.issue(tile_src(s + 3), lds + ((s + 3) & 3) * kBuf128);
+      const int t0 = seg0 + s * kTile128;
+      h128_tile<kMode>(lds + (s & 3) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, seg1, page_at(s) >= 0,
+                       a.scale_log2);
+      // Widen this lane's share of the next tile while the value MFMAs drain.
       if (s + 1 < n_tiles) {
         wait_vm_tiles(any_pages ? min(2, n_tiles - 1 - (s + 1)) : 0);
         D.convert(lds + ((s + 1) & 3) * kBuf128, valid_rows(s + 1));
       }
-      const int t0 = seg0 + s * kTile128;
-      h128_tile<kMode>(lds + (s & 3) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, seg1, page_at(s) >= 0,
-                       a.scale_log2);
     }
     wait_vm<0>();
   }
@@ -514,7 +535,8 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
       h128_pass_dma<2>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
     }
   } else {
-    using Loader = typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128>, LoaderInt4Reg<kTile128>>::type;
+    using Loader = typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128, kSwz128>,
+                                              LoaderInt4Reg<kTile128, kSwz128>>::type;
     h128_pass_reg<Loader, 0>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
     if (__syncthreads_or(overflow)) {
       m_ref = -INFINITY;
@@ -584,11 +606,11 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
   const int tw = 16 * wave;                                          // this wave's rows
   uint32_t qk_off[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) qk_off[par] = swz(tw + hl, 4 * par + grp);
+  for (int par = 0; par < 2; ++par) qk_off[par] = swz<kSwz16>(tw + hl, 4 * par + grp);
   const int pv_row = tw + 4 * grp + (hl >> 2);
   uint32_t pv_off[4];
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4) pv_off[t4] = swz(pv_row, 2 * t4 + ((hl & 3) >> 1)) + 8 * (hl & 1);
+  for (int t4 = 0; t4 < 4; ++t4) pv_off[t4] = swz<kSwz16>(pv_row, 2 * t4 + ((hl & 3) >> 1)) + 8 * (hl & 1);
 
   for (int s = 0; s < n_tiles; ++s) {
     __syncthreads();
@@ -691,6 +713,10 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+using H16Bf16 = LoaderBf16Reg<kTile16, kSwz16>;
+using H16Int8 = LoaderInt8Reg<kTile16, kSwz16>;
+using H16Int4 = LoaderInt4Reg<kTile16, kSwz16>;
+
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid(a.n_items), block(256);
@@ -700,9 +726,9 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
-    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<LoaderBf16Reg<kTile16>>, grid, block, 0, stream, a);
-    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<LoaderInt8Reg<kTile16>>, grid, block, 0, stream, a);
-    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<LoaderInt4Reg<kTile16>>, grid, block, 0, stream, a);
+    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<H16Bf16>, grid, block, 0, stream, a);
+    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<H16Int8>, grid, block, 0, stream, a);
+    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
