@@ -101,8 +101,10 @@ def recorded_traffic(workload, cache_dtype):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The card runs this workload at its power limit, and its clock settles only
+    # after some tens of milliseconds of sustained load: warm up for ~0.3 s.
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="v3_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cache-dtype", default="bf16", choices=sorted(DTYPES))
     ap.add_argument("--chunk-pages", type=int, default=0)

@@ -11,29 +11,30 @@
 //
 // gfx950 design
 //   * One work-group (4 wave64s) per work item; the item's tokens stream through
-//     LDS in tiles of fp16 rows (1,152 B, 16-byte chunks XOR-swizzled by row).
-//   * H = 128: wave w owns heads 32w..32w+31 and the whole 32-token tile:
-//       S^T[32 tok x 32 head] = K[32 x 576] . Q^T    36 x mfma 32x32x16 (K from LDS,
-//                                                     Q resident in VGPRs)
-//       O^T[512 x 32 head] += V^T . P^T               32 x mfma 32x32x16 (V^T read from
-//                                                     the same row-major tile with
-//                                                     ds_read_b64_tr_b16; P^T is the
-//                                                     score accumulator's own layout)
-//     so all 128 heads share each LDS read of the latent.  bf16 tiles arrive by
-//     direct global->LDS loads (no VGPRs) into a 4-tile ring and are widened to
-//     fp16 in place by the lane that loaded them; two tiles stay in flight.
+//     LDS in tiles of fp16 rows (1,152 B, 16-byte chunks XOR-swizzled by row so
+//     that every MFMA operand fetch is free of bank conflicts).
+//   * Tiles are staged through VGPRs: each thread loads its share of the next
+//     tile one tile ahead, widens bf16 -> fp16 (or dequantises) in registers and
+//     writes it to the other LDS buffer.  Loads and conversions are woven into
+//     the matrix-instruction stream, so they run in the MFMA shadow.
+//   * H = 128 (per 32-token tile): wave w computes the scores of heads
+//     32w..32w+31 (S^T = K . Q^T, 36 x mfma 32x32x16, K from LDS, Q^T mostly in
+//     VGPRs), writes fp16 P to a small LDS exchange buffer, and then the value
+//     product for features 128w..128w+127 of all 128 heads (O^T += V^T . P^T,
+//     32 x mfma 32x32x16, V^T read transposed with ds_read_b64_tr_b16).  Every
+//     wave thus reads all of K but only a quarter of V: on this part the LDS,
+//     more than the matrix cores, bounds the rate, and the chip's power limit
+//     bounds the clock.
 //   * H = 16: each wave takes 16 tokens of a 64-token page for all 16 heads
 //     (mfma 16x16x32 scores, 16x16x16 values); the four waves' (max, sum, O) are
 //     merged through LDS at the end.
-//   * Quantised tiles, and H = 16, use register prefetch one tile ahead and a
-//     2-tile LDS ring.
 //   * Softmax in the log2 domain.  H = 128 fixes each head's reference max at its
 //     first non-empty tile and never rescales O inside the loop (P <= 2^15 fits
 //     fp16); if a later tile exceeds that by more than 2^15 the item is redone
 //     against exact maxima (one scores-only pass, one accumulate pass).  H = 16
 //     rescales lazily (only when the max grows by more than 2^8).
 //   * Tokens past the item's end, or on pages whose id is outside the pool, are
-//     zero-filled in LDS and masked to -inf.
+//     loaded from an all-zero page and masked to -inf.
 #include <type_traits>
 
 #include "common.h"
@@ -95,33 +96,90 @@ __device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int t) {
   return (p >= 0 && p < a.num_pages) ? p : -1;
 }
 
+// Every pipeline looks its pages up in an LDS copy of the item's block-table
+// slice, refreshed every kSegPages pages: a global read of the table inside a
+// tile loop would make the compiler's wait for it also drain the tile prefetch
+// issued before it (vector-memory counters retire in order).
+constexpr int kSegPages = 2048;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 |
+// lgkmcnt[11:8] = 15 | vmcnt[5:4] in bits [15:14]).
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((kN & 15) | (7 << 4) | (15 << 8) | ((kN >> 4) << 14));
+}
+__device__ __forceinline__ void fill_ptab(const DecodeArgs& a, int b, int t0, int t1, int32_t* ptab) {
+  const int n = (t1 - t0 + kBlock - 1) / kBlock;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ptab[i] = (int32_t)page_of(a, b, t0 + i * kBlock);
+}
+
 // ===========================================================================
-// Register-prefetch tile loaders: issue() loads a tile into registers, commit()
-// writes it as fp16 rows into an LDS buffer.  kTok tokens (32 or 64), starting
-// at a multiple of kTok within a page.  Thread tid owns token (tid >> 3) of each
-// 32-token pass and the 16-byte output chunks (tid & 7) + 8k, k = 0..8 (k = 8 is
-// the RoPE key), so all offsets are affine in k.  Rows past t_end and pages out
-// of range become zeros.
+// Register-prefetch tile loaders: issue() loads a tile of physical page `page`
+// (-1: out of range) into registers, commit() writes it as fp16 rows into an LDS
+// buffer.  kTok tokens (32 or 64), starting at a multiple of kTok within a page.
+// Thread tid owns token (tid >> 3) of each 32-token pass and the 16-byte output
+// chunks (tid & 7) + 8k, k = 0..8 (k = 8 is the RoPE key), so all offsets are
+// affine in k.  Both are free of branches, so that a caller can interleave them
+// with matrix instructions: a row past t_end, or on a page out of range, is
+// loaded from an all-zero page and so written as zeros.
 // ===========================================================================
+
+// Rows that are out of range are read from this all-zero page instead (device
+// globals start zeroed; it is as large as the largest page format, so every
+// field offset stays valid), and every cache format decodes zero bytes to zeros.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_page[kBlock * kRowBytesBf16];
+
+// Base of page `page`, or of the zero page when the row is out of range.
+__device__ __forceinline__ const uint8_t* page_base(const DecodeArgs& a, int64_t page, bool ok, int64_t page_bytes) {
+  return ok ? a.pool + page * page_bytes : g_zero_page;
+}
+
+
 template <int kTok, int kSwz>
 struct LoaderBf16Reg {
   static constexpr int kPass = kTok / 32;
+  static constexpr int kScorePrefetch = 3;   // K fragments in flight in the 128-head score loop
   u32x4 r[9 * kPass];
 
-  __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
-    const int64_t page = page_of(a, b, t0);
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = threadIdx.x >> 3;
-    const uint8_t* base = a.pool + (page < 0 ? 0 : page) * (int64_t)(kBlock * kRowBytesBf16) +
-                          (int64_t)((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (threadIdx.x & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const uint8_t* src = page_base(a, page, ok, kBlock * kRowBytesBf16) +
+                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (threadIdx.x & 7);
 #pragma unroll
-      for (int k = 0; k < 9; ++k)
-        r[9 * p + k] = ok ? ld16_stream(base + 32 * p * kRowBytesBf16 + 128 * k) : u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < 9; ++k) r[9 * p + k] = ld16_stream(src + 128 * k);
     }
+    return page >= 0;
   }
-  __device__ __forceinline__ void commit(char* lds_buf) const {
+  // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's row
+  // source; load_step<I>, called right after store_step<I>, reloads the
+  // registers that store freed, so the loads trickle out one per MFMA.
+  const uint8_t* src;
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = threadIdx.x >> 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (threadIdx.x & 7);
+  }
+  template <int I>
+  __device__ __forceinline__ void load_step() {
+    r[I] = ld16_stream(src + 128 * I);
+  }
+  // Staging in two stages (one pass): widen_step<I> converts dword I % 4 of chunk
+  // I / 4 in place (36 steps, one per score MFMA); store_step<I> writes chunk I.
+  static constexpr int kWidenSteps = 36, kStoreSteps = 9;
+  template <int I>
+  __device__ __forceinline__ void widen_step() {
+    uint32_t v = bf16x2_to_f16x2(r[I / 4][I % 4]);
+    asm volatile("" : "+v"(v));   // keep the conversion here, not sunk to the store
+    r[I / 4][I % 4] = v;
+  }
+  template <int I>
+  __device__ __forceinline__ void store_step(char* lds_buf) {
+    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * I) = r[I];
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
     const int tok = threadIdx.x >> 3;
     char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
 #pragma unroll
@@ -149,29 +207,70 @@ __device__ __forceinline__ u32x2 int8x4_to_f16(uint32_t c, half2v s) {
 template <int kTok, int kSwz>
 struct LoaderInt8Reg {
   static constexpr int kPass = kTok / 32;
+  static constexpr int kScorePrefetch = 3;
   static constexpr int kPage = kBlock * 672;
   u32x2 c[9 * kPass];
   float s[9 * kPass];
 
-  __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
-    const int64_t page = page_of(a, b, t0);
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
-    const uint8_t* pg = a.pool + (page < 0 ? 0 : page) * (int64_t)kPage;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
-      const int row = (t0 % kBlock) + 32 * p + tok;
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const int row = (t0 % kBlock) + 32 * p + tok;
+      const uint8_t* pg = page_base(a, page, ok, kPage);
       const uint8_t* codes = pg + row * 576 + 8 * c8;
       const float* cs = reinterpret_cast<const float*>(pg + 64 * 576) + row * 16 + (c8 >> 2);
       const float* ks = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64) + row * 8 + c8;
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        c[9 * p + k] = ok ? *reinterpret_cast<const u32x2*>(codes + 64 * k) : u32x2{0u, 0u};
-        s[9 * p + k] = ok ? (k < 8 ? cs[2 * k] : ks[0]) : 0.f;
+        c[9 * p + k] = *reinterpret_cast<const u32x2*>(codes + 64 * k);
+        s[9 * p + k] = k < 8 ? cs[2 * k] : ks[0];
       }
     }
+    return page >= 0;
   }
-  __device__ __forceinline__ void commit(char* lds_buf) const {
+  // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's page
+  // and row; load_step<I> (after store_step<I>) reloads chunk I / 2 once its
+  // store is done (odd I).
+  const uint8_t* pg;
+  int row;
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = threadIdx.x >> 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    pg = page_base(a, page, ok, kPage);
+    row = (t0 % kBlock) + tok;
+  }
+  template <int I>
+  __device__ __forceinline__ void load_step() {
+    if constexpr (I % 2 == 1) {
+      constexpr int k = I / 2;
+      const int c8 = threadIdx.x & 7;
+      c[k] = *reinterpret_cast<const u32x2*>(pg + row * 576 + 8 * c8 + 64 * k);
+      if constexpr (k < 8) s[k] = reinterpret_cast<const float*>(pg + 64 * 576)[row * 16 + (c8 >> 2) + 2 * k];
+      else s[k] = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64)[row * 8 + c8];
+    }
+  }
+  // Stepwise commit: step 2c dequantises the first four codes of chunk c, step
+  // 2c+1 the other four and stores the chunk.
+  static constexpr int kWidenSteps = 0, kStoreSteps = 18 * kPass;
+  template <int I>
+  __device__ __forceinline__ void widen_step() {}
+  u32x2 part;
+  template <int I>
+  __device__ __forceinline__ void store_step(char* lds_buf) {
+    constexpr int kc = I / 2, p = kc / 9, k = kc % 9;
+    const _Float16 sh = (_Float16)s[kc];
+    const half2v s2 = {sh, sh};
+    if constexpr (I % 2 == 0) {
+      part = int8x4_to_f16(c[kc][0], s2);
+    } else {
+      const u32x2 hi = int8x4_to_f16(c[kc][1], s2);
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 32 * p * kRowLds + 128 * k) =
+          u32x4{part[0], part[1], hi[0], hi[1]};
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
     const int tok = threadIdx.x >> 3;
     char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
 #pragma unroll
@@ -191,38 +290,102 @@ struct LoaderInt8Reg {
 template <int kTok, int kSwz>
 struct LoaderInt4Reg {
   static constexpr int kPass = kTok / 32;
+  static constexpr int kScorePrefetch = 2;    // its staging registers leave room for two
   static constexpr int kPage = kBlock * 480;
   uint32_t n[8 * kPass];     // 8 nibbles (latent chunk k) per dword
   u32x2 kc[kPass];           // 8 key codes (chunk 8)
   float s[9 * kPass];        // scale per chunk (k = 8: key scale)
   float z[8 * kPass];        // zero point per latent chunk
 
-  __device__ __forceinline__ void issue(const DecodeArgs& a, int b, int t0, int t_end) {
-    const int64_t page = page_of(a, b, t0);
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
-    const uint8_t* pg = a.pool + (page < 0 ? 0 : page) * (int64_t)kPage;
-    const float* scales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
-    const float* zeros = scales + 64 * 16;
-    const float* kscales = zeros + 64 * 16;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
-      const int row = (t0 % kBlock) + 32 * p + tok;
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const int row = (t0 % kBlock) + 32 * p + tok;
+      const uint8_t* pg = page_base(a, page, ok, kPage);
+      const float* scales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + row * 16 + (c8 >> 2);
+      const float* zeros = scales + 64 * 16;
+      const float* kscales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + 2 * 64 * 16 + row * 8 + c8;
       const uint8_t* nib = pg + row * 256 + 4 * c8;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        n[8 * p + k] = ok ? *reinterpret_cast<const uint32_t*>(nib + 32 * k) : 0u;
-        s[9 * p + k] = ok ? scales[row * 16 + 2 * k + (c8 >> 2)] : 0.f;
-        z[8 * p + k] = ok ? zeros[row * 16 + 2 * k + (c8 >> 2)] : 0.f;
+        n[8 * p + k] = *reinterpret_cast<const uint32_t*>(nib + 32 * k);
+        s[9 * p + k] = scales[2 * k];
+        z[8 * p + k] = zeros[2 * k];
       }
-      kc[p] = ok ? *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8) : u32x2{0u, 0u};
-      s[9 * p + 8] = ok ? kscales[row * 8 + c8] : 0.f;
+      kc[p] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
+      s[9 * p + 8] = kscales[0];
+    }
+    return page >= 0;
+  }
+  // Byte j of nibble word w (elements 2j, 2j+1) -> two fp16 values q * s + z.
+  static __device__ __forceinline__ uint32_t nib2(uint32_t w, int j, half2v s2, half2v z2) {
+    const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    const uint32_t byte = (w >> (8 * j)) & 0xffu;
+    // (element 2j, element 2j+1) = (low nibble, high nibble) as fp16 1024 + q
+    const uint32_t h = 0x64006400u | (byte & 0xfu) | ((byte >> 4) << 16);
+    const half2v qv = __builtin_bit_cast(half2v, h) + bias;
+    return __builtin_bit_cast(uint32_t, qv * s2 + z2);
+  }
+  // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's page
+  // and row; load_step<I> (after store_step<I>) reloads chunk I / 2 once its
+  // store is done (odd I).
+  const uint8_t* pg;
+  int row;
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = threadIdx.x >> 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    pg = page_base(a, page, ok, kPage);
+    row = (t0 % kBlock) + tok;
+  }
+  template <int I>
+  __device__ __forceinline__ void load_step() {
+    if constexpr (I % 2 == 1) {
+      constexpr int k = I / 2;
+      const int c8 = threadIdx.x & 7;
+      const float* meta = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
+      if constexpr (k < 8) {
+        n[k] = *reinterpret_cast<const uint32_t*>(pg + row * 256 + 4 * c8 + 32 * k);
+        s[k] = meta[row * 16 + (c8 >> 2) + 2 * k];
+        z[k] = meta[64 * 16 + row * 16 + (c8 >> 2) + 2 * k];
+      } else {
+        kc[0] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
+        s[8] = meta[2 * 64 * 16 + row * 8 + c8];
+      }
     }
   }
-  __device__ __forceinline__ void commit(char* lds_buf) const {
+  // Stepwise commit: step 2c converts the first half of 16-byte chunk c, step
+  // 2c+1 the second half and stores the chunk (chunk 8 of a pass is the key).
+  static constexpr int kWidenSteps = 0, kStoreSteps = 18 * kPass;
+  template <int I>
+  __device__ __forceinline__ void widen_step() {}
+  u32x2 part;
+  template <int I>
+  __device__ __forceinline__ void store_step(char* lds_buf) {
+    constexpr int kcx = I / 2, p = kcx / 9, k = kcx % 9;
+    u32x2 cur;
+    if constexpr (k < 8) {
+      const _Float16 sh = (_Float16)s[9 * p + k], zh = (_Float16)z[8 * p + k];
+      const half2v s2 = {sh, sh}, z2 = {zh, zh};
+      const uint32_t w = n[8 * p + k];
+      constexpr int j0 = 2 * (I % 2);
+      cur = u32x2{nib2(w, j0, s2, z2), nib2(w, j0 + 1, s2, z2)};
+    } else {
+      const _Float16 kh = (_Float16)s[9 * p + 8];
+      const half2v k2 = {kh, kh};
+      cur = int8x4_to_f16(kc[p][I % 2], k2);
+    }
+    if constexpr (I % 2 == 0) {
+      part = cur;
+    } else {
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 32 * p * kRowLds + 128 * k) =
+          u32x4{part[0], part[1], cur[0], cur[1]};
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
     const int tok = threadIdx.x >> 3;
     char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
-    const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
 #pragma unroll
@@ -232,13 +395,7 @@ struct LoaderInt4Reg {
         const uint32_t w = n[8 * p + k];
         u32x4 v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t byte = (w >> (8 * j)) & 0xffu;
-          // (element 2j, element 2j+1) = (low nibble, high nibble) as fp16 1024 + q
-          const uint32_t h = 0x64006400u | (byte & 0xfu) | ((byte >> 4) << 16);
-          const half2v qv = __builtin_bit_cast(half2v, h) + bias;
-          v[j] = __builtin_bit_cast(uint32_t, qv * s2 + z2);
-        }
+        for (int j = 0; j < 4; ++j) v[j] = nib2(w, j, s2, z2);
         *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = v;
       }
       const _Float16 kh = (_Float16)s[9 * p + 8];
@@ -252,20 +409,51 @@ struct LoaderInt4Reg {
 // ===========================================================================
 // H = 128
 // ===========================================================================
+// Per 32-token tile and wave w (4 waves, one work-group per work item):
+//   scores   S^T[32 tok x 32 heads] for heads 32w..32w+31 over all 576 columns:
+//            36 x mfma 32x32x16 (K fragments from the LDS tile, Q^T in VGPRs);
+//   softmax  per head against a fixed reference max; P (fp16) is written to a
+//            small LDS exchange buffer [128 heads][32 tokens];
+//   values   O^T[128 features x 128 heads] for features 128w..128w+127:
+//            32 x mfma 32x32x16 (V^T read transposed from the tile, P^T of all
+//            heads from the exchange buffer).
+// Splitting the value product by features rather than heads makes every wave
+// read only its quarter of V; the LDS, not the matrix cores, is the scarce unit.
+// The next tile is staged meanwhile: its rows sit in VGPRs (loaded one tile
+// ahead), are widened to fp16 and written to the other LDS buffer between the
+// value MFMAs; then the loads for the tile after it are issued.
 constexpr int kTile128 = 32;
 constexpr int kBuf128 = kTile128 * kRowLds;        // 36,864 B
+constexpr int kPRow = 2 * kTile128;                // P exchange row: 32 tokens x fp16
+constexpr int kPBuf = 128 * kPRow;                 // 8,192 B
 
 struct H128Lane {
-  uint32_t qk_off[4];     // score operand: row hl, chunk 2 ks + g
-  uint32_t pv_off[4];     // transposed value read: row 4 g + (gi >> 2) + 8 hi (+16 j); [2 hi + parity]
-  int g;
+  uint32_t qk_off[4];     // score operand: row hl, chunk 2 k4 + g
+  uint32_t pv_off[4];     // transposed value read: row 4 g + (gi >> 2) + 8 hi; [2 hi + parity]
+  int g, hl;
+  // P exchange: head hl's 16 bytes for token half j (head group 0).
+  __device__ __forceinline__ uint32_t p_off(int j) const { return hl * kPRow + 16 * ((2 * j + g) ^ ((hl >> 2) & 3)); }
 };
 
+// Q^T of the first kQReg k-steps (16 columns each) stays in VGPRs; the last
+// kQTail k-steps (128 latent columns and the 64 RoPE columns) of all 128 heads
+// live in LDS, which leaves the VGPRs the tile pipeline needs.  Row h (256 B)
+// holds q_abs[b][h][448..575], 16-byte chunk c stored at c ^ (h & 15), so the 16
+// heads a lane group reads land in distinct banks.
+constexpr int kQReg = 28, kQTail = kDk / 16 - kQReg;
+constexpr int kQTailRow = kQTail * 32;                    // 256 B
+constexpr int kQTailBytes = 128 * kQTailRow;              // 32,768 B
+__device__ __forceinline__ uint32_t qtail_off(int h, int c) { return h * kQTailRow + 16 * (c ^ (h & 15)); }
+
+// P exchange layout: row h (64 B) holds, for token half j and lane group g, the
+// eight fp16 values lane (g, h % 32) of the owning wave computed, in the 16-byte
+// chunk (2 j + g) ^ ((h >> 2) & 3) (the XOR keeps 16-lane accesses conflict free).
 __device__ __forceinline__ H128Lane h128_lane() {
   H128Lane L;
   const int lane = threadIdx.x & 63;
   const int hl = lane & 31, g = lane >> 5, grp = lane >> 4, gi = lane & 15;
   L.g = g;
+  L.hl = hl;
 #pragma unroll
   for (int k4 = 0; k4 < 4; ++k4) L.qk_off[k4] = swz<kSwz128>(hl, 2 * k4 + g);
 #pragma unroll
@@ -278,27 +466,65 @@ __device__ __forceinline__ H128Lane h128_lane() {
   return L;
 }
 
-// One 32-token tile of work for one wave.  kMode 0: accumulate with a per-head
-// reference max fixed at the head's first non-empty tile (sets `overflow` when a
-// later tile exceeds it by more than kTauFixed); kMode 1: scores only, m_ref
-// becomes the exact max; kMode 2: accumulate against the exact max in m_ref.
-template <int kMode>
-__device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, const half8 (&q)[kDk / 16],
-                                          floatx16 (&o)[16], float& m_ref, float& l_sum, bool& overflow,
-                                          int t0, int t_end, bool page_ok, float scale_log2) {
-  auto kread = [&](int ks) -> half8 {
+// Score MFMA chain of one tile, as fenced steps: step ks issues MFMA ks, the
+// K (and, for the RoPE columns, Q^T) fragment reads kPf steps ahead, and one
+// widening step of the staged next tile, whose VALU work then runs in the
+// running MFMA's shadow.  kPf is as deep as the registers allow without
+// spilling: a spill reload here would wait behind the tile loads in flight
+// (vector-memory counters retire in order).
+template <int kPf, class Loader>
+struct H128Scores {
+  const char* buf;
+  const char* qtail;
+  const H128Lane& L;
+  const half8 (&q)[kQReg];
+  Loader& ld;
+  int hq;
+  floatx16 sacc;
+  half8 kb[kPf], qb[kPf];
+  static constexpr int kSteps = kDk / 16;
+
+  __device__ __forceinline__ half8 kread(int ks) const {
     return *reinterpret_cast<const half8*>(buf + L.qk_off[ks & 3] + 128 * (ks >> 2));
-  };
-  floatx16 sacc = floatx16{};
-  half8 k0 = kread(0), k1 = kread(1), k2 = kread(2);
-#pragma unroll
-  for (int ks = 0; ks < kDk / 16; ++ks) {
-    const half8 kn = (ks + 3 < kDk / 16) ? kread(ks + 3) : k2;
-    sacc = mfma32x32x16(k0, q[ks], sacc);
-    k0 = k1;
-    k1 = k2;
-    k2 = kn;
   }
+  template <int KS>
+  __device__ __forceinline__ void step() {
+    if constexpr (KS < kQReg) sacc = mfma32x32x16(kb[KS % kPf], q[KS], sacc);
+    else sacc = mfma32x32x16(kb[KS % kPf], qb[KS % kPf], sacc);
+    constexpr int kn = KS + kPf;
+    if constexpr (kn < kSteps) {
+      kb[KS % kPf] = kread(kn);
+      if constexpr (kn >= kQReg)
+        qb[KS % kPf] = *reinterpret_cast<const half8*>(qtail + qtail_off(hq, 2 * (kn - kQReg) + L.g));
+    }
+    if constexpr (KS < Loader::kWidenSteps) ld.template widen_step<KS>();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KS + 1 < kSteps) step<KS + 1>();
+  }
+  __device__ __forceinline__ floatx16 run() {
+    static_assert(Loader::kWidenSteps <= kSteps, "widening must fit in the score chain");
+    __builtin_amdgcn_sched_barrier(0);
+    sacc = floatx16{};
+#pragma unroll
+    for (int d = 0; d < kPf; ++d) kb[d] = kread(d);
+    static_assert(kQReg >= kPf, "the first Q^T fragments come from VGPRs");
+    __builtin_amdgcn_sched_barrier(0);
+    step<0>();
+    return sacc;
+  }
+};
+
+// Scores and softmax of one tile for this wave's 32 heads.  kMode 0: fixed
+// reference max per head, taken at its first non-empty tile (`overflow` is set
+// when a later tile exceeds it by more than kTauFixed); kMode 1: scores only,
+// m_ref becomes the exact max; kMode 2: against the exact max in m_ref.
+// Returns P^T as the value product's B operand (p[j]: token half j).
+template <int kMode, int kPf, class Loader>
+__device__ __forceinline__ void h128_scores(const char* buf, const char* qtail, const H128Lane& L,
+                                            const half8 (&q)[kQReg], Loader& ld, float& m_ref, float& l_sum,
+                                            bool& overflow, int t0, int t_end, bool page_ok, float scale_log2,
+                                            half8 (&p)[2]) {
+  floatx16 sacc = H128Scores<kPf, Loader>{buf, qtail, L, q, ld, 32 * (int)(threadIdx.x >> 6) + L.hl}.run();
 #pragma unroll
   for (int r = 0; r < 16; ++r) sacc[r] *= scale_log2;
   if (!page_ok || t0 + kTile128 > t_end) {          // partial tile: mask the missing rows
@@ -321,7 +547,6 @@ __device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, co
     overflow |= mx > m_ref + kTauFixed;
   }
   const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-  half8 p[2];
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -330,238 +555,228 @@ __device__ __forceinline__ void h128_tile(const char* buf, const H128Lane& L, co
     p[r >> 3][r & 7] = (_Float16)e;
   }
   l_sum += psum;
-  // O^T += V^T . P^T: step i covers tokens 16 (i / 16) .. +15 and features
-  // 32 (i % 16) .. +31; the transposed reads run two steps ahead of the MFMAs.
-  auto vread = [&](int i) -> half8 {
-    const int j = i >> 4, tile = i & 15;
-    const uint32_t off = 16 * j * kRowLds + 128 * (tile >> 1);
-    const half4 lo = lds_read_tr(buf, L.pv_off[tile & 1] + off);
-    const half4 hi = lds_read_tr(buf, L.pv_off[2 + (tile & 1)] + off);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  half8 v0 = vread(0), v1 = vread(1);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const half8 vn = (i + 2 < 32) ? vread(i + 2) : v1;
-    o[i & 15] = mfma32x32x16(v0, p[i >> 4], o[i & 15]);
-    v0 = v1;
-    v1 = vn;
-  }
 }
 
-// ---- pipeline A: register prefetch, 2-tile ring (quantised formats) ----------
-template <class Loader, int kMode>
-__device__ __forceinline__ void h128_pass_reg(const DecodeArgs& a, const ItemRange& it, char* lds,
-                                              const H128Lane& L, const half8 (&q)[kDk / 16], floatx16 (&o)[16],
-                                              float& m_ref, float& l_sum, bool& overflow) {
-  const int n_tiles = (it.t_end - it.t_begin + kTile128 - 1) / kTile128;
-  Loader ld;
-  if (n_tiles > 0) {
-    ld.issue(a, it.b, it.t_begin, it.t_end);
-    __syncthreads();                       // earlier users of the buffers are done
-    ld.commit(lds);
-    if (n_tiles > 1) ld.issue(a, it.b, it.t_begin + kTile128, it.t_end);
-  }
-  for (int s = 0; s < n_tiles; ++s) {
-    __syncthreads();                       // tile s visible; buffer (s+1)&1 free
-    if (s + 1 < n_tiles) {
-      ld.commit(lds + ((s + 1) & 1) * kBuf128);
-      if (s + 2 < n_tiles) ld.issue(a, it.b, it.t_begin + (s + 2) * kTile128, it.t_end);
-    }
-    const int t0 = it.t_begin + s * kTile128;
-    h128_tile<kMode>(lds + (s & 1) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, it.t_end,
-                     page_of(a, it.b, t0) >= 0, a.scale_log2);
-  }
-}
-
-// ---- pipeline B: direct global->LDS loads, 4-tile ring (bf16) ----------------
-// Wave w fills LDS bytes [9216 w, 9216 w + 9216) of a tile with 9 loads of
-// 64 lanes x 16 B; the lane writing LDS offset o carries the global chunk
-// (row = o / 1152, logical chunk = physical chunk ^ (row & 7)).  After its own
-// loads have landed, each lane widens exactly those 16 bytes to fp16 in place
-// (or zeroes them for rows past the end / bad pages), so no other lane's data
-// is touched before the next barrier.
-struct DmaBf16Tile {
-  uint32_t loff;          // LDS byte offset of this lane's chunk 0 within a tile
+// Value product of one tile for this wave's 128 features and all 128 heads,
+// with the staging of the next tile woven in.  MFMA I = 16 j + 4 f + hg
+// accumulates O^T[feature block 4 wave + f][head group hg] over token half j.
+// Each step holds one MFMA, the operand reads for four MFMAs later and one
+// staging piece (an LDS store, or dequantisation and store for the quantised
+// formats, followed by the load that refills the registers it freed), fenced so
+// that the scheduler keeps that order: the staging work then executes in the
+// shadow of the running MFMA, and the loads trickle out one per MFMA instead of
+// stalling the wave on the address queue as a burst would.  P^T of
+// token half j stays in pt[] while its 16 MFMAs run (the next half's fragment
+// hg replaces it right after its last use); V^T fragments alternate between two
+// buffers.
+template <class Loader, class Begin>
+struct H128Values {
+  const char* buf;
+  const char* pbuf;
+  const H128Lane& L;
   int wave;
+  floatx16 (&o)[16];
+  Loader& ld;
+  char* nxt;
+  Begin& begin;
+  half8 pt[4], vb[2];
+  // Stores of the staged tile start at this step: spread one per MFMA when they
+  // are plain stores (widened during the scores), from step 0 otherwise.
+  static constexpr int kStoreAt = Loader::kWidenSteps > 0 ? 4 : 0;
 
-  __device__ __forceinline__ void init() {
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    loff = 9216 * wave + 16 * (threadIdx.x & 63);
+  // V^T fragment (32 features x 16 tokens) for feature block 4 wave + f, token half j.
+  __device__ __forceinline__ half8 vread(int j, int f) const {
+    const int blk = 4 * wave + f;
+    const uint32_t off = 16 * j * kRowLds + 128 * (blk >> 1);
+    const half4 lo = lds_read_tr(buf, L.pv_off[blk & 1] + off);
+    const half4 hi = lds_read_tr(buf, L.pv_off[2 + (blk & 1)] + off);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Byte offset, from the tile's first cache row, of the chunk lane-slot k carries.
-  __device__ __forceinline__ uint32_t goff(int k) const {
-    const uint32_t o = loff + 1024 * k;
-    const uint32_t row = o / kRowLds;
-    const uint32_t pc = (o - row * kRowLds) >> 4;
-    return row * kRowBytesBf16 + 16 * (pc ^ swz_key<kSwz128>((int)row));
+  __device__ __forceinline__ half8 pread(int j, int hg) const {
+    return *reinterpret_cast<const half8*>(pbuf + hg * 32 * kPRow + L.p_off(j));
   }
-  // The load is issued through inline assembly so that the compiler does not
-  // track it: otherwise it waits for every outstanding direct load before any
-  // LDS read it cannot prove disjoint, which would serialise the ring.  The
-  // waits are placed explicitly (wait_vm_tiles) instead.
-  __device__ __forceinline__ void issue(const uint8_t* src, char* lds_tile) const {
-    const uint32_t lds_base =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds_tile + 9216 * wave);
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const uint8_t* g = src + goff(k);
-      asm volatile(
-          "s_mov_b32 m0, %1\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %0, off"
-          :
-          : "v"(g), "s"(lds_base + 1024 * k)
-          : "memory", "m0");
+  template <int I>
+  __device__ __forceinline__ void step() {
+    constexpr int j = I >> 4, f = (I >> 2) & 3, hg = I & 3;
+    o[4 * f + hg] = mfma32x32x16(vb[f & 1], pt[hg], o[4 * f + hg]);
+    if constexpr (hg == 0 && I + 4 < 32) vb[(f + 1) & 1] = vread((I + 4) >> 4, ((I + 4) >> 2) & 3);
+    if constexpr (j == 0 && f == 3) pt[hg] = pread(1, hg);
+    if constexpr (I < kStoreAt + Loader::kStoreSteps && I >= kStoreAt) {
+      ld.template store_step<I - kStoreAt>(nxt);
+      if constexpr (I == kStoreAt) begin();
+      __builtin_amdgcn_sched_barrier(0);     // the refill may not overtake the store of the same registers
+      ld.template load_step<I - kStoreAt>();
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (I + 1 < 32) step<I + 1>();
   }
-  __device__ __forceinline__ void convert(char* lds_tile, int valid_rows) const {
-    u32x4 v[9];
+  __device__ __forceinline__ void run() {
+    static_assert(kStoreAt + Loader::kStoreSteps < 32, "staging must fit in the value product");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < 9; ++k) v[k] = *reinterpret_cast<const u32x4*>(lds_tile + loff + 1024 * k);
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const uint32_t o = loff + 1024 * k;
-      const int row = (int)(o / kRowLds);
-      *reinterpret_cast<u32x4*>(lds_tile + o) = row < valid_rows ? bf16x8_to_f16x8(v[k]) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int hg = 0; hg < 4; ++hg) pt[hg] = pread(0, hg);
+    vb[0] = vread(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step<0>();
   }
 };
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 |
-// lgkmcnt[11:8] = 15 | vmcnt[5:4] in bits [15:14]).
-template <int kN>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((kN & 15) | (7 << 4) | (15 << 8) | ((kN >> 4) << 14));
-}
-// Wait until this wave's loads for a tile have landed while `tiles_after` later
-// tiles (9 loads each) may still be in flight.
-__device__ __forceinline__ void wait_vm_tiles(int tiles_after) {
-  if (tiles_after >= 2) wait_vm<18>();
-  else if (tiles_after == 1) wait_vm<9>();
-  else wait_vm<0>();
+// All store steps of a loader at once (when there is no value product to hide them in).
+template <int I = 0, class Loader>
+__device__ __forceinline__ void store_all(Loader& ld, char* buf) {
+  if constexpr (I < Loader::kStoreSteps) {
+    ld.template store_step<I>(buf);
+    store_all<I + 1>(ld, buf);
+  }
 }
 
-// The pages of an item are looked up from an LDS copy of its block-table slice,
-// refreshed every kSegPages pages while no direct load is in flight, so the only
-// vector-memory operations inside the pipeline are the tile loads themselves
-// (the vmcnt accounting above relies on that).
-constexpr int kSegPages = 2048;
+// One tile step: scores and softmax on `cur`, P exchange, then the value
+// product with the next tile staged into `nxt`.  `cur` and `nxt` are distinct
+// LDS arrays (the caller alternates them by unrolling), so the compiler can
+// prove the staging writes never alias the operand reads and is free to
+// interleave them.
+template <class Loader, int kMode, class PageAt>
+__device__ __forceinline__ void h128_step(const DecodeArgs& a, int s, int seg0, int seg1, const char* cur,
+                                          char* nxt, char* pbuf, const char* qtail,
+                                          const H128Lane& L, int wave,
+                                          const half8 (&q)[kQReg], floatx16 (&o)[16], float& m_ref,
+                                          float& l_sum, bool& overflow, Loader& ld, PageAt&& page_at) {
+  __syncthreads();                         // tile s complete; P buffer and `nxt` free
+  // Page ids of this tile and of the one staged after the next, read here, where no
+  // other LDS access is in flight, and kept in SGPRs (a table read between the
+  // value MFMAs would drain their operand reads).
+  int pg0 = __builtin_amdgcn_readfirstlane((int)page_at(s));
+  int pg2 = __builtin_amdgcn_readfirstlane((int)page_at(s + 2));
+  asm volatile("" : "+s"(pg0), "+s"(pg2));
+  const int t0 = seg0 + s * kTile128;
+  half8 p[2];
+  h128_scores<kMode, Loader::kScorePrefetch>(cur, qtail, L, q, ld, m_ref, l_sum, overflow, t0, seg1, pg0 >= 0,
+                                                  a.scale_log2, p);
+  auto begin = [&]() { ld.begin(a, pg2, seg0 + (s + 2) * kTile128, seg1); };
+  if (kMode != 1) {
+    char* pw = pbuf + wave * 32 * kPRow;
+    *reinterpret_cast<half8*>(pw + L.p_off(0)) = p[0];
+    *reinterpret_cast<half8*>(pw + L.p_off(1)) = p[1];
+    __syncthreads();                       // P of all heads visible
+    H128Values<Loader, decltype(begin)>{cur, pbuf, L, wave, o, ld, nxt, begin}.run();
+  } else {
+    store_all(ld, nxt);
+    ld.issue(a, pg2, seg0 + (s + 2) * kTile128, seg1);
+  }
+}
 
-template <int kMode>
-__device__ __forceinline__ void h128_pass_dma(const DecodeArgs& a, const ItemRange& it, char* lds, int32_t* ptab,
-                                              const H128Lane& L, const DmaBf16Tile& D, const half8 (&q)[kDk / 16],
-                                              floatx16 (&o)[16], float& m_ref, float& l_sum, bool& overflow) {
+template <class Loader, int kMode>
+__device__ __forceinline__ void h128_pass(const DecodeArgs& a, const ItemRange& it, char* lds0, char* lds1,
+                                          char* pbuf, const char* qtail, int32_t* ptab,
+                                          const H128Lane& L,
+                                          int wave, const half8 (&q)[kQReg], floatx16 (&o)[16], float& m_ref,
+                                          float& l_sum, bool& overflow) {
   for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
     const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
-    const int n_pages = (seg1 - seg0 + kBlock - 1) / kBlock;
-    __syncthreads();                       // earlier users of the ring and the table are done
-    for (int i = threadIdx.x; i < n_pages; i += 256) ptab[i] = (int32_t)page_of(a, it.b, seg0 + i * kBlock);
+    __syncthreads();                       // earlier users of the buffers and the table are done
+    fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile128 - 1) / kTile128;
-    auto page_at = [&](int t) -> int { return ptab[(t * kTile128) / kBlock]; };
-    auto tile_src = [&](int t) -> const uint8_t* {
-      const int page = page_at(t);
-      return a.pool + (int64_t)(page < 0 ? 0 : page) * (kBlock * kRowBytesBf16) +
-             (int64_t)(((seg0 + t * kTile128) % kBlock) * kRowBytesBf16);
+    auto page_at = [&](int t) -> int64_t {       // -1 past the segment; branch free (read clamped, then select)
+      const int pg = ptab[(min(t, n_tiles - 1) * kTile128) / kBlock];
+      return t < n_tiles ? pg : -1;
     };
-    auto valid_rows = [&](int t) -> int {
-      return page_at(t) >= 0 ? min(kTile128, seg1 - (seg0 + t * kTile128)) : 0;
-    };
-    const bool any_pages = a.num_pages > 0;
-    if (any_pages) {
-      for (int t = 0; t < min(3, n_tiles); ++t) D.issue(tile_src(t), lds + t * kBuf128);
+    Loader ld;
+    ld.issue(a, page_at(0), seg0, seg1);
+    ld.commit(lds0);
+    ld.issue(a, page_at(1), seg0 + kTile128, seg1);
+    for (int s = 0; s < n_tiles; s += 2) {
+      h128_step<Loader, kMode>(a, s, seg0, seg1, lds0, lds1, pbuf, qtail, L, wave, q, o, m_ref, l_sum,
+                               overflow, ld, page_at);
+      if (s + 1 < n_tiles)
+        h128_step<Loader, kMode>(a, s + 1, seg0, seg1, lds1, lds0, pbuf, qtail, L, wave, q, o, m_ref,
+                                 l_sum, overflow, ld, page_at);
     }
-    wait_vm_tiles(any_pages ? min(2, n_tiles - 1) : 0);
-    D.convert(lds, valid_rows(0));
-    for (int s = 0; s < n_tiles; ++s) {
-      __syncthreads();                     // tile s converted by all; tile s-1 no longer read
-      if (s + 3 < n_tiles && any_pages) D.issue(tile_src(s + 3), lds + ((s + 3) & 3) * kBuf128);
-      const int t0 = seg0 + s * kTile128;
-      h128_tile<kMode>(lds + (s & 3) * kBuf128, L, q, o, m_ref, l_sum, overflow, t0, seg1, page_at(s) >= 0,
-                       a.scale_log2);
-      // Widen this lane's share of the next tile while the value MFMAs drain.
-      if (s + 1 < n_tiles) {
-        wait_vm_tiles(any_pages ? min(2, n_tiles - 1 - (s + 1)) : 0);
-        D.convert(lds + ((s + 1) & 3) * kBuf128, valid_rows(s + 1));
-      }
-    }
-    wait_vm<0>();
   }
 }
 
 template <int kCache>
 __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
-  constexpr int kRing = (kCache == 0) ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) char lds[kRing * kBuf128];
-  __shared__ int32_t ptab[kCache == 0 ? kSegPages : 1];
-  const ItemRange it = item_range(a);
+  __shared__ __attribute__((aligned(16))) char lds0[kBuf128];
+  __shared__ __attribute__((aligned(16))) char lds1[kBuf128];
+  __shared__ __attribute__((aligned(16))) char pbuf[kPBuf];
+  __shared__ __attribute__((aligned(16))) char qtail[kQTailBytes];
+  __shared__ int32_t ptab[kSegPages];
+  ItemRange it = item_range(a);
   if (!it.ok) return;
+  if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane & 31;
   const int g = lane >> 5;
-  const int h = wave * 32 + hl;
+  const int h = wave * 32 + hl;                    // this lane's head in the score phase
   const H128Lane L = h128_lane();
 
-  // Q^T as the B operand: lane holds q_abs[b][h][16 ks + 8 g .. +7].
-  half8 q[kDk / 16];
+  // Q^T as the B operand: lane holds q_abs[b][h][16 ks + 8 g .. +7] for the
+  // first kQReg k-steps; the rest of every head's row goes to LDS.
+  half8 q[kQReg];
   {
     const uint16_t* qp = a.q_abs + ((int64_t)it.b * 128 + h) * kDk + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < kDk / 16; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 16 * ks));
+    for (int ks = 0; ks < kQReg; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 16 * ks));
+    const int hr = threadIdx.x >> 1, c0 = kQTail * (threadIdx.x & 1);
+    const uint16_t* qr = a.q_abs + ((int64_t)it.b * 128 + hr) * kDk + 16 * kQReg;
+#pragma unroll
+    for (int c = c0; c < c0 + kQTail; ++c) *reinterpret_cast<u32x4*>(qtail + qtail_off(hr, c)) = ld16(qr + 8 * c);
   }
+  // Retire the Q loads here: otherwise the compiler's wait for them sits inside
+  // the tile loop and also drains the tile loads issued after them.
+  wait_vm<0>();
   floatx16 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = floatx16{};
   float m_ref = -INFINITY, l_sum = 0.f;
   bool overflow = false;
 
-  if constexpr (kCache == 0) {
-    // Retire the Q loads before the first direct load: the compiler cannot see
-    // the direct loads, so its own vmcnt waits for Q inside the loop would
-    // otherwise also stall on tile loads.
-    wait_vm<0>();
-    DmaBf16Tile D;
-    D.init();
-    h128_pass_dma<0>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
-    if (__syncthreads_or(overflow)) {
-      // Rare: some head's scores grew by more than 2^15 after its first tile.
-      m_ref = -INFINITY;
-      h128_pass_dma<1>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
+  using Loader = typename std::conditional<
+      kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
+      typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128, kSwz128>,
+                                LoaderInt4Reg<kTile128, kSwz128>>::type>::type;
+  h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
+                         overflow);
+  if (__syncthreads_or(overflow)) {
+    // Rare: some head's scores grew by more than 2^15 after its first tile.
+    m_ref = -INFINITY;
+    h128_pass<Loader, 1>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
+                         overflow);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = floatx16{};
-      l_sum = 0.f;
-      h128_pass_dma<2>(a, it, lds, ptab, L, D, q, o, m_ref, l_sum, overflow);
-    }
-  } else {
-    using Loader = typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128, kSwz128>,
-                                              LoaderInt4Reg<kTile128, kSwz128>>::type;
-    h128_pass_reg<Loader, 0>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
-    if (__syncthreads_or(overflow)) {
-      m_ref = -INFINITY;
-      h128_pass_reg<Loader, 1>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = floatx16{};
-      l_sum = 0.f;
-      h128_pass_reg<Loader, 2>(a, it, lds, L, q, o, m_ref, l_sum, overflow);
-    }
+    for (int i = 0; i < 16; ++i) o[i] = floatx16{};
+    l_sum = 0.f;
+    h128_pass<Loader, 2>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
+                         overflow);
   }
 
-  // ---- normalise and write the partial ----
+  // ---- per-head sums from the owning waves, then normalise and write ----
   const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
-  float* op = a.o_part + ((int64_t)it.out_row * 128 + h) * kDc + 4 * g;
+  float* red = reinterpret_cast<float*>(pbuf);
+  __syncthreads();                                 // every wave is done with the P buffer
+  if (g == 0) red[h] = l_tot;
+  __syncthreads();
+  float inv[4];
 #pragma unroll
-  for (int tile = 0; tile < 16; ++tile) {
+  for (int hg = 0; hg < 4; ++hg) {
+    const float l = red[32 * hg + hl];
+    inv[hg] = l > 0.f ? 1.f / l : 0.f;
+  }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      floatx4 v = {o[tile][4 * rr], o[tile][4 * rr + 1], o[tile][4 * rr + 2], o[tile][4 * rr + 3]};
-      *reinterpret_cast<floatx4*>(op + 32 * tile + 8 * rr) = v * inv;
+  for (int f = 0; f < 4; ++f) {
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      float* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + 128 * wave + 32 * f + 4 * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const floatx16& v = o[4 * f + hg];
+        const floatx4 x = {v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]};
+        *reinterpret_cast<floatx4*>(op + 8 * rr) = x * inv[hg];
+      }
     }
   }
-  if (g == 0) a.lse_part[(int64_t)it.out_row * 128 + h] = lse;
+  if (g == 0) a.lse_part[(int64_t)it.out_row * 128 + h] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ===========================================================================
@@ -573,13 +788,14 @@ constexpr int kBuf16 = kTile16 * kRowLds;          // 73,728 B
 template <class Loader>
 __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kBuf16];
-  const ItemRange it = item_range(a);
+  __shared__ int32_t ptab[kSegPages];
+  ItemRange it = item_range(a);
   if (!it.ok) return;
+  if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int hl = lane & 15;          // head (MFMA column)
   const int grp = lane >> 4;         // 0..3
-  const int n_tiles = (it.t_end - it.t_begin + kTile16 - 1) / kTile16;
 
   // Q^T as the B operand of 16x16x32: lane holds q_abs[b][hl][32 ks + 8 grp .. +7].
   half8 q[kDk / 32];
@@ -588,18 +804,14 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kDk / 32; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 32 * ks));
   }
+  // Retire the Q loads here: otherwise the compiler's wait for them sits inside
+  // the tile loop and also drains the tile prefetch issued after them.
+  wait_vm<0>();
   floatx4 o[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) o[i] = floatx4{};
   float m_run = -INFINITY;
   float l_sum = 0.f;
-
-  Loader ld;
-  if (n_tiles > 0) {
-    ld.issue(a, it.b, it.t_begin, it.t_end);
-    ld.commit(lds);
-    if (n_tiles > 1) ld.issue(a, it.b, it.t_begin + kTile16, it.t_end);
-  }
 
   // Score operand: row tw + hl, chunk 4 ks + grp.  Transposed value read:
   // row tw + 4 grp + (hl >> 2), chunk 2 tile + ((hl & 3) >> 1), +8 B when hl odd.
@@ -612,56 +824,84 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) pv_off[t4] = swz<kSwz16>(pv_row, 2 * t4 + ((hl & 3) >> 1)) + 8 * (hl & 1);
 
-  for (int s = 0; s < n_tiles; ++s) {
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+    __syncthreads();                       // earlier users of the buffers and the table are done
+    fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
-    if (s + 1 < n_tiles) {
-      ld.commit(lds + ((s + 1) & 1) * kBuf16);
-      if (s + 2 < n_tiles) ld.issue(a, it.b, it.t_begin + (s + 2) * kTile16, it.t_end);
-    }
-    const char* buf = lds + (s & 1) * kBuf16;
-    const int t0 = it.t_begin + s * kTile16;
-    const bool page_ok = page_of(a, it.b, t0) >= 0;
+    const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
+    Loader ld;
+    ld.issue(a, ptab[0], seg0, seg1);
+    ld.commit(lds);
+    if (n_tiles > 1) ld.issue(a, ptab[1], seg0 + kTile16, seg1);
+    for (int s = 0; s < n_tiles; ++s) {
+      __syncthreads();
+      if (s + 1 < n_tiles) {
+        ld.commit(lds + ((s + 1) & 1) * kBuf16);
+        if (s + 2 < n_tiles) ld.issue(a, ptab[s + 2], seg0 + (s + 2) * kTile16, seg1);
+      }
+      const char* buf = lds + (s & 1) * kBuf16;
+      const int t0 = seg0 + s * kTile16;
+      const bool page_ok = ptab[s] >= 0;
 
-    floatx4 sacc = floatx4{};
+      // Scores: 18 k-steps as two interleaved chains, reads kPf steps ahead
+      // (pinned as in the 128-head kernel).
+      constexpr int kSteps = kDk / 32, kPf = 4;
+      __builtin_amdgcn_sched_barrier(0);
+      floatx4 sacc0 = floatx4{}, sacc1 = floatx4{};
+      half8 kb[kPf];
 #pragma unroll
-    for (int ks = 0; ks < kDk / 32; ++ks) {
-      const half8 kv = *reinterpret_cast<const half8*>(buf + qk_off[ks & 1] + 128 * (ks >> 1));
-      sacc = mfma16x16x32(kv, q[ks], sacc);
-    }
-    float mx = -INFINITY;
+      for (int d = 0; d < kPf; ++d) kb[d] = *reinterpret_cast<const half8*>(buf + qk_off[d & 1] + 128 * (d >> 1));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = t0 + tw + 4 * grp + r;
-      float v = sacc[r] * a.scale_log2;
-      if (!page_ok || tt >= it.t_end) v = -INFINITY;
-      sacc[r] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const bool need = mx > m_run + kTau;
-    if (__ballot(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      for (int ks = 0; ks < kSteps; ++ks) {
+        if (ks & 1) sacc1 = mfma16x16x32(kb[ks % kPf], q[ks], sacc1);
+        else sacc0 = mfma16x16x32(kb[ks % kPf], q[ks], sacc0);
+        const int kn = ks + kPf;
+        if (kn < kSteps) kb[ks % kPf] = *reinterpret_cast<const half8*>(buf + qk_off[kn & 1] + 128 * (kn >> 1));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-      l_sum *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    half4 p;
-    float psum = 0.f;
+      for (int ks = 0; ks < kSteps; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks + kPf < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      floatx4 sacc = sacc0 + sacc1;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
-      psum += e;
-      p[r] = (_Float16)e;
-    }
-    l_sum += psum;
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + tw + 4 * grp + r;
+        float v = sacc[r] * a.scale_log2;
+        if (!page_ok || tt >= seg1) v = -INFINITY;
+        sacc[r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const bool need = mx > m_run + kTau;
+      if (__ballot(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
 #pragma unroll
-    for (int tile = 0; tile < 32; ++tile) {
-      const half4 av = lds_read_tr(buf, pv_off[tile & 3] + 128 * (tile >> 2));
-      o[tile] = mfma16x16x16(av, p, o[tile]);
+        for (int i = 0; i < 32; ++i) o[i] *= alpha;
+        l_sum *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      half4 p;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
+        psum += e;
+        p[r] = (_Float16)e;
+      }
+      l_sum += psum;
+#pragma unroll
+      for (int tile = 0; tile < 32; ++tile) {
+        const half4 av = lds_read_tr(buf, pv_off[tile & 3] + 128 * (tile >> 2));
+        o[tile] = mfma16x16x16(av, p, o[tile]);
+      }
     }
   }
 
