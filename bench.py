@@ -173,7 +173,7 @@ def main():
     log("setup %.1f s: %s, %d tokens, %d work items" % (time.time() - t0, desc, case.total_tokens, n_items))
 
     def step():
-        run.step(q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c, new_r, new_s)
+        run.step(q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c, new_r, new_s, keep_latent=False)
 
     for _ in range(args.warmup):
         step()

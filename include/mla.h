@@ -101,7 +101,7 @@ typedef struct {
 mla_status mla_config_check(const mla_config* cfg);
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
 size_t mla_cache_page_bytes(const mla_config* cfg);
-/* o_part (n_items x H x 512 f32) plus lse_part (n_items x H f32), in bytes. */
+/* o_part (n_items x H x 512 fp16) plus lse_part (n_items x H f32), in bytes. */
 size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
 
 /* ------------------------------------------------------------------ a-1
@@ -172,27 +172,30 @@ mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, 
  *                ids outside [0, num_pages) make their tokens contribute nothing
  *   seq_lens     device [batch] int32
  *   items        device [n_items] (from mla_plan_splits, uploaded by the caller)
- *   o_part       device [n_items][H][512] f32, lse_part device [n_items][H] f32
+ *   o_part       device [n_items][H][512] fp16 (IEEE binary16 bits),
+ *                lse_part device [n_items][H] f32
  *                (mla_decode_workspace_bytes(n_items) bytes in all); an item whose
  *                seq or out_row is out of range is skipped
  * Numerics: scores and probabilities use fp16 operands on the matrix cores
  * with fp32 accumulation; the bf16 latent is widened to fp16 exactly (values
- * beyond +-65504 are not supported); softmax state is fp32.                */
+ * beyond +-65504 are not supported); softmax state is fp32; the normalised
+ * partial o_j is rounded to fp16 (round to nearest even), lse_j stays fp32.  */
 mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const void* pool,
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_seq, const int32_t* seq_lens,
                            const mla_work_item* items, int32_t n_items,
-                           float* o_part, float* lse_part, int32_t batch,
+                           uint16_t* o_part, float* lse_part, int32_t batch,
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------ a-4
  * mla_decode_combine: exact log-sum-exp merge of each sequence's partials:
  *   lse = ln sum_j exp(lse_j);  o_lat = sum_j exp(lse_j - lse) o_j.
  * A sequence whose partials are all empty gets o_lat = 0, lse = -inf.
+ *   o_part, lse_part  as written by mla_decode_attn (fp16, f32); sums are fp32
  *   split_offsets  device [batch + 1] int32 (from mla_plan_splits)
  *   o_lat          device [batch][H][512] f32, written
  *   lse            device [batch][H] f32, written (may be NULL)            */
-mla_status mla_decode_combine(const mla_config* cfg, const float* o_part, const float* lse_part,
+mla_status mla_decode_combine(const mla_config* cfg, const uint16_t* o_part, const float* lse_part,
                               const int32_t* split_offsets, float* o_lat, float* lse,
                               int32_t batch, hipStream_t stream);
 
@@ -213,6 +216,23 @@ mla_status mla_decode_combine(const mla_config* cfg, const float* o_part, const 
 mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const uint16_t* w_uv,
                         uint16_t* out, const uint16_t* w_o, int32_t hidden, uint16_t* y,
                         float* out_f32, int32_t batch, hipStream_t stream);
+
+/* ------------------------------------------------------------------ a-4 + a-5
+ * mla_decode_combine_out_proj: mla_decode_combine followed by mla_out_proj in
+ * one pass (same definitions and numerics: [Audit] §2.3; [Tutorial] §四):
+ * o_lat is formed on chip from the partials and, unless asked for, never
+ * written, which saves its round trip through HBM and a launch.
+ *   o_part, lse_part, split_offsets   as for mla_decode_combine
+ *   w_uv       device [H][128][512] bf16 ("hdc")
+ *   out        device [batch][H][128] bf16, written
+ *   o_lat      device [batch][H][512] f32, written when not NULL
+ *   lse        device [batch][H] f32, written when not NULL
+ *   w_o, hidden, y, out_f32   as for mla_out_proj (W_O product when w_o != NULL)
+ * The merged o_lat enters the expansion rounded to fp16, as in mla_out_proj. */
+mla_status mla_decode_combine_out_proj(const mla_config* cfg, const uint16_t* o_part, const float* lse_part,
+                                       const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out,
+                                       float* o_lat, float* lse, const uint16_t* w_o, int32_t hidden,
+                                       uint16_t* y, float* out_f32, int32_t batch, hipStream_t stream);
 
 /* ------------------------------------------------------------------ errors */
 const char* mla_status_string(mla_status s);

@@ -11,10 +11,11 @@ The five steps of one decode, in order:
     decode_attn    -> split-KV attention over the shared latent (partials)
     decode_combine -> log-sum-exp merge of the partials (o_lat, lse)
     out_proj       -> expand through W_UV (and optionally W_O)
-plus the host-side planner plan_splits.
+plus the host-side planner plan_splits, and decode_combine_out_proj, which
+runs the last two in one pass.
 """
 from .api import (  # noqa: F401
     MlaError, Config, config, cache_bytes_per_token, cache_page_bytes, decode_workspace_bytes,
-    plan_splits, cache_append, absorb_q, decode_attn, decode_combine, out_proj, status_string,
+    plan_splits, cache_append, absorb_q, decode_attn, decode_combine, out_proj, decode_combine_out_proj, status_string,
     CACHE_BF16, CACHE_INT8, CACHE_INT4,
 )

@@ -41,6 +41,8 @@ SIGNATURES = {
                                   C.c_int32, _P]),
     "mla_decode_combine": (C.c_int, [_CFG, _P, _P, _P, _P, _P, C.c_int32, _P]),
     "mla_out_proj": (C.c_int, [_CFG, _P, _P, _P, _P, C.c_int32, _P, _P, C.c_int32, _P]),
+    "mla_decode_combine_out_proj": (C.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, C.c_int32, _P, _P,
+                                              C.c_int32, _P]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
     "mla_last_hip_error": (C.c_int32, []),
 }

@@ -138,7 +138,7 @@ def decode_attn(cfg: Config, q_abs, pool, block_table, seq_lens, items, o_part, 
     n_items = int(items.shape[0])
     _need(items, "items", (n_items, 4), 4)
     rows = int(o_part.shape[0])
-    _need(o_part, "o_part", (rows, H, 512), 4)
+    _need(o_part, "o_part", (rows, H, 512), 2)
     _need(lse_part, "lse_part", (rows, H), 4)
     page = cache_page_bytes(cfg)
     nbytes = pool.numel() * pool.element_size()
@@ -158,6 +158,30 @@ def decode_combine(cfg: Config, o_part, lse_part, split_offsets, o_lat, lse=None
     _check(L.load().mla_decode_combine(C.byref(cfg), _dev(o_part, "o_part"), _dev(lse_part, "lse_part"),
                                        _dev(split_offsets, "split_offsets"), _dev(o_lat, "o_lat"),
                                        _dev(lse, "lse"), B, _stream()), "mla_decode_combine")
+
+
+def decode_combine_out_proj(cfg: Config, o_part, lse_part, split_offsets, w_uv, out, o_lat=None, lse=None,
+                            w_o=None, y=None, out_f32=None) -> None:
+    B, H = int(out.shape[0]), cfg.num_heads
+    _need(o_part, "o_part", (int(o_part.shape[0]), H, 512), 2)
+    _need(lse_part, "lse_part", (int(o_part.shape[0]), H), 4)
+    _need(split_offsets, "split_offsets", (B + 1,), 4)
+    _need(w_uv, "w_uv", (H, 128, 512), 2)
+    _need(out, "out", (B, H, 128), 2)
+    if o_lat is not None:
+        _need(o_lat, "o_lat", (B, H, 512), 4)
+    if lse is not None:
+        _need(lse, "lse", (B, H), 4)
+    hidden = 0
+    if w_o is not None:
+        hidden = int(w_o.shape[0])
+        _need(w_o, "w_o", (hidden, H * 128), 2)
+        _need(y, "y", (B, hidden), 2)
+        _need(out_f32, "out_f32", (B, H, 128), 4)
+    _check(L.load().mla_decode_combine_out_proj(
+        C.byref(cfg), _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(split_offsets, "split_offsets"),
+        _dev(w_uv, "w_uv"), _dev(out, "out"), _dev(o_lat, "o_lat"), _dev(lse, "lse"), _dev(w_o, "w_o"), hidden,
+        _dev(y, "y"), _dev(out_f32, "out_f32"), B, _stream()), "mla_decode_combine_out_proj")
 
 
 def out_proj(cfg: Config, o_lat, w_uv, out, w_o=None, y=None, out_f32=None) -> None:

@@ -73,7 +73,7 @@ size_t mla_cache_page_bytes(const mla_config* cfg) { return 64 * mla_cache_bytes
 
 size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items) {
   if (mla_config_check(cfg) != MLA_OK || n_items < 0) return 0;
-  return (size_t)n_items * cfg->num_heads * (512 + 1) * sizeof(float);
+  return (size_t)n_items * cfg->num_heads * (512 * sizeof(uint16_t) + sizeof(float));
 }
 
 mla_status mla_cache_append(const mla_config* cfg, void* pool, int64_t num_pages, const uint16_t* c_kv,
@@ -103,7 +103,7 @@ mla_status mla_absorb_q(const mla_config* cfg, const uint16_t* q_nope, const uin
 
 mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const void* pool, int64_t num_pages,
                            const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
-                           const mla_work_item* items, int32_t n_items, float* o_part, float* lse_part,
+                           const mla_work_item* items, int32_t n_items, uint16_t* o_part, float* lse_part,
                            int32_t batch, hipStream_t stream) {
   mla_status s = mla_config_check(cfg);
   if (s != MLA_OK) return s;
@@ -130,7 +130,7 @@ mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const v
   return launched(mla::launch_decode_attn(a, cfg->num_heads, cfg->cache_dtype, stream));
 }
 
-mla_status mla_decode_combine(const mla_config* cfg, const float* o_part, const float* lse_part,
+mla_status mla_decode_combine(const mla_config* cfg, const uint16_t* o_part, const float* lse_part,
                               const int32_t* split_offsets, float* o_lat, float* lse, int32_t batch,
                               hipStream_t stream) {
   mla_status s = mla_config_check(cfg);
@@ -159,6 +159,30 @@ mla_status mla_out_proj(const mla_config* cfg, const float* o_lat, const uint16_
   if (w_o != nullptr && (!aligned16(w_o) || !aligned16(y) || !aligned16(out_f32))) return MLA_ERR_ALIGN;
   if ((s = check_device()) != MLA_OK) return s;
   hipError_t e = mla::launch_out_proj(cfg->num_heads, o_lat, w_uv, out, w_o ? out_f32 : nullptr, batch, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (w_o != nullptr)
+    return launched(mla::launch_wo_proj(cfg->num_heads * 128, out_f32, w_o, hidden, y, batch, stream));
+  return MLA_OK;
+}
+
+mla_status mla_decode_combine_out_proj(const mla_config* cfg, const uint16_t* o_part, const float* lse_part,
+                                       const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out,
+                                       float* o_lat, float* lse, const uint16_t* w_o, int32_t hidden, uint16_t* y,
+                                       float* out_f32, int32_t batch, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (batch < 0) return MLA_ERR_VALUE;
+  if (w_o != nullptr && hidden <= 0) return MLA_ERR_VALUE;
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !split_offsets || !w_uv || !out) return MLA_ERR_NULL;
+  if (w_o != nullptr && (!y || !out_f32)) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(split_offsets) || !aligned16(w_uv) ||
+      !aligned16(out) || (o_lat && !aligned16(o_lat)) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGN;
+  if (w_o != nullptr && (!aligned16(w_o) || !aligned16(y) || !aligned16(out_f32))) return MLA_ERR_ALIGN;
+  if ((s = check_device()) != MLA_OK) return s;
+  hipError_t e = mla::launch_combine_out_proj(cfg->num_heads, o_part, lse_part, split_offsets, w_uv, out,
+                                              w_o ? out_f32 : nullptr, o_lat, lse, batch, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (w_o != nullptr)
     return launched(mla::launch_wo_proj(cfg->num_heads * 128, out_f32, w_o, hidden, y, batch, stream));

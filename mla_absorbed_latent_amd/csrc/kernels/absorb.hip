@@ -30,11 +30,19 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   const int c0 = (blockIdx.x % (kDc / kSlab)) * kSlab;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // Stage W_UK[h][0:128][c0:c0+128]: 128 rows x 16 chunks of 16 B.
+  // Stage W_UK[h][0:128][c0:c0+128] (128 rows x 16 chunks of 16 B): all eight
+  // loads of a thread are issued before any LDS write, so they overlap.
   const uint16_t* wsrc = w_uk + (int64_t)h * kDn * kDc + c0;
-  for (int i = threadIdx.x; i < kDn * 16; i += 256) {
-    const int d = i >> 4, ch = i & 15;
-    *reinterpret_cast<u32x4*>(lds + d * kWRow + 16 * (ch ^ (d & 7))) = ld16(wsrc + (int64_t)d * kDc + 8 * ch);
+  u32x4 wv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = threadIdx.x + 256 * i, d = idx >> 4, ch = idx & 15;
+    wv[i] = ld16(wsrc + (int64_t)d * kDc + 8 * ch);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = threadIdx.x + 256 * i, d = idx >> 4, ch = idx & 15;
+    *reinterpret_cast<u32x4*>(lds + d * kWRow + 16 * (ch ^ (d & 7))) = wv[i];
   }
   // q_pe passthrough (bf16 -> fp16 is exact in range), done by the first slab.
   if (c0 == 0) {
@@ -56,9 +64,13 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     const bool bok = b < B;
     floatx16 acc = floatx16{};
     const uint16_t* qrow = q_nope + ((int64_t)(bok ? b : 0) * H + h) * kDn + 8 * g;
+    u32x4 qa[kDn / 16];                                // all q fragments in flight at once
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) qa[ks] = ld16(qrow + 16 * ks);
+    // A sequence past B reads row 0 instead; its column is never stored.
 #pragma unroll
     for (int ks = 0; ks < kDn / 16; ++ks) {
-      u32x4 qv = bok ? ld16(qrow + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 qv = qa[ks];
       const int d = 16 * ks + 8 * g + (gi >> 2);
       const int ch = colh >> 3;
       const uint32_t off_lo = d * kWRow + 16 * (ch ^ (d & 7)) + 2 * (colh & 7);

@@ -3,6 +3,7 @@
 //
 // Merge (one work-group per (sequence, head); exact for any split of the tokens):
 //     lse = ln sum_j e^{lse_j},  o_lat = sum_j e^{lse_j - lse} o_j
+// with the fp16 partials o_j widened and summed in fp32.
 // An all-empty sequence gives o_lat = 0, lse = -inf; one split is a copy.
 //
 // Output projection ("DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界" §2.3:
@@ -13,8 +14,8 @@
 // (mfma 32x32x16): both operands come straight from HBM with 16-byte loads,
 // since each lane needs 8 consecutive c -- the contiguous axis of both W_UV and
 // o_lat.  W_UV is widened bf16 -> fp16 exactly; o_lat is rounded fp32 -> fp16.
-// One wave per (head, 32 rows of d); the fp32 sums go to `out` as bf16 and,
-// when a layer output is wanted, to an fp32 workspace for the W_O product.
+// The fp32 sums go to `out` as bf16 and, when a layer output is wanted, to an
+// fp32 workspace for the W_O product.
 //
 // W_O product (optional): y[b,n] = sum_k W_O[n,k] x[b,k], x = concat_h out[b,h,:]
 // in fp32; one wave per output feature, fp32 FMAs, a wave reduction.
@@ -24,7 +25,7 @@
 namespace mla {
 namespace {
 
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const int32_t* __restrict__ offsets, float* __restrict__ o_lat,
                                                       float* __restrict__ lse_out, int H) {
@@ -35,12 +36,25 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   floatx4 acc = floatx4{};
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int j = r0; j < r1; ++j) {
-      const float l = lse_part[(int64_t)j * H + h];
-      if (l == -INFINITY) continue;
-      const float w = expf(l - m);
-      wsum += w;
-      acc += w * *reinterpret_cast<const floatx4*>(o_part + ((int64_t)j * H + h) * kDc + 4 * threadIdx.x);
+    // Four splits per round: their rows are loaded together, then weighted; an
+    // empty split (lse = -inf) contributes nothing, whatever its row holds.
+    for (int j0 = r0; j0 < r1; j0 += 4) {
+      floatx4 x[4];
+      float l[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = min(j0 + k, r1 - 1);
+        l[k] = j0 + k < r1 ? lse_part[(int64_t)j * H + h] : -INFINITY;
+        x[k] = __builtin_convertvector(*reinterpret_cast<const half4*>(o_part + ((int64_t)j * H + h) * kDc + 4 * threadIdx.x),
+                                      floatx4);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool empty = l[k] == -INFINITY;      // skipped outright, as if not loaded
+        const float w = empty ? 0.f : expf(l[k] - m);
+        wsum += w;
+        acc += w * (empty ? floatx4{} : x[k]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -48,50 +62,182 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   if (lse_out != nullptr && threadIdx.x == 0) lse_out[(int64_t)b * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-__global__ __launch_bounds__(64) void out_proj_kernel(const float* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
-                                                      uint16_t* __restrict__ out, float* __restrict__ out_f32, int H,
-                                                      int B) {
+// One work-group per (head, 32 rows of d).  Its four waves split c into
+// quarters: each loads its W_UV slice and o_lat fragments up front (all
+// independent 16-byte loads, so the memory system sees them at once), runs 16
+// MFMAs per 64 sequences, and the four partial sums meet in LDS.
+__global__ __launch_bounds__(256, 2) void out_proj_kernel(const float* __restrict__ o_lat,
+                                                          const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out,
+                                                          float* __restrict__ out_f32, int H, int B) {
+  __shared__ float red[4][2][16][64];              // [wave][b block][acc register][lane], 32 KB
   const int h = blockIdx.x >> 2;
   const int d0 = (blockIdx.x & 3) * 32;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5;
-  const uint16_t* wrow = w_uv + ((int64_t)h * kDn + d0 + (lane & 31)) * kDc + 8 * g;
-  for (int b0 = 0; b0 < B; b0 += 32) {
-    const int b = b0 + (lane & 31);
-    const bool bok = b < B;
-    const float* orow = o_lat + ((int64_t)(bok ? b : 0) * H + h) * kDc + 8 * g;
-    floatx16 acc = floatx16{};
-#pragma unroll 4
-    for (int ks = 0; ks < kDc / 16; ++ks) {
-      const half8 a = __builtin_bit_cast(half8, bf16x8_to_f16x8(ld16(wrow + 16 * ks)));
-      half8 bv;
-      if (bok) {
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(orow + 16 * ks);
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(orow + 16 * ks + 4);
+  const int cq = 128 * wave;                        // this wave's quarter of c
+
+  // A operand: W_UV[h][d0 + lane % 32][cq + 16 ks + 8 g .. +7], widened exactly.
+  u32x4 wr[8];
+  const uint16_t* wrow = w_uv + ((int64_t)h * kDn + d0 + (lane & 31)) * kDc + cq + 8 * g;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bv[e] = (_Float16)x0[e];
-          bv[4 + e] = (_Float16)x1[e];
-        }
-      } else {
-        bv = half8{};
+  for (int ks = 0; ks < 8; ++ks) wr[ks] = ld16(wrow + 16 * ks);
+
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    // B operand: o_lat[b][h][cq + 16 ks + 8 g .. +7], b = b0 + 32 bb + lane % 32.  All
+    // loads of the chunk are issued before any is used.  A sequence past B reads
+    // row 0 instead; its column of the product is never stored.
+    floatx4 x[2][16];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = b0 + 32 * bb + (lane & 31);
+      const float* orow = o_lat + ((int64_t)(b < B ? b : 0) * H + h) * kDc + cq + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        x[bb][2 * ks] = *reinterpret_cast<const floatx4*>(orow + 16 * ks);
+        x[bb][2 * ks + 1] = *reinterpret_cast<const floatx4*>(orow + 16 * ks + 4);
       }
-      acc = mfma32x32x16(a, bv, acc);
     }
-    if (bok) {
-      // lane holds out^T[d0 + 8 (r/4) + 4 g + r%4][b]
-      uint16_t* dst = out + ((int64_t)b * H + h) * kDn + d0 + 4 * g;
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 acc[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 v;
-        v[0] = (uint32_t)f32_to_bf16_rne(acc[4 * rr]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 1]) << 16);
-        v[1] = (uint32_t)f32_to_bf16_rne(acc[4 * rr + 2]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 3]) << 16);
-        *reinterpret_cast<u32x2*>(dst + 8 * rr) = v;
-        if (out_f32 != nullptr) {
-          float* fd = out_f32 + ((int64_t)b * H + h) * kDn + d0 + 4 * g + 8 * rr;
-          *reinterpret_cast<floatx4*>(fd) = floatx4{acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+    for (int ks = 0; ks < 8; ++ks) {
+      const half8 a = __builtin_bit_cast(half8, bf16x8_to_f16x8(wr[ks]));
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const half4 lo = __builtin_convertvector(x[bb][2 * ks], half4);      // round to nearest even
+        const half4 hi = __builtin_convertvector(x[bb][2 * ks + 1], half4);
+        acc[bb] = mfma32x32x16(a, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), acc[bb]);
+      }
+    }
+    __syncthreads();                               // the previous chunk's sums have been read
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave][bb][r][lane] = acc[bb][r];
+    __syncthreads();
+    // Thread t sums registers 8 rh .. 8 rh + 7 of lane l2 in b block bb over the four waves:
+    // out^T[d0 + 8 (r / 4) + 4 (l2 / 32) + r % 4][b0 + 32 bb + l2 % 32].
+    const int bb = threadIdx.x >> 7, rh = (threadIdx.x >> 6) & 1, l2 = threadIdx.x & 63;   // bank = l2: conflict free
+    const int b = b0 + 32 * bb + (l2 & 31);
+    if (b < B) {
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        floatx4 v = floatx4{};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += red[w][bb][8 * rh + 4 * q4 + e][l2];
+        const int d = d0 + 8 * (2 * rh + q4) + 4 * (l2 >> 5);
+        u32x2 o2;
+        o2[0] = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        o2[1] = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(out + ((int64_t)b * H + h) * kDn + d) = o2;
+        if (out_f32 != nullptr) *reinterpret_cast<floatx4*>(out_f32 + ((int64_t)b * H + h) * kDn + d) = v;
+      }
+    }
+  }
+}
+
+// Merge and expansion in one pass, one work-group per (head, 32 sequences):
+//  1. merge: the work-group combines, for each of its sequences, the fp16
+//     partials of head h (fp32 sums, as combine_kernel), keeps o_lat[b][h][:]
+//     as fp16 in LDS, and writes o_lat / lse as well when asked;
+//  2. expand: wave w computes out^T[32 w .. 32 w + 31][b] = W_UV[h][d][:] . o_lat^T
+//     for the 32 sequences (32 x mfma 32x32x16), W_UV rows straight from HBM and
+//     o_lat^T fragments from LDS.
+// o_lat never leaves the chip, and one launch replaces two.
+constexpr int kCoB = 32;                            // sequences per work-group
+
+__global__ __launch_bounds__(256) void combine_out_proj_kernel(
+    const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ out_f32,
+    float* __restrict__ o_lat, float* __restrict__ lse_out, int H, int B) {
+  // o_lat tile, fp16: row bi (1 KB) holds sequence b0 + bi, 16-byte chunk c at
+  // c ^ (bi & 15), so that the 16 rows a lane group reads land in distinct banks.
+  __shared__ __attribute__((aligned(16))) char olds[kCoB * kDc * 2];   // 32 KB
+  const int h = blockIdx.x % H;
+  const int b0 = (blockIdx.x / H) * kCoB;
+  const int t = threadIdx.x;
+
+  // ---- 1. merge: thread t owns 16-byte chunk c8 = t % 64 of sequences b0 + t / 64 + 4 i
+  const int c8 = t & 63;
+#pragma unroll 2
+  for (int i = 0; i < kCoB / 4; ++i) {
+    const int bi = (t >> 6) + 4 * i, b = b0 + bi;
+    floatx4 acc0 = floatx4{}, acc1 = floatx4{};
+    float wsum = 0.f, m = -INFINITY;
+    if (b < B) {
+      const int r0 = offsets[b], r1 = offsets[b + 1];
+      for (int j = r0; j < r1; ++j) m = fmaxf(m, lse_part[(int64_t)j * H + h]);
+      if (m != -INFINITY) {
+        for (int j0 = r0; j0 < r1; j0 += 4) {
+          half8 x[4];
+          float l[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int j = min(j0 + k, r1 - 1);
+            l[k] = j0 + k < r1 ? lse_part[(int64_t)j * H + h] : -INFINITY;
+            x[k] = *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bool empty = l[k] == -INFINITY;    // skipped outright, as if not loaded
+            const float w = empty ? 0.f : expf(l[k] - m);
+            wsum += w;
+            const floatx4 lo = __builtin_convertvector(__builtin_shufflevector(x[k], x[k], 0, 1, 2, 3), floatx4);
+            const floatx4 hi = __builtin_convertvector(__builtin_shufflevector(x[k], x[k], 4, 5, 6, 7), floatx4);
+            acc0 += w * (empty ? floatx4{} : lo);
+            acc1 += w * (empty ? floatx4{} : hi);
+          }
         }
       }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    acc0 *= inv;
+    acc1 *= inv;
+    const half4 lo = __builtin_convertvector(acc0, half4), hi = __builtin_convertvector(acc1, half4);   // nearest even
+    *reinterpret_cast<half8*>(olds + bi * (kDc * 2) + 16 * (c8 ^ (bi & 15))) =
+        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if (b < B) {
+      if (o_lat != nullptr) {
+        float* dst = o_lat + ((int64_t)b * H + h) * kDc + 8 * c8;
+        *reinterpret_cast<floatx4*>(dst) = acc0;
+        *reinterpret_cast<floatx4*>(dst + 4) = acc1;
+      }
+      if (lse_out != nullptr && c8 == 0) lse_out[(int64_t)b * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. expand: out^T[d][b] for d = 32 wave + lane % 32 (A operand), b = b0 + lane % 32 (B operand)
+  const int lane = t & 63, wave = t >> 6, g = lane >> 5, r = lane & 31;
+  const uint16_t* wrow = w_uv + ((int64_t)h * kDn + 32 * wave + r) * kDc + 8 * g;
+  floatx16 acc = floatx16{};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    u32x4 wr[8];                                    // eight k-steps of W_UV in flight
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) wr[ks] = ld16(wrow + 16 * (8 * kb + ks));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kk = 8 * kb + ks;
+      const half8 bv = *reinterpret_cast<const half8*>(olds + r * (kDc * 2) + 16 * ((2 * kk + g) ^ (r & 15)));
+      acc = mfma32x32x16(__builtin_bit_cast(half8, bf16x8_to_f16x8(wr[ks])), bv, acc);
+    }
+  }
+  // lane holds out^T[32 wave + 8 (q / 4) + 4 g + q % 4][b0 + lane % 32], q = 0..15
+  const int b = b0 + r;
+  if (b < B) {
+    const int d = 32 * wave + 4 * g;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      u32x2 v;
+      v[0] = (uint32_t)f32_to_bf16_rne(acc[4 * rr]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 1]) << 16);
+      v[1] = (uint32_t)f32_to_bf16_rne(acc[4 * rr + 2]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 3]) << 16);
+      *reinterpret_cast<u32x2*>(out + ((int64_t)b * H + h) * kDn + d + 8 * rr) = v;
+      if (out_f32 != nullptr)
+        *reinterpret_cast<floatx4*>(out_f32 + ((int64_t)b * H + h) * kDn + d + 8 * rr) =
+            floatx4{acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
     }
   }
 }
@@ -124,7 +270,7 @@ __global__ __launch_bounds__(256) void wo_kernel(const float* __restrict__ x, co
 
 }  // namespace
 
-hipError_t launch_combine(int num_heads, const float* o_part, const float* lse_part, const int32_t* split_offsets,
+hipError_t launch_combine(int num_heads, const uint16_t* o_part, const float* lse_part, const int32_t* split_offsets,
                           float* o_lat, float* lse, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3(batch * num_heads), dim3(128), 0, stream, o_part, lse_part, split_offsets,
@@ -135,8 +281,17 @@ hipError_t launch_combine(int num_heads, const float* o_part, const float* lse_p
 hipError_t launch_out_proj(int num_heads, const float* o_lat, const uint16_t* w_uv, uint16_t* out, float* out_f32,
                            int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(out_proj_kernel, dim3(num_heads * 4), dim3(64), 0, stream, o_lat, w_uv, out, out_f32, num_heads,
+  hipLaunchKernelGGL(out_proj_kernel, dim3(num_heads * 4), dim3(256), 0, stream, o_lat, w_uv, out, out_f32, num_heads,
                      batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_out_proj(int num_heads, const uint16_t* o_part, const float* lse_part,
+                                  const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out, float* out_f32,
+                                  float* o_lat, float* lse, int batch, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(num_heads * ((batch + kCoB - 1) / kCoB)), dim3(256), 0, stream,
+                     o_part, lse_part, split_offsets, w_uv, out, out_f32, o_lat, lse, num_heads, batch);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;      // [batch]
   const mla_work_item* items;   // [n_items]
   int32_t n_items;
-  float* o_part;                // [rows][H][512]
+  uint16_t* o_part;             // [rows][H][512] fp16
   float* lse_part;              // [rows][H]
   int32_t batch;
   float scale_log2;             // softmax_scale * log2(e)

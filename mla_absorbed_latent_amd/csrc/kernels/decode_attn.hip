@@ -767,12 +767,12 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   for (int f = 0; f < 4; ++f) {
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
-      float* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + 128 * wave + 32 * f + 4 * g;
+      uint16_t* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + 128 * wave + 32 * f + 4 * g;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const floatx16& v = o[4 * f + hg];
-        const floatx4 x = {v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]};
-        *reinterpret_cast<floatx4*>(op + 8 * rr) = x * inv[hg];
+        const floatx4 x = floatx4{v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]} * inv[hg];
+        *reinterpret_cast<half4*>(op + 8 * rr) = __builtin_convertvector(x, half4);   // round to nearest even
       }
     }
   }
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
       l += ew[w] * red_l[w * 16 + head];
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* op = a.o_part + ((int64_t)it.out_row * 16 + head) * kDc + f0;
+    uint16_t* op = a.o_part + ((int64_t)it.out_row * 16 + head) * kDc + f0;
 #pragma unroll
     for (int f = 0; f < 32; f += 4) {
       floatx4 v = floatx4{};
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
         const floatx4 x = *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f0 + f);
         v += ew[w] * x;
       }
-      *reinterpret_cast<floatx4*>(op + f) = v * inv;
+      *reinterpret_cast<half4*>(op + f) = __builtin_convertvector(v * inv, half4);   // round to nearest even
     }
     if ((threadIdx.x & 15) == 0)
       a.lse_part[(int64_t)it.out_row * 16 + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;

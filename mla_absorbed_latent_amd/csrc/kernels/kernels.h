@@ -13,12 +13,15 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
 hipError_t launch_absorb_q(int num_heads, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk,
                            uint16_t* q_abs, int batch, hipStream_t stream);
 
-hipError_t launch_combine(int num_heads, const float* o_part, const float* lse_part, const int32_t* split_offsets,
+hipError_t launch_combine(int num_heads, const uint16_t* o_part, const float* lse_part, const int32_t* split_offsets,
                           float* o_lat, float* lse, int batch, hipStream_t stream);
 
 hipError_t launch_out_proj(int num_heads, const float* o_lat, const uint16_t* w_uv, uint16_t* out,
                            float* out_f32, int batch, hipStream_t stream);
 
+hipError_t launch_combine_out_proj(int num_heads, const uint16_t* o_part, const float* lse_part,
+                                  const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out, float* out_f32,
+                                  float* o_lat, float* lse, int batch, hipStream_t stream);
 hipError_t launch_wo_proj(int in_features, const float* x, const uint16_t* w_o, int hidden, uint16_t* y,
                           int batch, hipStream_t stream);
 

@@ -48,7 +48,7 @@ class DecodeRunner:
         self.items = torch.from_numpy(np.ascontiguousarray(arr)).to(self.device)
         self.offsets = torch.from_numpy(offs).to(self.device)
         if self.o_part is None or self.o_part.shape[0] < rows:
-            self.o_part = torch.empty(rows, self.H, 512, dtype=torch.float32, device=self.device)
+            self.o_part = torch.empty(rows, self.H, 512, dtype=torch.float16, device=self.device)
             self.lse_part = torch.empty(rows, self.H, dtype=torch.float32, device=self.device)
         return self.n_items
 
@@ -71,13 +71,23 @@ class DecodeRunner:
     def project(self, w_uv, w_o=None, y=None, out_f32=None) -> None:
         api.out_proj(self.cfg, self.o_lat, w_uv, self.out, w_o, y, out_f32)
 
+    def combine_project(self, w_uv, w_o=None, y=None, out_f32=None, keep_latent=True) -> None:
+        """Merge and expand in one pass; o_lat / lse are written only with keep_latent."""
+        api.decode_combine_out_proj(self.cfg, self.o_part, self.lse_part, self.offsets, w_uv, self.out,
+                                    self.o_lat if keep_latent else None, self.lse if keep_latent else None,
+                                    w_o, y, out_f32)
+
     def step(self, q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c_kv=None, new_k_pe=None,
-             new_slots=None, w_o=None, y=None, out_f32=None):
-        """One decode step: append the new tokens, absorb, attend, merge, expand."""
+             new_slots=None, w_o=None, y=None, out_f32=None, fused=True, keep_latent=True):
+        """One decode step: append the new tokens, absorb, attend, merge, expand
+        (merge and expansion fused unless fused=False)."""
         if new_c_kv is not None:
             self.append(new_c_kv, new_k_pe, new_slots)
         self.absorb(q_nope, q_pe, w_uk)
         self.attend(block_table, seq_lens)
-        self.combine()
-        self.project(w_uv, w_o, y, out_f32)
+        if fused:
+            self.combine_project(w_uv, w_o, y, out_f32, keep_latent)
+        else:
+            self.combine()
+            self.project(w_uv, w_o, y, out_f32)
         return self.out

@@ -43,7 +43,7 @@ def test_sizes(lib):
         assert api.cache_bytes_per_token(cfg) == tok
         assert api.cache_page_bytes(cfg) == page
     cfg = api.config(128)
-    assert api.decode_workspace_bytes(cfg, 10) == 10 * 128 * 513 * 4
+    assert api.decode_workspace_bytes(cfg, 10) == 10 * 128 * (512 * 2 + 4)
     assert api.cache_bytes_per_token(api.config(8)) == 0       # invalid config -> 0
 
 

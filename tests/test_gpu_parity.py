@@ -169,7 +169,42 @@ def test_empty_sequence_and_invalid_pages(H):
     assert mx <= MAX_REL and mean <= MEAN_REL
 
 
-def test_output_projection_with_wo():
+@pytest.mark.parametrize("H", [16, 128])
+def test_fused_merge_expand_matches_separate(H):
+    """mla_decode_combine_out_proj against mla_decode_combine + mla_out_proj on the
+    same partials: o_lat and lse bitwise (same sums in the same order), out within
+    the output tolerance (the expansion sums its 512 terms in another order)."""
+    lens = [1, 700, 64, 2500, 0, 33] + [130] * 30      # more than one 32-sequence block
+    case = mla_synth.small_decode(case_id=20, H=H, seq_lens=[max(1, L) for L in lens])
+    case.seq_lens[4] = 0
+    run, dev = upload(case)
+    dev["seq_lens"] = torch.from_numpy(case.seq_lens.astype(np.int32)).to(DEV)
+    run.plan(case.seq_lens, chunk_pages=2)
+    run.step(dev["q_nope"], dev["q_pe"], dev["w_uk"], dev["w_uv"], dev["block_table"], dev["seq_lens"], fused=False)
+    torch.cuda.synchronize()
+    out_sep, olat_sep, lse_sep = run.out.clone(), run.o_lat.clone(), run.lse.clone()
+    run.combine_project(dev["w_uv"])
+    torch.cuda.synchronize()
+    assert torch.equal(run.o_lat, olat_sep) and torch.equal(run.lse, lse_sep)
+    mx, mean = errors(run.out.float().cpu().numpy(), out_sep.float().cpu().numpy().astype(np.float64))
+    assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
+    # without the latent outputs the expansion is unchanged, bit for bit
+    out_keep = run.out.clone()
+    run.out.zero_()
+    run.combine_project(dev["w_uv"], keep_latent=False)
+    torch.cuda.synchronize()
+    assert torch.equal(run.out, out_keep)
+    for b in (0, 1, 3, 4, 35):
+        ref_out, _, _ = oracle_seq(case, b)
+        if case.seq_lens[b] == 0:
+            assert np.all(run.out[b].float().cpu().numpy() == 0)
+            continue
+        mx, mean = errors(run.out[b].float().cpu().numpy(), ref_out)
+        assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_output_projection_with_wo(fused):
     """V2-Lite layer shapes: one sequence of 26 tokens, H=16, W_O to hidden 2048."""
     layer = mla_synth.v2lite_layer()
     case = mla_synth.small_decode(case_id=19, H=16, seq_lens=[26])
@@ -178,7 +213,7 @@ def test_output_projection_with_wo():
     y = torch.empty(1, 2048, dtype=torch.bfloat16, device=DEV)
     of = torch.empty(1, 16, 128, dtype=torch.float32, device=DEV)
     run.step(dev["q_nope"], dev["q_pe"], dev["w_uk"], dev["w_uv"], dev["block_table"], dev["seq_lens"],
-             w_o=to_dev_bits(layer.w_o), y=y, out_f32=of)
+             w_o=to_dev_bits(layer.w_o), y=y, out_f32=of, fused=fused)
     torch.cuda.synchronize()
     ref_out, _, _ = oracle_seq(case, 0)
     ref_y = mla_ref.wo_proj(ref_out[None], mla_ref.bf16_to_f64(layer.w_o))[0]
