@@ -154,8 +154,9 @@ struct LoaderBf16Reg {
     return page >= 0;
   }
   // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's row
-  // source; load_step<I>, called right after store_step<I>, reloads the
-  // registers that store freed, so the loads trickle out one per MFMA.
+  // source; load_step<I> (after store_step<I>) reloads chunk I / 2 once its
+  // store is done (odd I), so the loads trickle out one per two MFMAs and have a
+  // whole tile step to arrive before they are widened.
   const uint8_t* src;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = threadIdx.x >> 3;
@@ -164,20 +165,22 @@ struct LoaderBf16Reg {
   }
   template <int I>
   __device__ __forceinline__ void load_step() {
-    r[I] = ld16_stream(src + 128 * I);
+    if constexpr (I % 2 == 1) r[I / 2] = ld16_stream(src + 128 * (I / 2));
   }
-  // Staging in two stages (one pass): widen_step<I> converts dword I % 4 of chunk
-  // I / 4 in place (36 steps, one per score MFMA); store_step<I> writes chunk I.
-  static constexpr int kWidenSteps = 36, kStoreSteps = 9;
-  template <int I>
-  __device__ __forceinline__ void widen_step() {
-    uint32_t v = bf16x2_to_f16x2(r[I / 4][I % 4]);
-    asm volatile("" : "+v"(v));   // keep the conversion here, not sunk to the store
-    r[I / 4][I % 4] = v;
-  }
+  // Stepwise commit: step 2c widens the first half of chunk c in place, step
+  // 2c+1 the second half, and stores the chunk.
+  static constexpr int kStoreSteps = 18;
   template <int I>
   __device__ __forceinline__ void store_step(char* lds_buf) {
-    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * I) = r[I];
+    constexpr int kc = I / 2, d0 = 2 * (I % 2);
+#pragma unroll
+    for (int d = d0; d < d0 + 2; ++d) {
+      uint32_t v = bf16x2_to_f16x2(r[kc][d]);
+      asm volatile("" : "+v"(v));   // keep the conversion in this step, not sunk to the store
+      r[kc][d] = v;
+    }
+    if constexpr (I % 2 == 1)
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * kc) = r[kc];
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
     const int tok = threadIdx.x >> 3;
@@ -253,9 +256,7 @@ struct LoaderInt8Reg {
   }
   // Stepwise commit: step 2c dequantises the first four codes of chunk c, step
   // 2c+1 the other four and stores the chunk.
-  static constexpr int kWidenSteps = 0, kStoreSteps = 18 * kPass;
-  template <int I>
-  __device__ __forceinline__ void widen_step() {}
+  static constexpr int kStoreSteps = 18 * kPass;
   u32x2 part;
   template <int I>
   __device__ __forceinline__ void store_step(char* lds_buf) {
@@ -357,9 +358,7 @@ struct LoaderInt4Reg {
   }
   // Stepwise commit: step 2c converts the first half of 16-byte chunk c, step
   // 2c+1 the second half and stores the chunk (chunk 8 of a pass is the key).
-  static constexpr int kWidenSteps = 0, kStoreSteps = 18 * kPass;
-  template <int I>
-  __device__ __forceinline__ void widen_step() {}
+  static constexpr int kStoreSteps = 18 * kPass;
   u32x2 part;
   template <int I>
   __device__ __forceinline__ void store_step(char* lds_buf) {
@@ -466,19 +465,16 @@ __device__ __forceinline__ H128Lane h128_lane() {
   return L;
 }
 
-// Score MFMA chain of one tile, as fenced steps: step ks issues MFMA ks, the
-// K (and, for the RoPE columns, Q^T) fragment reads kPf steps ahead, and one
-// widening step of the staged next tile, whose VALU work then runs in the
-// running MFMA's shadow.  kPf is as deep as the registers allow without
+// Score MFMA chain of one tile, as fenced steps: step ks issues MFMA ks and the
+// K (and, for the last columns, Q^T) fragment reads kPf steps ahead.  kPf is as deep as the registers allow without
 // spilling: a spill reload here would wait behind the tile loads in flight
 // (vector-memory counters retire in order).
-template <int kPf, class Loader>
+template <int kPf>
 struct H128Scores {
   const char* buf;
   const char* qtail;
   const H128Lane& L;
   const half8 (&q)[kQReg];
-  Loader& ld;
   int hq;
   floatx16 sacc;
   half8 kb[kPf], qb[kPf];
@@ -497,12 +493,10 @@ struct H128Scores {
       if constexpr (kn >= kQReg)
         qb[KS % kPf] = *reinterpret_cast<const half8*>(qtail + qtail_off(hq, 2 * (kn - kQReg) + L.g));
     }
-    if constexpr (KS < Loader::kWidenSteps) ld.template widen_step<KS>();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KS + 1 < kSteps) step<KS + 1>();
   }
   __device__ __forceinline__ floatx16 run() {
-    static_assert(Loader::kWidenSteps <= kSteps, "widening must fit in the score chain");
     __builtin_amdgcn_sched_barrier(0);
     sacc = floatx16{};
 #pragma unroll
@@ -519,12 +513,12 @@ struct H128Scores {
 // when a later tile exceeds it by more than kTauFixed); kMode 1: scores only,
 // m_ref becomes the exact max; kMode 2: against the exact max in m_ref.
 // Returns P^T as the value product's B operand (p[j]: token half j).
-template <int kMode, int kPf, class Loader>
+template <int kMode, int kPf>
 __device__ __forceinline__ void h128_scores(const char* buf, const char* qtail, const H128Lane& L,
-                                            const half8 (&q)[kQReg], Loader& ld, float& m_ref, float& l_sum,
+                                            const half8 (&q)[kQReg], float& m_ref, float& l_sum,
                                             bool& overflow, int t0, int t_end, bool page_ok, float scale_log2,
                                             half8 (&p)[2]) {
-  floatx16 sacc = H128Scores<kPf, Loader>{buf, qtail, L, q, ld, 32 * (int)(threadIdx.x >> 6) + L.hl}.run();
+  floatx16 sacc = H128Scores<kPf>{buf, qtail, L, q, 32 * (int)(threadIdx.x >> 6) + L.hl}.run();
 #pragma unroll
   for (int r = 0; r < 16; ++r) sacc[r] *= scale_log2;
   if (!page_ok || t0 + kTile128 > t_end) {          // partial tile: mask the missing rows
@@ -580,9 +574,6 @@ struct H128Values {
   char* nxt;
   Begin& begin;
   half8 pt[4], vb[2];
-  // Stores of the staged tile start at this step: spread one per MFMA when they
-  // are plain stores (widened during the scores), from step 0 otherwise.
-  static constexpr int kStoreAt = Loader::kWidenSteps > 0 ? 4 : 0;
 
   // V^T fragment (32 features x 16 tokens) for feature block 4 wave + f, token half j.
   __device__ __forceinline__ half8 vread(int j, int f) const {
@@ -601,17 +592,17 @@ struct H128Values {
     o[4 * f + hg] = mfma32x32x16(vb[f & 1], pt[hg], o[4 * f + hg]);
     if constexpr (hg == 0 && I + 4 < 32) vb[(f + 1) & 1] = vread((I + 4) >> 4, ((I + 4) >> 2) & 3);
     if constexpr (j == 0 && f == 3) pt[hg] = pread(1, hg);
-    if constexpr (I < kStoreAt + Loader::kStoreSteps && I >= kStoreAt) {
-      ld.template store_step<I - kStoreAt>(nxt);
-      if constexpr (I == kStoreAt) begin();
+    if constexpr (I < Loader::kStoreSteps) {
+      ld.template store_step<I>(nxt);
+      if constexpr (I == 0) begin();
       __builtin_amdgcn_sched_barrier(0);     // the refill may not overtake the store of the same registers
-      ld.template load_step<I - kStoreAt>();
+      ld.template load_step<I>();
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (I + 1 < 32) step<I + 1>();
   }
   __device__ __forceinline__ void run() {
-    static_assert(kStoreAt + Loader::kStoreSteps < 32, "staging must fit in the value product");
+    static_assert(Loader::kStoreSteps < 32, "staging must fit in the value product");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) pt[hg] = pread(0, hg);
@@ -650,7 +641,7 @@ __device__ __forceinline__ void h128_step(const DecodeArgs& a, int s, int seg0, 
   asm volatile("" : "+s"(pg0), "+s"(pg2));
   const int t0 = seg0 + s * kTile128;
   half8 p[2];
-  h128_scores<kMode, Loader::kScorePrefetch>(cur, qtail, L, q, ld, m_ref, l_sum, overflow, t0, seg1, pg0 >= 0,
+  h128_scores<kMode, Loader::kScorePrefetch>(cur, qtail, L, q, m_ref, l_sum, overflow, t0, seg1, pg0 >= 0,
                                                   a.scale_log2, p);
   auto begin = [&]() { ld.begin(a, pg2, seg0 + (s + 2) * kTile128, seg1); };
   if (kMode != 1) {
@@ -752,31 +743,100 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   }
 
   // ---- per-head sums from the owning waves, then normalise and write ----
-  const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
-  float* red = reinterpret_cast<float*>(pbuf);
-  __syncthreads();                                 // every wave is done with the P buffer
-  if (g == 0) red[h] = l_tot;
-  __syncthreads();
-  float inv[4];
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    const float l = red[32 * hg + hl];
-    inv[hg] = l > 0.f ? 1.f / l : 0.f;
-  }
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  if constexpr (kCache == 2) {
+    // INT4: o_part is stored straight from the accumulator layout (16-byte row
+    // pieces): with the transposed write below, this kernel spills in its tile loop.
+    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
+    float* red = reinterpret_cast<float*>(pbuf);
+    __syncthreads();                                 // every wave is done with the P buffer
+    if (g == 0) red[h] = l_tot;
+    __syncthreads();
+    float inv[4];
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
-      uint16_t* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + 128 * wave + 32 * f + 4 * g;
+      const float l = red[32 * hg + hl];
+      inv[hg] = l > 0.f ? 1.f / l : 0.f;
+    }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const floatx16& v = o[4 * f + hg];
-        const floatx4 x = floatx4{v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]} * inv[hg];
-        *reinterpret_cast<half4*>(op + 8 * rr) = __builtin_convertvector(x, half4);   // round to nearest even
+    for (int f = 0; f < 4; ++f) {
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) {
+        uint16_t* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + 128 * wave + 32 * f + 4 * g;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const floatx16& v = o[4 * f + hg];
+          const floatx4 x = floatx4{v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]} * inv[hg];
+          *reinterpret_cast<half4*>(op + 8 * rr) = __builtin_convertvector(x, half4);   // round to nearest even
+        }
       }
     }
+    if (g == 0) a.lse_part[(int64_t)it.out_row * 128 + h] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    // Lane indices are recomputed here from an opaque copy of the thread id, so
+    // that no epilogue offset is kept live (in VGPRs) across the tile loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int elane = tid & 63, ehl = elane & 31, eg = elane >> 5, eh = wave * 32 + ehl;
+    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
+    float* red = reinterpret_cast<float*>(pbuf);
+    __syncthreads();                                 // every wave is done with the P buffer
+    if (eg == 0) red[eh] = l_tot;
+    __syncthreads();
+    float inv[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const float l = red[32 * hg + ehl];
+      inv[hg] = l > 0.f ? 1.f / l : 0.f;
+    }
+    // o_part rows leave through LDS so that every store writes whole 256-byte row
+    // pieces (16 lanes per row) instead of 16-byte fragments of 32 rows.  Each wave
+    // transposes its own features [128 wave, +128) of 64 heads at a time in a
+    // private 16 KB region (rows of 256 B, 16-byte chunk c at c ^ (row & 15)).
+    char* xbuf = (wave < 2 ? lds0 : lds1) + (wave & 1) * 16384;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int hgi = 0; hgi < 2; ++hgi) {
+        const int hg = 2 * hh + hgi, row = 32 * hgi + ehl;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            // features 32 f + 16 pr + 8 j + 4 eg + 0..3 of this lane's head (j = 0, 1)
+            const floatx16& v = o[4 * f + hg];
+            u32x2 x[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int r0 = 4 * (2 * pr + j);
+              const floatx4 y = floatx4{v[r0], v[r0 + 1], v[r0 + 2], v[r0 + 3]} * inv[hg];
+              x[j] = __builtin_bit_cast(u32x2, __builtin_convertvector(y, half4));   // round to nearest even
+            }
+            // v_permlane32_swap exchanges the upper half-wave of its first operand with
+            // the lower half-wave of its second: afterwards the lane of half eg holds the eight
+            // consecutive features 8 (1 - eg) .. +7 of this 16-feature pair as (x[1], x[0]).
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(x[1][d], x[0][d], false, false);
+              x[1][d] = sw[0];
+              x[0][d] = sw[1];
+            }
+            const int chunk = 4 * f + 2 * pr + 1 - eg;
+            *reinterpret_cast<u32x4*>(xbuf + row * 256 + 16 * (chunk ^ (row & 15))) =
+                u32x4{x[1][0], x[1][1], x[0][0], x[0][1]};
+          }
+        }
+      }
+      asm volatile("" ::: "memory");           // this wave's LDS writes before its reads (in-order per wave)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int row = 4 * k + (elane >> 4), chunk = elane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xbuf + row * 256 + 16 * (chunk ^ (row & 15)));
+        st16(a.o_part + ((int64_t)it.out_row * 128 + 64 * hh + row) * kDc + 128 * wave + 8 * chunk, v);
+      }
+      asm volatile("" ::: "memory");           // reads done before the next half overwrites the region
+    }
+    if (eg == 0) a.lse_part[(int64_t)it.out_row * 128 + eh] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
-  if (g == 0) a.lse_part[(int64_t)it.out_row * 128 + h] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ===========================================================================
