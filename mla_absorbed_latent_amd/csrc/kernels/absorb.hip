@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   // Stage W_UK[h][0:128][c0:c0+128] (128 rows x 16 chunks of 16 B): all eight
-  // loads of a thread are issued before any LDS write, so they overlap.
+  // loads of a thread, and the q_nope rows of the first 32 sequences, are issued
+  // before any LDS write, so they overlap.
   const uint16_t* wsrc = w_uk + (int64_t)h * kDn * kDc + c0;
   u32x4 wv[8];
 #pragma unroll
@@ -39,6 +40,17 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     const int idx = threadIdx.x + 256 * i, d = idx >> 4, ch = idx & 15;
     wv[i] = ld16(wsrc + (int64_t)d * kDc + 8 * ch);
   }
+  const int g = lane >> 5, grp = lane >> 4, gi = lane & 15;
+  // q_nope[b][h][16 ks + 8 g .. +7] for b = b0 + lane % 32 (a sequence past B
+  // reads row 0 instead; its column is never stored).
+  auto load_q = [&](int b0, u32x4 (&qa)[kDn / 16]) {
+    const int b = b0 + (lane & 31);
+    const uint16_t* qrow = q_nope + ((int64_t)(b < B ? b : 0) * H + h) * kDn + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDn / 16; ++ks) qa[ks] = ld16(qrow + 16 * ks);
+  };
+  u32x4 qa[kDn / 16];
+  load_q(0, qa);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int idx = threadIdx.x + 256 * i, d = idx >> 4, ch = idx & 15;
@@ -54,7 +66,6 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   }
   __syncthreads();
 
-  const int g = lane >> 5, grp = lane >> 4, gi = lane & 15;
   // Transposed read: group lane gi addresses row (d) d0 + (gi >> 2), columns
   // 16 (grp & 1) + 4 (gi & 3) of this wave's 32-column block.
   const int cw = 32 * wave;                            // wave's columns within the slab
@@ -63,11 +74,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     const int b = b0 + (lane & 31);
     const bool bok = b < B;
     floatx16 acc = floatx16{};
-    const uint16_t* qrow = q_nope + ((int64_t)(bok ? b : 0) * H + h) * kDn + 8 * g;
-    u32x4 qa[kDn / 16];                                // all q fragments in flight at once
-#pragma unroll
-    for (int ks = 0; ks < kDn / 16; ++ks) qa[ks] = ld16(qrow + 16 * ks);
-    // A sequence past B reads row 0 instead; its column is never stored.
+    u32x4 qn[kDn / 16];                                // the next 32 sequences, in flight meanwhile
+    if (b0 + 32 < B) load_q(b0 + 32, qn);
 #pragma unroll
     for (int ks = 0; ks < kDn / 16; ++ks) {
       const u32x4 qv = qa[ks];
@@ -90,6 +98,10 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
         v[1] = (uint32_t)f32_to_f16_bits(acc[4 * rr + 2]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 3]) << 16);
         *reinterpret_cast<u32x2*>(dst + 8 * rr) = v;
       }
+    }
+    if (b0 + 32 < B) {
+#pragma unroll
+      for (int ks = 0; ks < kDn / 16; ++ks) qa[ks] = qn[ks];
     }
   }
 }

@@ -36,11 +36,13 @@ __global__ __launch_bounds__(256) void append_bf16(uint8_t* pool, int64_t num_pa
   const int64_t tok = gid / 72;
   const int chunk = (int)(gid % 72);
   if (tok >= n) return;
+  // Both loads are issued before either is used (one memory round trip).
+  const uint16_t* src = chunk < 64 ? c_kv + tok * kDc + chunk * 8 : k_pe + tok * kDr + (chunk - 64) * 8;
+  const u32x4 v = ld16(src);
   const int64_t slot = slots[tok];
   if (!slot_ok(slot, num_pages)) return;
-  const uint16_t* src = chunk < 64 ? c_kv + tok * kDc + chunk * 8 : k_pe + tok * kDr + (chunk - 64) * 8;
   uint8_t* dst = pool + (slot / kBlock) * kPageBf16 + (slot % kBlock) * kRowBytesBf16 + chunk * 16;
-  st16(dst, ld16(src));
+  st16(dst, v);
 }
 
 // Symmetric INT8 of `kG` consecutive bf16 values.

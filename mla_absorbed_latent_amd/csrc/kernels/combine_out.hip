@@ -138,17 +138,23 @@ __global__ __launch_bounds__(256, 2) void out_proj_kernel(const float* __restric
   }
 }
 
-// Merge and expansion in one pass, one work-group per (head, 32 sequences):
+// Merge and expansion in one pass, one work-group (8 waves) per (head, 32 sequences):
 //  1. merge: the work-group combines, for each of its sequences, the fp16
 //     partials of head h (fp32 sums, as combine_kernel), keeps o_lat[b][h][:]
 //     as fp16 in LDS, and writes o_lat / lse as well when asked;
-//  2. expand: wave w computes out^T[32 w .. 32 w + 31][b] = W_UV[h][d][:] . o_lat^T
-//     for the 32 sequences (32 x mfma 32x32x16), W_UV rows straight from HBM and
-//     o_lat^T fragments from LDS.
-// o_lat never leaves the chip, and one launch replaces two.
+//  2. expand: wave w computes out^T[16 w .. 16 w + 15][b] = W_UV[h][d][:] . o_lat^T
+//     for the 32 sequences (32 x mfma 16x16x32), W_UV rows from HBM and o_lat^T
+//     fragments from LDS.
+// Every load that does not depend on another is issued before the first use:
+// the W_UV rows at entry, the split rows of all four of a thread's sequences
+// together, so the kernel waits for about two memory round trips in all.  o_lat
+// never leaves the chip, and one launch replaces two.
 constexpr int kCoB = 32;                            // sequences per work-group
+constexpr int kCoThreads = 512;
+constexpr int kCoSeq = kCoB / (kCoThreads / 64);    // sequences per thread in the merge
+constexpr int kCoRound = 4;                         // split rows loaded together per sequence
 
-__global__ __launch_bounds__(256) void combine_out_proj_kernel(
+__global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
     const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ out_f32,
     float* __restrict__ o_lat, float* __restrict__ lse_out, int H, int B) {
@@ -157,38 +163,76 @@ __global__ __launch_bounds__(256) void combine_out_proj_kernel(
   __shared__ __attribute__((aligned(16))) char olds[kCoB * kDc * 2];   // 32 KB
   const int h = blockIdx.x % H;
   const int b0 = (blockIdx.x / H) * kCoB;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int grp = t >> 6;                           // sequence group of the merge
 
-  // ---- 1. merge: thread t owns 16-byte chunk c8 = t % 64 of sequences b0 + t / 64 + 4 i
+  // A operand of the expansion: W_UV[h][16 wave + lane % 16][32 ks + 8 (lane / 16) .. +7].
+  u32x4 wr[16];
+  {
+    const uint16_t* wrow = w_uv + ((int64_t)h * kDn + 16 * wave + (lane & 15)) * kDc + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wr[ks] = ld16(wrow + 32 * ks);
+  }
+
+  // ---- 1. merge: thread t owns 16-byte chunk c8 = t % 64 of sequences b0 + grp + 8 i
   const int c8 = t & 63;
-#pragma unroll 2
-  for (int i = 0; i < kCoB / 4; ++i) {
-    const int bi = (t >> 6) + 4 * i, b = b0 + bi;
+  int r0[kCoSeq], r1[kCoSeq];
+#pragma unroll
+  for (int i = 0; i < kCoSeq; ++i) {
+    const int b = b0 + grp + 8 * i;
+    r0[i] = b < B ? offsets[b] : 0;
+    r1[i] = b < B ? offsets[b + 1] : 0;
+  }
+  float l[kCoSeq][kCoRound];
+  half8 x[kCoSeq][kCoRound];
+#pragma unroll
+  for (int i = 0; i < kCoSeq; ++i)
+#pragma unroll
+    for (int k = 0; k < kCoRound; ++k) {
+      const int j = r0[i] + k;
+      l[i][k] = -INFINITY;
+      x[i][k] = half8{};
+      if (j < r1[i]) {
+        l[i][k] = lse_part[(int64_t)j * H + h];
+        x[i][k] = *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8);
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < kCoSeq; ++i) {
+    const int bi = grp + 8 * i, b = b0 + bi;
+    // The same sums in the same order as combine_kernel: the maximum over all
+    // rows first, then the rows in rounds of kCoRound; an empty split (lse =
+    // -inf) contributes nothing, whatever its row holds.
+    float m = -INFINITY, wsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCoRound; ++k) m = fmaxf(m, l[i][k]);
+    for (int j = r0[i] + kCoRound; j < r1[i]; ++j) m = fmaxf(m, lse_part[(int64_t)j * H + h]);
     floatx4 acc0 = floatx4{}, acc1 = floatx4{};
-    float wsum = 0.f, m = -INFINITY;
-    if (b < B) {
-      const int r0 = offsets[b], r1 = offsets[b + 1];
-      for (int j = r0; j < r1; ++j) m = fmaxf(m, lse_part[(int64_t)j * H + h]);
-      if (m != -INFINITY) {
-        for (int j0 = r0; j0 < r1; j0 += 4) {
-          half8 x[4];
-          float l[4];
+    if (m != -INFINITY) {
+      for (int j0 = r0[i]; j0 < r1[i]; j0 += kCoRound) {
+        float lr[kCoRound];
+        half8 xr[kCoRound];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int j = min(j0 + k, r1 - 1);
-            l[k] = j0 + k < r1 ? lse_part[(int64_t)j * H + h] : -INFINITY;
-            x[k] = *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8);
+        for (int k = 0; k < kCoRound; ++k) {
+          if (j0 == r0[i]) {
+            lr[k] = l[i][k];
+            xr[k] = x[i][k];
+          } else {
+            const int j = j0 + k;
+            lr[k] = j < r1[i] ? lse_part[(int64_t)j * H + h] : -INFINITY;
+            xr[k] = j < r1[i] ? *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8)
+                              : half8{};
           }
+        }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const bool empty = l[k] == -INFINITY;    // skipped outright, as if not loaded
-            const float w = empty ? 0.f : expf(l[k] - m);
-            wsum += w;
-            const floatx4 lo = __builtin_convertvector(__builtin_shufflevector(x[k], x[k], 0, 1, 2, 3), floatx4);
-            const floatx4 hi = __builtin_convertvector(__builtin_shufflevector(x[k], x[k], 4, 5, 6, 7), floatx4);
-            acc0 += w * (empty ? floatx4{} : lo);
-            acc1 += w * (empty ? floatx4{} : hi);
-          }
+        for (int k = 0; k < kCoRound; ++k) {
+          const bool empty = lr[k] == -INFINITY;
+          const float w = empty ? 0.f : expf(lr[k] - m);
+          wsum += w;
+          const floatx4 lo = __builtin_convertvector(__builtin_shufflevector(xr[k], xr[k], 0, 1, 2, 3), floatx4);
+          const floatx4 hi = __builtin_convertvector(__builtin_shufflevector(xr[k], xr[k], 4, 5, 6, 7), floatx4);
+          acc0 += w * (empty ? floatx4{} : lo);
+          acc1 += w * (empty ? floatx4{} : hi);
         }
       }
     }
@@ -209,35 +253,29 @@ __global__ __launch_bounds__(256) void combine_out_proj_kernel(
   }
   __syncthreads();
 
-  // ---- 2. expand: out^T[d][b] for d = 32 wave + lane % 32 (A operand), b = b0 + lane % 32 (B operand)
-  const int lane = t & 63, wave = t >> 6, g = lane >> 5, r = lane & 31;
-  const uint16_t* wrow = w_uv + ((int64_t)h * kDn + 32 * wave + r) * kDc + 8 * g;
-  floatx16 acc = floatx16{};
+  // ---- 2. expand: out^T[d][b], d = 16 wave + 4 (lane / 16) + r, b = b0 + 16 bb + lane % 16
+  const int bl = lane & 15, kg = lane >> 4;
+  floatx4 acc[2] = {floatx4{}, floatx4{}};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    u32x4 wr[8];                                    // eight k-steps of W_UV in flight
+  for (int ks = 0; ks < 16; ++ks) {
+    const half8 a = __builtin_bit_cast(half8, bf16x8_to_f16x8(wr[ks]));
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) wr[ks] = ld16(wrow + 16 * (8 * kb + ks));
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int kk = 8 * kb + ks;
-      const half8 bv = *reinterpret_cast<const half8*>(olds + r * (kDc * 2) + 16 * ((2 * kk + g) ^ (r & 15)));
-      acc = mfma32x32x16(__builtin_bit_cast(half8, bf16x8_to_f16x8(wr[ks])), bv, acc);
+    for (int bb = 0; bb < 2; ++bb) {
+      const int bi = 16 * bb + bl;
+      const half8 bv = *reinterpret_cast<const half8*>(olds + bi * (kDc * 2) + 16 * ((4 * ks + kg) ^ bl));
+      acc[bb] = mfma16x16x32(a, bv, acc[bb]);
     }
   }
-  // lane holds out^T[32 wave + 8 (q / 4) + 4 g + q % 4][b0 + lane % 32], q = 0..15
-  const int b = b0 + r;
-  if (b < B) {
-    const int d = 32 * wave + 4 * g;
+  const int d = 16 * wave + 4 * kg;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+  for (int bb = 0; bb < 2; ++bb) {
+    const int b = b0 + 16 * bb + bl;
+    if (b < B) {
       u32x2 v;
-      v[0] = (uint32_t)f32_to_bf16_rne(acc[4 * rr]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 1]) << 16);
-      v[1] = (uint32_t)f32_to_bf16_rne(acc[4 * rr + 2]) | ((uint32_t)f32_to_bf16_rne(acc[4 * rr + 3]) << 16);
-      *reinterpret_cast<u32x2*>(out + ((int64_t)b * H + h) * kDn + d + 8 * rr) = v;
-      if (out_f32 != nullptr)
-        *reinterpret_cast<floatx4*>(out_f32 + ((int64_t)b * H + h) * kDn + d + 8 * rr) =
-            floatx4{acc[4 * rr], acc[4 * rr + 1], acc[4 * rr + 2], acc[4 * rr + 3]};
+      v[0] = (uint32_t)f32_to_bf16_rne(acc[bb][0]) | ((uint32_t)f32_to_bf16_rne(acc[bb][1]) << 16);
+      v[1] = (uint32_t)f32_to_bf16_rne(acc[bb][2]) | ((uint32_t)f32_to_bf16_rne(acc[bb][3]) << 16);
+      *reinterpret_cast<u32x2*>(out + ((int64_t)b * H + h) * kDn + d) = v;
+      if (out_f32 != nullptr) *reinterpret_cast<floatx4*>(out_f32 + ((int64_t)b * H + h) * kDn + d) = acc[bb];
     }
   }
 }
@@ -290,7 +328,7 @@ hipError_t launch_combine_out_proj(int num_heads, const uint16_t* o_part, const 
                                   const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out, float* out_f32,
                                   float* o_lat, float* lse, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(num_heads * ((batch + kCoB - 1) / kCoB)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(num_heads * ((batch + kCoB - 1) / kCoB)), dim3(kCoThreads), 0, stream,
                      o_part, lse_part, split_offsets, w_uv, out, out_f32, o_lat, lse, num_heads, batch);
   return hipGetLastError();
 }

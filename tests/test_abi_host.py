@@ -113,6 +113,13 @@ def test_planner_uniform_batch(lib):
     items, offs = api.plan_splits(cfg, [8192] * 64, 256)
     assert len(items) == 256 and set(items[:, 2]) == {32}
     _check_plan(items, offs, [8192] * 64)
+    # the four items of a sequence sit 8 positions apart (one XCD of the 8 that
+    # work-groups are dealt to round robin), and each XCD gets 32 of them
+    pos = {}
+    for p, (seq, _, _, _) in enumerate(items):
+        pos.setdefault(seq, []).append(p % 8)
+    assert all(len(set(v)) == 1 and len(v) == 4 for v in pos.values())
+    assert sorted(np.bincount([v[0] for v in pos.values()], minlength=8)) == [8] * 8
 
 
 def test_planner_ragged_and_edges(lib):
