@@ -100,7 +100,7 @@ __device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int t) {
 // slice, refreshed every kSegPages pages: a global read of the table inside a
 // tile loop would make the compiler's wait for it also drain the tile prefetch
 // issued before it (vector-memory counters retire in order).
-constexpr int kSegPages = 2048;
+constexpr int kSegPages = 1024;
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 |
 // lgkmcnt[11:8] = 15 | vmcnt[5:4] in bits [15:14]).
@@ -129,6 +129,10 @@ __device__ __forceinline__ void fill_ptab(const DecodeArgs& a, int b, int t0, in
 // field offset stays valid), and every cache format decodes zero bytes to zeros.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[kBlock * kRowBytesBf16];
 
+// Loader thread index: a loader spreads a tile over 256 threads (the whole
+// work-group, or its 256 loading threads).
+__device__ __forceinline__ int ltid() { return threadIdx.x & 255; }
+
 // Base of page `page`, or of the zero page when the row is out of range.
 __device__ __forceinline__ const uint8_t* page_base(const DecodeArgs& a, int64_t page, bool ok, int64_t page_bytes) {
   return ok ? a.pool + page * page_bytes : g_zero_page;
@@ -142,12 +146,12 @@ struct LoaderBf16Reg {
   u32x4 r[9 * kPass];
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3;
+    const int tok = ltid() >> 3;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
       const uint8_t* src = page_base(a, page, ok, kBlock * kRowBytesBf16) +
-                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (threadIdx.x & 7);
+                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (ltid() & 7);
 #pragma unroll
       for (int k = 0; k < 9; ++k) r[9 * p + k] = ld16_stream(src + 128 * k);
     }
@@ -159,9 +163,9 @@ struct LoaderBf16Reg {
   // whole tile step to arrive before they are widened.
   const uint8_t* src;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3;
+    const int tok = ltid() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
-    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (threadIdx.x & 7);
+    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (ltid() & 7);
   }
   template <int I>
   __device__ __forceinline__ void load_step() {
@@ -180,11 +184,11 @@ struct LoaderBf16Reg {
       r[kc][d] = v;
     }
     if constexpr (I % 2 == 1)
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * kc) = r[kc];
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 128 * kc) = r[kc];
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
+    const int tok = ltid() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -216,7 +220,7 @@ struct LoaderInt8Reg {
   float s[9 * kPass];
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
+    const int tok = ltid() >> 3, c8 = ltid() & 7;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
@@ -239,7 +243,7 @@ struct LoaderInt8Reg {
   const uint8_t* pg;
   int row;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3;
+    const int tok = ltid() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
     pg = page_base(a, page, ok, kPage);
     row = (t0 % kBlock) + tok;
@@ -248,7 +252,7 @@ struct LoaderInt8Reg {
   __device__ __forceinline__ void load_step() {
     if constexpr (I % 2 == 1) {
       constexpr int k = I / 2;
-      const int c8 = threadIdx.x & 7;
+      const int c8 = ltid() & 7;
       c[k] = *reinterpret_cast<const u32x2*>(pg + row * 576 + 8 * c8 + 64 * k);
       if constexpr (k < 8) s[k] = reinterpret_cast<const float*>(pg + 64 * 576)[row * 16 + (c8 >> 2) + 2 * k];
       else s[k] = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64)[row * 8 + c8];
@@ -267,13 +271,13 @@ struct LoaderInt8Reg {
       part = int8x4_to_f16(c[kc][0], s2);
     } else {
       const u32x2 hi = int8x4_to_f16(c[kc][1], s2);
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 32 * p * kRowLds + 128 * k) =
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 32 * p * kRowLds + 128 * k) =
           u32x4{part[0], part[1], hi[0], hi[1]};
     }
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
+    const int tok = ltid() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -299,7 +303,7 @@ struct LoaderInt4Reg {
   float z[8 * kPass];        // zero point per latent chunk
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3, c8 = threadIdx.x & 7;
+    const int tok = ltid() >> 3, c8 = ltid() & 7;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
@@ -335,7 +339,7 @@ struct LoaderInt4Reg {
   const uint8_t* pg;
   int row;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = threadIdx.x >> 3;
+    const int tok = ltid() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
     pg = page_base(a, page, ok, kPage);
     row = (t0 % kBlock) + tok;
@@ -344,7 +348,7 @@ struct LoaderInt4Reg {
   __device__ __forceinline__ void load_step() {
     if constexpr (I % 2 == 1) {
       constexpr int k = I / 2;
-      const int c8 = threadIdx.x & 7;
+      const int c8 = ltid() & 7;
       const float* meta = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
       if constexpr (k < 8) {
         n[k] = *reinterpret_cast<const uint32_t*>(pg + row * 256 + 4 * c8 + 32 * k);
@@ -378,13 +382,13 @@ struct LoaderInt4Reg {
     if constexpr (I % 2 == 0) {
       part = cur;
     } else {
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 32 * p * kRowLds + 128 * k) =
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 32 * p * kRowLds + 128 * k) =
           u32x4{part[0], part[1], cur[0], cur[1]};
     }
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = threadIdx.x >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, threadIdx.x & 7);
+    const int tok = ltid() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
 #pragma unroll
@@ -844,28 +848,86 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
 // ===========================================================================
 constexpr int kTile16 = 64;
 constexpr int kBuf16 = kTile16 * kRowLds;          // 73,728 B
+// Q^T of the first kQ16Reg k-steps (32 columns each) stays in VGPRs; the other
+// k-steps sit in LDS as the register image of a wave (k-step j: 64 lanes x 16 B,
+// lane l at 16 l), which leaves the VGPRs for two staged tiles.
+constexpr int kQ16Reg = 10, kQ16Lds = kDk / 32 - kQ16Reg;
+
+// The work-group has 8 waves.  Waves 0-3 compute: wave w takes tokens 16 w ..
+// 16 w + 15 of each 64-token tile for all 16 heads (mfma 16x16x32 scores,
+// 16x16x16 values); their (max, sum, O) are merged through LDS at the end.
+// Waves 4-7 only stage tiles: they hold the next two tiles in VGPRs, write tile
+// s + 1 (widened or dequantised to fp16) into the free LDS buffer while the
+// compute waves work on tile s, and then issue the loads of tile s + 3.  Each
+// SIMD runs one wave of each kind and interleaves them, so the staging work and
+// the compute overlap, and every tile's loads have two tile steps to arrive.
+// Staging waves of decode_h16: the same segment loop and barriers as the compute
+// waves.  Stage (s + 1) % 2 holds tile s + 1 (written at step s, then reloaded
+// with tile s + 3); the other holds tile s + 2.
+template <class Loader>
+__device__ __forceinline__ void h16_stage(const DecodeArgs& a, const ItemRange& it, char* lds, int32_t* ptab) {
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+    __syncthreads();                       // earlier users of the buffers and the table are done
+    fill_ptab(a, it.b, seg0, seg1, ptab);
+    __syncthreads();
+    const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
+    Loader ld0, ld1;
+    ld0.issue(a, ptab[0], seg0, seg1);
+    ld0.commit(lds);
+    if (n_tiles > 1) ld1.issue(a, ptab[1], seg0 + kTile16, seg1);
+    if (n_tiles > 2) ld0.issue(a, ptab[2], seg0 + 2 * kTile16, seg1);
+    auto stage_step = [&](int s, Loader& ldn) {
+      __syncthreads();
+      if (s + 1 < n_tiles) {
+        ldn.commit(lds + ((s + 1) & 1) * kBuf16);
+        if (s + 3 < n_tiles) ldn.issue(a, ptab[s + 3], seg0 + (s + 3) * kTile16, seg1);
+      }
+    };
+    for (int s = 0; s < n_tiles; s += 2) {
+      stage_step(s, ld1);
+      if (s + 1 < n_tiles) stage_step(s + 1, ld0);
+    }
+  }
+}
 
 template <class Loader>
-__global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
+__global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kBuf16];
+  __shared__ __attribute__((aligned(16))) char qt16[kQ16Lds * 1024];
   __shared__ int32_t ptab[kSegPages];
   ItemRange it = item_range(a);
   if (!it.ok) return;
   if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
+  const bool stager = threadIdx.x >= 256;          // waves 4-7 (uniform per wave)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = (threadIdx.x >> 6) & 3;
   const int hl = lane & 15;          // head (MFMA column)
   const int grp = lane >> 4;         // 0..3
 
+  // Q^T k-steps past kQ16Reg go to LDS (all threads), the rest to the compute
+  // waves' VGPRs below.
+  for (int i = threadIdx.x; i < kQ16Lds * 64; i += blockDim.x) {
+    const int j = i >> 6, l = i & 63;
+    const uint16_t* src = a.q_abs + ((int64_t)it.b * 16 + (l & 15)) * kDk + 32 * (kQ16Reg + j) + 8 * (l >> 4);
+    *reinterpret_cast<u32x4*>(qt16 + 16 * i) = ld16(src);
+  }
+  if (stager) {
+    wait_vm<0>();
+    h16_stage<Loader>(a, it, lds, ptab);
+    __syncthreads();                       // the two barriers of the compute waves' merge
+    __syncthreads();
+    return;
+  }
   // Q^T as the B operand of 16x16x32: lane holds q_abs[b][hl][32 ks + 8 grp .. +7].
-  half8 q[kDk / 32];
+  half8 q[kQ16Reg];
   {
     const uint16_t* qp = a.q_abs + ((int64_t)it.b * 16 + hl) * kDk + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < kDk / 32; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 32 * ks));
+    for (int ks = 0; ks < kQ16Reg; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 32 * ks));
   }
   // Retire the Q loads here: otherwise the compiler's wait for them sits inside
-  // the tile loop and also drains the tile prefetch issued after them.
+  // the tile loop and also drains the tile loads.
   wait_vm<0>();
   floatx4 o[32];
 #pragma unroll
@@ -890,42 +952,38 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
     fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
-    Loader ld;
-    ld.issue(a, ptab[0], seg0, seg1);
-    ld.commit(lds);
-    if (n_tiles > 1) ld.issue(a, ptab[1], seg0 + kTile16, seg1);
+    // One barrier per tile, as in h16_stage: at the barrier of step s, tile s is
+    // complete in buffer s % 2 and buffer (s + 1) % 2 is free.
     for (int s = 0; s < n_tiles; ++s) {
       __syncthreads();
-      if (s + 1 < n_tiles) {
-        ld.commit(lds + ((s + 1) & 1) * kBuf16);
-        if (s + 2 < n_tiles) ld.issue(a, ptab[s + 2], seg0 + (s + 2) * kTile16, seg1);
-      }
       const char* buf = lds + (s & 1) * kBuf16;
       const int t0 = seg0 + s * kTile16;
       const bool page_ok = ptab[s] >= 0;
 
-      // Scores: 18 k-steps as two interleaved chains, reads kPf steps ahead
-      // (pinned as in the 128-head kernel).
+      // Scores: 18 k-steps as two interleaved chains, the K (and, past kQ16Reg,
+      // Q^T) fragments read kPf steps ahead, one fenced step per MFMA.
       constexpr int kSteps = kDk / 32, kPf = 4;
       __builtin_amdgcn_sched_barrier(0);
       floatx4 sacc0 = floatx4{}, sacc1 = floatx4{};
-      half8 kb[kPf];
+      half8 kb[kPf], qb[kPf];
+      auto kread = [&](int ks) { return *reinterpret_cast<const half8*>(buf + qk_off[ks & 1] + 128 * (ks >> 1)); };
+      auto qread = [&](int ks) { return *reinterpret_cast<const half8*>(qt16 + (ks - kQ16Reg) * 1024 + 16 * lane); };
 #pragma unroll
-      for (int d = 0; d < kPf; ++d) kb[d] = *reinterpret_cast<const half8*>(buf + qk_off[d & 1] + 128 * (d >> 1));
-#pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        if (ks & 1) sacc1 = mfma16x16x32(kb[ks % kPf], q[ks], sacc1);
-        else sacc0 = mfma16x16x32(kb[ks % kPf], q[ks], sacc0);
-        const int kn = ks + kPf;
-        if (kn < kSteps) kb[ks % kPf] = *reinterpret_cast<const half8*>(buf + qk_off[kn & 1] + 128 * (kn >> 1));
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
-#pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks + kPf < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      for (int d = 0; d < kPf; ++d) kb[d] = kread(d);
+      static_assert(kQ16Reg >= kPf, "the first Q^T fragments come from VGPRs");
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const half8 qv = ks < kQ16Reg ? q[ks < kQ16Reg ? ks : 0] : qb[ks % kPf];
+        if (ks & 1) sacc1 = mfma16x16x32(kb[ks % kPf], qv, sacc1);
+        else sacc0 = mfma16x16x32(kb[ks % kPf], qv, sacc0);
+        const int kn = ks + kPf;
+        if (kn < kSteps) {
+          kb[ks % kPf] = kread(kn);
+          if (kn >= kQ16Reg) qb[ks % kPf] = qread(kn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       floatx4 sacc = sacc0 + sacc1;
       float mx = -INFINITY;
 #pragma unroll
@@ -973,19 +1031,23 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
   float* red = reinterpret_cast<float*>(lds);        // [4][16][512] O, then [4][16] m, [4][16] l
   float* red_m = red + 4 * 16 * kDc;
   float* red_l = red_m + 64;
+  {
 #pragma unroll
-  for (int tile = 0; tile < 32; ++tile) {
+    for (int tile = 0; tile < 32; ++tile) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 16 + hl) * kDc + 16 * tile + 4 * grp + r] = o[tile][r];
-  }
-  if (grp == 0) {
-    red_m[wave * 16 + hl] = m_run;
-    red_l[wave * 16 + hl] = l_w;
+      for (int r = 0; r < 4; ++r) red[(wave * 16 + hl) * kDc + 16 * tile + 4 * grp + r] = o[tile][r];
+    }
+    if (grp == 0) {
+      red_m[wave * 16 + hl] = m_run;
+      red_l[wave * 16 + hl] = l_w;
+    }
   }
   __syncthreads();
   {
+    // 16 threads per head; thread i writes 16-byte chunks i + 16 k of the head's
+    // row, so a store instruction covers 256 contiguous bytes of four rows.
     const int head = threadIdx.x >> 4;               // 0..15
-    const int f0 = (threadIdx.x & 15) * 32;          // 32 features each
+    const int ci = threadIdx.x & 15;
     float mw[4], m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) { mw[w] = red_m[w * 16 + head]; m = fmaxf(m, mw[w]); }
@@ -996,16 +1058,18 @@ __global__ __launch_bounds__(256, 1) void decode_h16(DecodeArgs a) {
       l += ew[w] * red_l[w * 16 + head];
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = a.o_part + ((int64_t)it.out_row * 16 + head) * kDc + f0;
+    uint16_t* op = a.o_part + ((int64_t)it.out_row * 16 + head) * kDc;
 #pragma unroll
-    for (int f = 0; f < 32; f += 4) {
-      floatx4 v = floatx4{};
+    for (int k = 0; k < 4; ++k) {
+      const int f = 8 * ci + 128 * k;
+      floatx4 v0 = floatx4{}, v1 = floatx4{};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f0 + f);
-        v += ew[w] * x;
+        v0 += ew[w] * *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f);
+        v1 += ew[w] * *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f + 4);
       }
-      *reinterpret_cast<half4*>(op + f) = __builtin_convertvector(v * inv, half4);   // round to nearest even
+      const half4 h0 = __builtin_convertvector(v0 * inv, half4), h1 = __builtin_convertvector(v1 * inv, half4);
+      *reinterpret_cast<half8*>(op + f) = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);   // nearest even
     }
     if ((threadIdx.x & 15) == 0)
       a.lse_part[(int64_t)it.out_row * 16 + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
@@ -1026,9 +1090,10 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
-    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<H16Bf16>, grid, block, 0, stream, a);
-    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<H16Int8>, grid, block, 0, stream, a);
-    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block, 0, stream, a);
+    const dim3 block16(512);                       // 4 compute + 4 staging waves
+    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<H16Bf16>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<H16Int8>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
