@@ -149,27 +149,35 @@ __global__ __launch_bounds__(256, 2) void out_proj_kernel(const float* __restric
 // the W_UV rows at entry, the split rows of all four of a thread's sequences
 // together, so the kernel waits for about two memory round trips in all.  o_lat
 // never leaves the chip, and one launch replaces two.
-constexpr int kCoB = 32;                            // sequences per work-group
+// Shapes with few (head, 32-sequence) groups (16 heads, a few dozen sequences)
+// take work-groups of 8 sequences and a quarter of d each (each quarter merges
+// its sequences again; the partials are small), so that enough CUs work.
 constexpr int kCoThreads = 512;
-constexpr int kCoSeq = kCoB / (kCoThreads / 64);    // sequences per thread in the merge
-constexpr int kCoRound = 4;                         // split rows loaded together per sequence
 
+template <int kCoB, int kCoRound, int kDSplit>
 __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
     const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ out_f32,
     float* __restrict__ o_lat, float* __restrict__ lse_out, int H, int B) {
+  constexpr int kCoSeq = kCoB / (kCoThreads / 64);   // sequences per thread in the merge
+  constexpr int kRows = kCoB < 16 ? 16 : kCoB;        // LDS rows (the MFMA takes 16 sequences)
+  constexpr int kDPart = kDn / kDSplit;               // output rows d of this work-group
+  constexpr int kWaves = kDPart / 16;                 // waves with expansion work
+  static_assert(kCoSeq >= 1 && kRows % 16 == 0 && kWaves >= 1, "work-group shape");
   // o_lat tile, fp16: row bi (1 KB) holds sequence b0 + bi, 16-byte chunk c at
   // c ^ (bi & 15), so that the 16 rows a lane group reads land in distinct banks.
-  __shared__ __attribute__((aligned(16))) char olds[kCoB * kDc * 2];   // 32 KB
+  __shared__ __attribute__((aligned(16))) char olds[kRows * kDc * 2];
+  const int n_bc = (B + kCoB - 1) / kCoB;
   const int h = blockIdx.x % H;
-  const int b0 = (blockIdx.x / H) * kCoB;
+  const int b0 = ((blockIdx.x / H) % n_bc) * kCoB;
+  const int d0 = (blockIdx.x / (H * n_bc)) * kDPart;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int grp = t >> 6;                           // sequence group of the merge
 
-  // A operand of the expansion: W_UV[h][16 wave + lane % 16][32 ks + 8 (lane / 16) .. +7].
+  // A operand of the expansion: W_UV[h][d0 + 16 wave + lane % 16][32 ks + 8 (lane / 16) .. +7].
   u32x4 wr[16];
-  {
-    const uint16_t* wrow = w_uv + ((int64_t)h * kDn + 16 * wave + (lane & 15)) * kDc + 8 * (lane >> 4);
+  if (wave < kWaves) {
+    const uint16_t* wrow = w_uv + ((int64_t)h * kDn + d0 + 16 * wave + (lane & 15)) * kDc + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) wr[ks] = ld16(wrow + 32 * ks);
   }
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
     const half4 lo = __builtin_convertvector(acc0, half4), hi = __builtin_convertvector(acc1, half4);   // nearest even
     *reinterpret_cast<half8*>(olds + bi * (kDc * 2) + 16 * (c8 ^ (bi & 15))) =
         __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    if (b < B) {
+    if (b < B && d0 == 0) {
       if (o_lat != nullptr) {
         float* dst = o_lat + ((int64_t)b * H + h) * kDc + 8 * c8;
         *reinterpret_cast<floatx4*>(dst) = acc0;
@@ -251,26 +259,32 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
       if (lse_out != nullptr && c8 == 0) lse_out[(int64_t)b * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
     }
   }
+  for (int bi = kCoB + grp; bi < kRows; bi += kCoThreads / 64)      // rows past kCoB: zeros
+    *reinterpret_cast<half8*>(olds + bi * (kDc * 2) + 16 * (c8 ^ (bi & 15))) = half8{};
   __syncthreads();
+  if (wave >= kWaves) return;
 
-  // ---- 2. expand: out^T[d][b], d = 16 wave + 4 (lane / 16) + r, b = b0 + 16 bb + lane % 16
+  // ---- 2. expand: out^T[d][b], d = d0 + 16 wave + 4 (lane / 16) + r, b = b0 + 16 bb + lane % 16
+  constexpr int kBB = kRows / 16;
   const int bl = lane & 15, kg = lane >> 4;
-  floatx4 acc[2] = {floatx4{}, floatx4{}};
+  floatx4 acc[kBB];
+#pragma unroll
+  for (int bb = 0; bb < kBB; ++bb) acc[bb] = floatx4{};
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const half8 a = __builtin_bit_cast(half8, bf16x8_to_f16x8(wr[ks]));
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
+    for (int bb = 0; bb < kBB; ++bb) {
       const int bi = 16 * bb + bl;
       const half8 bv = *reinterpret_cast<const half8*>(olds + bi * (kDc * 2) + 16 * ((4 * ks + kg) ^ bl));
       acc[bb] = mfma16x16x32(a, bv, acc[bb]);
     }
   }
-  const int d = 16 * wave + 4 * kg;
+  const int d = d0 + 16 * wave + 4 * kg;
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
+  for (int bb = 0; bb < kBB; ++bb) {
     const int b = b0 + 16 * bb + bl;
-    if (b < B) {
+    if (16 * bb + bl < kCoB && b < B) {
       u32x2 v;
       v[0] = (uint32_t)f32_to_bf16_rne(acc[bb][0]) | ((uint32_t)f32_to_bf16_rne(acc[bb][1]) << 16);
       v[1] = (uint32_t)f32_to_bf16_rne(acc[bb][2]) | ((uint32_t)f32_to_bf16_rne(acc[bb][3]) << 16);
@@ -328,8 +342,12 @@ hipError_t launch_combine_out_proj(int num_heads, const uint16_t* o_part, const 
                                   const int32_t* split_offsets, const uint16_t* w_uv, uint16_t* out, float* out_f32,
                                   float* o_lat, float* lse, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_out_proj_kernel, dim3(num_heads * ((batch + kCoB - 1) / kCoB)), dim3(kCoThreads), 0, stream,
-                     o_part, lse_part, split_offsets, w_uv, out, out_f32, o_lat, lse, num_heads, batch);
+  if (num_heads * ((batch + 31) / 32) >= 128)
+    hipLaunchKernelGGL((combine_out_proj_kernel<32, 4, 1>), dim3(num_heads * ((batch + 31) / 32)), dim3(kCoThreads), 0,
+                       stream, o_part, lse_part, split_offsets, w_uv, out, out_f32, o_lat, lse, num_heads, batch);
+  else
+    hipLaunchKernelGGL((combine_out_proj_kernel<8, 8, 4>), dim3(num_heads * ((batch + 7) / 8) * 4), dim3(kCoThreads), 0,
+                       stream, o_part, lse_part, split_offsets, w_uv, out, out_f32, o_lat, lse, num_heads, batch);
   return hipGetLastError();
 }
 
