@@ -80,11 +80,11 @@ def cpu_baseline(case, cache_dtype, budget_s=15.0):
 def recorded_traffic(workload, cache_dtype):
     """HBM bytes per launch of mla_decode_attn measured with rocprofv3 FETCH_SIZE /
     WRITE_SIZE (scaled by a plain-copy calibration), as recorded in
-    profiles/decode_attn_<workload>.md -- or None when that record is missing or
-    was taken on a different version of the kernel source."""
+    profiles/decode_attn_<workload>_<cache dtype>.md -- or None when that record is
+    missing or was taken on a different version of the kernel source."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "decode_attn_%s.md" % workload)
+    path = os.path.join(ROOT, "profiles", "decode_attn_%s_%s.md" % (workload, cache_dtype))
     src = os.path.join(ROOT, "mla_absorbed_latent_amd", "csrc", "kernels", "decode_attn.hip")
     if not os.path.exists(path):
         return None

@@ -26,6 +26,10 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ w_uk,
                                                        uint16_t* __restrict__ q_abs, int H, int B) {
   __shared__ __attribute__((aligned(16))) char lds[kDn * kWRow];     // 32 KB
+  // Output tile of 32 sequences x 128 columns (fp16, rows of 256 B, 16-byte chunk c
+  // at c ^ (row & 15)): written in the accumulator layout, read back as whole
+  // 256-byte row pieces so that the q_abs stores are contiguous.
+  __shared__ __attribute__((aligned(16))) char otile[32 * kWRow];    // 8 KB
   const int h = blockIdx.x / (kDc / kSlab);
   const int c0 = (blockIdx.x % (kDc / kSlab)) * kSlab;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,8 +75,6 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   const int cw = 32 * wave;                            // wave's columns within the slab
   const int colh = cw + 16 * (grp & 1) + 4 * (gi & 3);  // in halves
   for (int b0 = 0; b0 < B; b0 += 32) {
-    const int b = b0 + (lane & 31);
-    const bool bok = b < B;
     floatx16 acc = floatx16{};
     u32x4 qn[kDn / 16];                                // the next 32 sequences, in flight meanwhile
     if (b0 + 32 < B) load_q(b0 + 32, qn);
@@ -89,16 +91,23 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc = mfma32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qv), acc);
     }
-    if (bok) {
-      uint16_t* dst = q_abs + ((int64_t)b * H + h) * kDk + c0 + cw + 4 * g;
+    // lane holds columns cw + 8 rr + 4 g + 0..3 of sequence b0 + lane % 32
+    const int bl = lane & 31;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 v;
-        v[0] = (uint32_t)f32_to_f16_bits(acc[4 * rr]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 1]) << 16);
-        v[1] = (uint32_t)f32_to_f16_bits(acc[4 * rr + 2]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 3]) << 16);
-        *reinterpret_cast<u32x2*>(dst + 8 * rr) = v;
-      }
+    for (int rr = 0; rr < 4; ++rr) {
+      u32x2 v;
+      v[0] = (uint32_t)f32_to_f16_bits(acc[4 * rr]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 1]) << 16);
+      v[1] = (uint32_t)f32_to_f16_bits(acc[4 * rr + 2]) | ((uint32_t)f32_to_f16_bits(acc[4 * rr + 3]) << 16);
+      *reinterpret_cast<u32x2*>(otile + bl * kWRow + 16 * (((cw >> 3) + rr) ^ (bl & 15)) + 8 * g) = v;
     }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int row = 16 * pass + (threadIdx.x >> 4), chunk = threadIdx.x & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(otile + row * kWRow + 16 * (chunk ^ (row & 15)));
+      if (b0 + row < B) st16(q_abs + ((int64_t)(b0 + row) * H + h) * kDk + c0 + 8 * chunk, v);
+    }
+    __syncthreads();                                   // the tile is free for the next 32 sequences
     if (b0 + 32 < B) {
 #pragma unroll
       for (int ks = 0; ks < kDn / 16; ++ks) qa[ks] = qn[ks];
