@@ -55,18 +55,20 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   };
   u32x4 qa[kDn / 16];
   load_q(0, qa);
+  // q_pe passthrough (bf16 -> fp16 is exact in range): the four slab work-groups of
+  // a head share it, sequence b going to slab b % 4; its loads join the ones above.
+  {
+    const int slab = c0 / kSlab, nb = (B - slab + 3) / 4;
+    for (int i = threadIdx.x; i < nb * 8; i += 256) {
+      const int b = slab + 4 * (i >> 3), ch = i & 7;
+      const u32x4 v = ld16(q_pe + ((int64_t)b * H + h) * kDr + 8 * ch);
+      st16(q_abs + ((int64_t)b * H + h) * kDk + kDc + 8 * ch, bf16x8_to_f16x8(v));
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int idx = threadIdx.x + 256 * i, d = idx >> 4, ch = idx & 15;
     *reinterpret_cast<u32x4*>(lds + d * kWRow + 16 * (ch ^ (d & 7))) = wv[i];
-  }
-  // q_pe passthrough (bf16 -> fp16 is exact in range), done by the first slab.
-  if (c0 == 0) {
-    for (int i = threadIdx.x; i < B * 8; i += 256) {
-      const int b = i >> 3, ch = i & 7;
-      const u32x4 v = ld16(q_pe + ((int64_t)b * H + h) * kDr + 8 * ch);
-      st16(q_abs + ((int64_t)b * H + h) * kDk + kDc + 8 * ch, bf16x8_to_f16x8(v));
-    }
   }
   __syncthreads();
 
