@@ -2,9 +2,12 @@
 //
 // Every sequence's pages are cut into contiguous runs of about `chunk` pages;
 // each run is one work item (one work-group).  With chunk_pages <= 0 the chunk
-// is chosen so the batch yields at least ~num_cus items, which keeps all
-// compute units busy when there are fewer sequences than CUs, while the
-// partial results stay small relative to the cache they summarise.  Runs of
+// is chosen between total / (8 num_cus) and total / num_cus by a model of the
+// run: the makespan of items dispatched longest first onto the CU that frees
+// first (an item costs its pages plus a fixed overhead for its query load and
+// partial write, about three pages' time), plus the merge's read of the partials
+// (H x 1 KB per item, spread over all CUs).  Uniform batches get one item per
+// CU; ragged ones get finer splits where that evens out the CUs' loads.  Runs of
 // one sequence are as equal as possible.  Items are ordered longest first so
 // the dispatcher starts the long ones early (a simple LPT schedule).  Within a
 // run of equally long items, the items of one sequence are placed 8 positions
@@ -16,6 +19,41 @@
 #include <vector>
 
 #include "../../../include/mla.h"
+
+#include <functional>
+#include <queue>
+
+namespace {
+
+constexpr int64_t kItemOverheadPages = 3;
+
+// Pages of each item when every sequence is cut into runs of about `chunk` pages.
+void item_pages(const int32_t* seq_lens, int32_t batch, int64_t block, int64_t chunk, std::vector<int64_t>& out) {
+  out.clear();
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t pages = (seq_lens[b] + block - 1) / block;
+    const int64_t n = std::max<int64_t>(1, (pages + chunk - 1) / chunk);
+    const int64_t base = pages / n, rem = pages % n;
+    for (int64_t j = 0; j < n; ++j) out.push_back(base + (j < rem ? 1 : 0));
+  }
+}
+
+// Modelled completion time: items longest first, each to the CU that frees first.
+int64_t modelled_makespan(std::vector<int64_t>& pages, int64_t cus) {
+  std::sort(pages.begin(), pages.end(), std::greater<int64_t>());
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int64_t i = 0; i < cus; ++i) free_at.push(0);
+  int64_t end = 0;
+  for (int64_t p : pages) {
+    const int64_t t = free_at.top() + p + kItemOverheadPages;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+}  // namespace
 
 extern "C" mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch,
                                       int32_t num_cus, int32_t chunk_pages, mla_work_item* items_host,
@@ -34,7 +72,20 @@ extern "C" mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_
   int64_t chunk = chunk_pages;
   if (chunk <= 0) {
     const int64_t cus = num_cus > 0 ? num_cus : 256;
-    chunk = std::max<int64_t>(1, (total_pages + cus - 1) / cus);
+    std::vector<int64_t> pages;
+    double best = -1.0;
+    chunk = 1;
+    const int64_t c_hi = std::max<int64_t>(1, (total_pages + cus - 1) / cus);
+    const int64_t c_lo = std::max<int64_t>(1, (total_pages + 8 * cus - 1) / (8 * cus));
+    for (int64_t c = c_hi; c >= c_lo; --c) {          // ties keep the larger chunk (fewer items)
+      item_pages(seq_lens_host, batch, block, c, pages);
+      const double t = (double)modelled_makespan(pages, cus) +
+                       (double)pages.size() * cfg->num_heads * 2048.0 / ((double)mla_cache_page_bytes(cfg) * cus);
+      if (best < 0 || t < best) {
+        best = t;
+        chunk = c;
+      }
+    }
   }
   // Count items.
   int64_t count = 0;
