@@ -129,9 +129,11 @@ __device__ __forceinline__ void fill_ptab(const DecodeArgs& a, int b, int t0, in
 // field offset stays valid), and every cache format decodes zero bytes to zeros.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[kBlock * kRowBytesBf16];
 
-// Loader thread index: a loader spreads a tile over 256 threads (the whole
-// work-group, or its 256 loading threads).
-__device__ __forceinline__ int ltid() { return threadIdx.x & 255; }
+// Loader thread index: a loader spreads a tile over 256 threads, work-group
+// threads kTid0 .. kTid0 + 255 (the whole 128-head work-group, or the staging
+// waves of the 16-head one).
+template <int kTid0>
+__device__ __forceinline__ int ltid() { return (int)threadIdx.x - kTid0; }
 
 // Base of page `page`, or of the zero page when the row is out of range.
 __device__ __forceinline__ const uint8_t* page_base(const DecodeArgs& a, int64_t page, bool ok, int64_t page_bytes) {
@@ -139,19 +141,19 @@ __device__ __forceinline__ const uint8_t* page_base(const DecodeArgs& a, int64_t
 }
 
 
-template <int kTok, int kSwz>
+template <int kTok, int kSwz, int kTid0 = 0>
 struct LoaderBf16Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 3;   // K fragments in flight in the 128-head score loop
   u32x4 r[9 * kPass];
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3;
+    const int tok = ltid<kTid0>() >> 3;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
       const uint8_t* src = page_base(a, page, ok, kBlock * kRowBytesBf16) +
-                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (ltid() & 7);
+                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (ltid<kTid0>() & 7);
 #pragma unroll
       for (int k = 0; k < 9; ++k) r[9 * p + k] = ld16_stream(src + 128 * k);
     }
@@ -163,9 +165,9 @@ struct LoaderBf16Reg {
   // whole tile step to arrive before they are widened.
   const uint8_t* src;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3;
+    const int tok = ltid<kTid0>() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
-    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (ltid() & 7);
+    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (ltid<kTid0>() & 7);
   }
   template <int I>
   __device__ __forceinline__ void load_step() {
@@ -184,11 +186,11 @@ struct LoaderBf16Reg {
       r[kc][d] = v;
     }
     if constexpr (I % 2 == 1)
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 128 * kc) = r[kc];
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid<kTid0>() >> 3, ltid<kTid0>() & 7) + 128 * kc) = r[kc];
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = ltid() >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
+    const int tok = ltid<kTid0>() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid<kTid0>() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -211,7 +213,7 @@ __device__ __forceinline__ u32x2 int8x4_to_f16(uint32_t c, half2v s) {
 }
 
 // INT8 page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key scales.
-template <int kTok, int kSwz>
+template <int kTok, int kSwz, int kTid0 = 0>
 struct LoaderInt8Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 3;
@@ -220,7 +222,7 @@ struct LoaderInt8Reg {
   float s[9 * kPass];
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3, c8 = ltid() & 7;
+    const int tok = ltid<kTid0>() >> 3, c8 = ltid<kTid0>() & 7;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
@@ -243,7 +245,7 @@ struct LoaderInt8Reg {
   const uint8_t* pg;
   int row;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3;
+    const int tok = ltid<kTid0>() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
     pg = page_base(a, page, ok, kPage);
     row = (t0 % kBlock) + tok;
@@ -252,7 +254,7 @@ struct LoaderInt8Reg {
   __device__ __forceinline__ void load_step() {
     if constexpr (I % 2 == 1) {
       constexpr int k = I / 2;
-      const int c8 = ltid() & 7;
+      const int c8 = ltid<kTid0>() & 7;
       c[k] = *reinterpret_cast<const u32x2*>(pg + row * 576 + 8 * c8 + 64 * k);
       if constexpr (k < 8) s[k] = reinterpret_cast<const float*>(pg + 64 * 576)[row * 16 + (c8 >> 2) + 2 * k];
       else s[k] = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64)[row * 8 + c8];
@@ -271,13 +273,13 @@ struct LoaderInt8Reg {
       part = int8x4_to_f16(c[kc][0], s2);
     } else {
       const u32x2 hi = int8x4_to_f16(c[kc][1], s2);
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 32 * p * kRowLds + 128 * k) =
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid<kTid0>() >> 3, ltid<kTid0>() & 7) + 32 * p * kRowLds + 128 * k) =
           u32x4{part[0], part[1], hi[0], hi[1]};
     }
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = ltid() >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
+    const int tok = ltid<kTid0>() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid<kTid0>() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
@@ -292,7 +294,7 @@ struct LoaderInt8Reg {
 
 // INT4 page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32 scales
 //            | [64][16] f32 zeros | [64][8] f32 key scales.
-template <int kTok, int kSwz>
+template <int kTok, int kSwz, int kTid0 = 0>
 struct LoaderInt4Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 2;    // its staging registers leave room for two
@@ -303,7 +305,7 @@ struct LoaderInt4Reg {
   float z[8 * kPass];        // zero point per latent chunk
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3, c8 = ltid() & 7;
+    const int tok = ltid<kTid0>() >> 3, c8 = ltid<kTid0>() & 7;
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
@@ -339,7 +341,7 @@ struct LoaderInt4Reg {
   const uint8_t* pg;
   int row;
   __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
-    const int tok = ltid() >> 3;
+    const int tok = ltid<kTid0>() >> 3;
     const bool ok = page >= 0 && t0 + tok < t_end;
     pg = page_base(a, page, ok, kPage);
     row = (t0 % kBlock) + tok;
@@ -348,7 +350,7 @@ struct LoaderInt4Reg {
   __device__ __forceinline__ void load_step() {
     if constexpr (I % 2 == 1) {
       constexpr int k = I / 2;
-      const int c8 = ltid() & 7;
+      const int c8 = ltid<kTid0>() & 7;
       const float* meta = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
       if constexpr (k < 8) {
         n[k] = *reinterpret_cast<const uint32_t*>(pg + row * 256 + 4 * c8 + 32 * k);
@@ -382,13 +384,13 @@ struct LoaderInt4Reg {
     if constexpr (I % 2 == 0) {
       part = cur;
     } else {
-      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid() >> 3, ltid() & 7) + 32 * p * kRowLds + 128 * k) =
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid<kTid0>() >> 3, ltid<kTid0>() & 7) + 32 * p * kRowLds + 128 * k) =
           u32x4{part[0], part[1], cur[0], cur[1]};
     }
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
-    const int tok = ltid() >> 3;
-    char* dst = lds_buf + swz<kSwz>(tok, ltid() & 7);
+    const int tok = ltid<kTid0>() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid<kTid0>() & 7);
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
 #pragma unroll
@@ -1077,9 +1079,9 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-using H16Bf16 = LoaderBf16Reg<kTile16, kSwz16>;
-using H16Int8 = LoaderInt8Reg<kTile16, kSwz16>;
-using H16Int4 = LoaderInt4Reg<kTile16, kSwz16>;
+using H16Bf16 = LoaderBf16Reg<kTile16, kSwz16, 256>;   // the staging waves are threads 256..511
+using H16Int8 = LoaderInt8Reg<kTile16, kSwz16, 256>;
+using H16Int4 = LoaderInt4Reg<kTile16, kSwz16, 256>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;

@@ -1,0 +1,74 @@
+"""Code-generation checks of the decode kernels (CPU only: hipcc cross-compiles).
+
+A register spill reloaded inside a tile loop waits behind the tile loads in
+flight (vector-memory counters retire in order) and costs a memory latency per
+reload; one such regression made the 128-head INT4 kernel six times slower with
+every parity test still passing.  This test compiles decode_attn.hip to gfx950
+assembly and checks that no hot loop of any decode kernel (a loop holding more
+than 30 matrix instructions, innermost) reads scratch memory, and that every decode kernel
+uses no private scratch arrays beyond a few spilled values.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KDIR = os.path.join(ROOT, "mla_absorbed_latent_amd", "csrc", "kernels")
+HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+
+pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("asm") / "decode_attn.s")
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I" + KDIR, "-I" + os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-o", out, os.path.join(KDIR, "decode_attn.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    return open(out).read().split("\n")
+
+
+def _kernels(lines):
+    starts = [(i, m.group(1)) for i, l in enumerate(lines) for m in [re.match(r"^(_ZN3mla\d+decode_h\w+):", l)] if m]
+    assert len(starts) == 6, starts          # decode_h128 x 3 formats, decode_h16 x 3 loaders
+    for st, name in starts:
+        en = next(i for i in range(st, len(lines)) if "s_endpgm" in lines[i])
+        yield name, lines[st:en]
+
+
+def _hot_loops(body):
+    """Innermost loops holding more than 30 matrix instructions (the tile loops)."""
+    labels = {}
+    for i, l in enumerate(body):
+        m = re.match(r"^(\.LBB\d+_\d+):", l)
+        if m:
+            labels[m.group(1)] = i
+    loops = []
+    for i, l in enumerate(body):
+        m = re.search(r"s_(?:c)?branch\w*\s+(\.LBB\d+_\d+)$", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            a, b = labels[m.group(1)], i
+            if sum("v_mfma" in body[j] for j in range(a, b)) > 30:
+                loops.append((a, b))
+    for a, b in loops:
+        if not any(a <= c and d <= b and (c, d) != (a, b) for c, d in loops):
+            yield a, b
+
+
+def test_no_scratch_reads_in_tile_loops(asm):
+    for name, body in _kernels(asm):
+        loops = list(_hot_loops(body))
+        assert loops, name
+        for a, b in loops:
+            reloads = sum("scratch_load" in body[j] for j in range(a, b))
+            assert reloads == 0, (name, a, b, reloads)
+
+
+def test_scratch_stays_small(asm):
+    text = "\n".join(asm)
+    for m in re.finditer(r"\.name:\s+(_ZN3mla\d+decode_h\S+)\s*\n(?:.*\n){0,80}?\s+\.private_segment_fixed_size:\s+(\d+)", text):
+        assert int(m.group(2)) <= 128, (m.group(1), m.group(2))
