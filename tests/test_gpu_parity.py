@@ -223,6 +223,26 @@ def test_output_projection_with_wo(fused):
     assert mx <= MAX_REL and mean <= MEAN_REL
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_item_longer_than_a_page_table_segment(H):
+    """One work item of 1,032 pages: the kernels copy the block table to LDS in
+    segments of 1,024 pages, so this item crosses a segment boundary (and ends in
+    a ragged tile).  A short second sequence rides along."""
+    lens = [66_000, 300]
+    case = mla_synth.small_decode(case_id=21, H=H, seq_lens=lens)
+    run, dev = upload(case)
+    run.plan(lens, chunk_pages=2000)
+    assert run.n_items == 2
+    out = run.step(dev["q_nope"], dev["q_pe"], dev["w_uk"], dev["w_uv"], dev["block_table"], dev["seq_lens"])
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    for b in (0, 1):
+        ref_out, _, _ = oracle_seq(case, b)
+        mx, mean = errors(out[b], ref_out)
+        _note("  seq %d L=%d max_rel %.2e mean_rel %.2e" % (b, lens[b], mx, mean))
+        assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled
 FULL = [
     ("v2lite_decode", lambda: mla_synth.v2lite_decode(), 0),
