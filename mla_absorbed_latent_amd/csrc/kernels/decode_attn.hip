@@ -135,9 +135,12 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_page[kBlock * kRowBytesB
 template <int kTid0>
 __device__ __forceinline__ int ltid() { return (int)threadIdx.x - kTid0; }
 
-// Base of page `page`, or of the zero page when the row is out of range.
+// Base of page `page`, or of the zero page when the row is out of range.  Both
+// operands are selected, so that no branch (and no exec-masked region) forms
+// around the multiply inside a tile loop.
 __device__ __forceinline__ const uint8_t* page_base(const DecodeArgs& a, int64_t page, bool ok, int64_t page_bytes) {
-  return ok ? a.pool + page * page_bytes : g_zero_page;
+  const uint8_t* base = ok ? a.pool : g_zero_page;
+  return base + (ok ? page : 0) * page_bytes;
 }
 
 
@@ -207,6 +210,18 @@ __device__ __forceinline__ u32x2 int8x4_to_f16(uint32_t c, half2v s) {
   const uint32_t u = c ^ 0x80808080u;
   const uint32_t h0 = 0x64006400u | (u & 0xffu) | ((u & 0xff00u) << 8);
   const uint32_t h1 = 0x64006400u | ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u);
+  const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  return u32x2{__builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h0) + bias) * s),
+               __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h1) + bias) * s)};
+}
+// The same values, each fp16 pair assembled by one byte permute (bytes 0-3 of
+// the permute's 8-byte source are u, bytes 4-7 the constant 0x64 bytes).  The two
+// selectors occupy VGPRs, so only the staging waves of the 16-head kernel,
+// which have registers to spare, use this form.
+__device__ __forceinline__ u32x2 int8x4_to_f16_perm(uint32_t c, half2v s) {
+  const uint32_t u = c ^ 0x80808080u;
+  const uint32_t h0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);   // (u.b0, u.b1)
+  const uint32_t h1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);   // (u.b2, u.b3)
   const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   return u32x2{__builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h0) + bias) * s),
                __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h1) + bias) * s)};
@@ -408,6 +423,291 @@ struct LoaderInt4Reg {
       const u32x2 lo = int8x4_to_f16(kc[p][0], k2), hi = int8x4_to_f16(kc[p][1], k2);
       *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Wide loaders of the 16-head kernel's staging waves (64-token tiles, 256
+// threads): four threads per token, each loading 16-byte pieces, so that a tile
+// takes a third of the load instructions of the loaders above (their narrow
+// code, scale and zero loads made the staging waves issue-bound).  Thread t owns
+// bytes 16 c4 + 64 i of each code row of token wide_tok(t), c4 = t % 4.  The
+// values written to LDS are the same as the loaders above write.
+//
+// A wave covers 16 tokens; its 4-thread groups alternate between tokens r and
+// r + 8, whose swizzle keys differ in their low bit, so that the eight threads
+// of two neighbouring groups store into complementary halves of a 128-byte bank
+// row (tokens r and r + 1 share a key and would collide).
+template <int kTid0>
+__device__ __forceinline__ int wide_tok() {
+  const int t = ltid<kTid0>(), g = (t >> 2) & 15;
+  return 16 * (t >> 6) + (g >> 1) + 8 * (g & 1);
+}
+
+// Eight packed nibbles (byte b: element 2b in its low nibble, 2b + 1 in its high
+// one) -> eight fp16 values q * s + z, as four fp16 pairs.  Byte permutes place
+// each nibble under the constant 0x64 high byte (fp16 1024 + q, exactly).
+__device__ __forceinline__ u32x4 nib8_to_f16(uint32_t w, half2v s2, half2v z2) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  const uint32_t x0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // lo.b0 hi.b0 lo.b1 hi.b1
+  const uint32_t x1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // lo.b2 hi.b2 lo.b3 hi.b3
+  // Each pair is formed in a scalar: hipcc's __builtin_bit_cast of a vector
+  // element (r[j]) reads element 0 whatever the index.
+  const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  auto cv = [&](uint32_t h) { return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h) + bias) * s2 + z2); };
+  return u32x4{cv(__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)), cv(__builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)),
+               cv(__builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)), cv(__builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u))};
+}
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Loads written as inline assembly whose destination is tied to the register
+// that held the previous tile ("+v"), for the staging waves of the 16-head
+// kernel.  With compiler-visible loads, the register allocator kept the two
+// alternating tiles in different registers from one pass of the loop to the
+// next and copied them at the back edge; each copy waited for its load, so a
+// load issued two steps ahead was in practice waited for one step ahead.  The
+// compiler does not count these loads: their users wait with wait_vm<> and then
+// settle() the registers (an empty asm that reads and writes them), so that no
+// use moves above the wait.
+template <int kOff>
+__device__ __forceinline__ void asm_ld16_nt(u32x4& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2 nt" : "+v"(r) : "v"(p), "n"(kOff));
+}
+template <int kOff>
+__device__ __forceinline__ void asm_ld16(floatx4& r, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "+v"(r) : "v"(p), "n"(kOff));
+}
+template <int kOff, class T>
+__device__ __forceinline__ void asm_ld8(T& r, const void* p) {
+  static_assert(sizeof(T) == 8, "8-byte register pair");
+  asm volatile("global_load_dwordx2 %0, %1, off offset:%2" : "+v"(r) : "v"(p), "n"(kOff));
+}
+template <int kOff>
+__device__ __forceinline__ void asm_ld4(float& r, const void* p) {
+  asm volatile("global_load_dword %0, %1, off offset:%2" : "+v"(r) : "v"(p), "n"(kOff));
+}
+template <class T>
+__device__ __forceinline__ void settle(T& r) { asm volatile("" : "+v"(r)); }
+
+// Value of x in lane kLane of this lane's quad (lanes 4q .. 4q + 3), by DPP.
+template <int kLane>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kLane * 0x55, 0xf, 0xf, false));
+}
+
+// 4 x 4 transpose within a quad: lane r (= r) of the quad returns
+// (a_0[r], a_1[r], a_2[r], a_3[r]), a_k being lane k's argument.  Two exchange
+// rounds, with partner r ^ 1 and then r ^ 2.
+__device__ __forceinline__ floatx4 quad_transpose(floatx4 a, int r) {
+  auto xchg = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  const bool r0 = r & 1, r1 = r & 2;
+  floatx4 c;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {       // c[k] = a from lane (r & ~1) | (k & 1), component (k & ~1) | (r & 1)
+    const float recv = xchg(r0 ? a[2 * p] : a[2 * p + 1], std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    c[2 * p] = r0 ? recv : a[2 * p];
+    c[2 * p + 1] = r0 ? a[2 * p + 1] : recv;
+  }
+  floatx4 d;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {       // d[k] = c from lane (r & ~2) | (k & 2), component (k & ~2) | (r & 2)
+    const float recv = xchg(r1 ? c[q] : c[q + 2], std::integral_constant<int, 0x4E>{});       // quad_perm [2,3,0,1]
+    d[q] = r1 ? recv : c[q];
+    d[q + 2] = r1 ? c[q + 2] : recv;
+  }
+  return d;
+}
+
+// bf16 for the 16-head kernel's staging waves: the row mapping of LoaderBf16Reg
+// (eight threads per token, two 32-token passes), with tied assembly loads.
+template <int kSwz, int kTid0>
+struct LoaderBf16Wide {
+  static constexpr int kLoads = 18;      // load instructions per tile
+  u32x4 r[18] = {};
+
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = ltid<kTid0>() >> 3;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      const uint8_t* src = page_base(a, page, ok, kBlock * kRowBytesBf16) +
+                           ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 + 16 * (ltid<kTid0>() & 7);
+      asm_ld16_nt<0>(r[9 * p + 0], src);
+      asm_ld16_nt<128>(r[9 * p + 1], src);
+      asm_ld16_nt<256>(r[9 * p + 2], src);
+      asm_ld16_nt<384>(r[9 * p + 3], src);
+      asm_ld16_nt<512>(r[9 * p + 4], src);
+      asm_ld16_nt<640>(r[9 * p + 5], src);
+      asm_ld16_nt<768>(r[9 * p + 6], src);
+      asm_ld16_nt<896>(r[9 * p + 7], src);
+      asm_ld16_nt<1024>(r[9 * p + 8], src);
+    }
+    return page >= 0;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int k = 0; k < 18; ++k) settle(r[k]);
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    const int tok = ltid<kTid0>() >> 3;
+    char* dst = lds_buf + swz<kSwz>(tok, ltid<kTid0>() & 7);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int k = 0; k < 9; ++k)
+        *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = bf16x8_to_f16x8(r[9 * p + k]);
+  }
+};
+
+// INT8 (page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key
+// scales).  Piece i < 8 holds latent codes 64 i + 16 c4 .. +15, one 32-code
+// block (c4 / 2 + 2 i); piece 8 the key codes 16 c4 .. +15, key blocks 2 c4 and
+// 2 c4 + 1.  Its two 8-code halves are LDS chunks 2 c4 and 2 c4 + 1 of 128-byte
+// group i.  The four threads of a token (one quad of lanes) load its 16 latent
+// scales as four 16-byte pieces and pass them round by DPP: one load instead of
+// eight 4-byte ones, since load instructions, not bytes, pace the staging.
+template <int kSwz, int kTid0>
+struct LoaderInt8Wide {
+  static constexpr int kPage = kBlock * 672;
+  static constexpr int kLoads = 11;      // load instructions per tile
+  u32x4 c[9] = {};
+  floatx4 sv = {};           // latent scales 4 c4 .. 4 c4 + 3 of the token
+  floatx2 ks = {};
+
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = wide_tok<kTid0>(), c4 = ltid<kTid0>() & 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    const int row = (t0 % kBlock) + tok;
+    const uint8_t* pg = page_base(a, page, ok, kPage);
+    const uint8_t* codes = pg + row * 576 + 16 * c4;
+    asm_ld16_nt<0>(c[0], codes);
+    asm_ld16_nt<64>(c[1], codes);
+    asm_ld16_nt<128>(c[2], codes);
+    asm_ld16_nt<192>(c[3], codes);
+    asm_ld16_nt<256>(c[4], codes);
+    asm_ld16_nt<320>(c[5], codes);
+    asm_ld16_nt<384>(c[6], codes);
+    asm_ld16_nt<448>(c[7], codes);
+    asm_ld16_nt<512>(c[8], codes);
+    asm_ld16<0>(sv, pg + 64 * 576 + row * 64 + 16 * c4);
+    asm_ld8<0>(ks, pg + 64 * 576 + 64 * 64 + row * 32 + 8 * c4);
+    return page >= 0;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) settle(c[i]);
+    settle(sv);
+    settle(ks);
+  }
+  // Scale of piece i < 8, block b = c4 / 2 + 2 i: component b % 4 of quad lane b / 4 = i / 2.
+  template <int I>
+  __device__ __forceinline__ float scale(bool upper) const {
+    const float lo = quad_bcast<I / 2>(sv[2 * (I % 2)]), hi = quad_bcast<I / 2>(sv[2 * (I % 2) + 1]);
+    return upper ? hi : lo;
+  }
+  template <int I>
+  __device__ __forceinline__ void commit_piece(char* d0, char* d1, bool upper) {
+    float f0, f1;
+    if constexpr (I < 8) {
+      f0 = f1 = scale<I>(upper);
+    } else {
+      f0 = ks[0];
+      f1 = ks[1];
+    }
+    const _Float16 s0 = (_Float16)f0, s1 = (_Float16)f1;
+    const u32x2 a0 = int8x4_to_f16_perm(c[I][0], half2v{s0, s0}), a1 = int8x4_to_f16_perm(c[I][1], half2v{s0, s0});
+    const u32x2 b0 = int8x4_to_f16_perm(c[I][2], half2v{s1, s1}), b1 = int8x4_to_f16_perm(c[I][3], half2v{s1, s1});
+    *reinterpret_cast<u32x4*>(d0 + 128 * I) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(d1 + 128 * I) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    const int tok = wide_tok<kTid0>(), c4 = ltid<kTid0>() & 3;
+    char* d0 = lds_buf + swz<kSwz>(tok, 2 * c4);
+    char* d1 = lds_buf + swz<kSwz>(tok, 2 * c4 + 1);
+    const bool upper = c4 >= 2;
+    commit_piece<0>(d0, d1, upper);
+    commit_piece<1>(d0, d1, upper);
+    commit_piece<2>(d0, d1, upper);
+    commit_piece<3>(d0, d1, upper);
+    commit_piece<4>(d0, d1, upper);
+    commit_piece<5>(d0, d1, upper);
+    commit_piece<6>(d0, d1, upper);
+    commit_piece<7>(d0, d1, upper);
+    commit_piece<8>(d0, d1, upper);
+  }
+};
+
+// INT4 (page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32
+// scales | [64][16] f32 zeros | [64][8] f32 key scales).  Piece i < 4 holds the
+// 32 latent values 32 c4 + 128 i .. +31, one block (c4 + 4 i); its 16-byte
+// chunks j = 0..3 are chunks 4 (c4 % 2) + j of 128-byte group 2 i + c4 / 2.
+// Threads c4 >= 2 write their chunks in the order j ^ 2, so that the four
+// threads of a token write four different LDS bank groups at every store.  The
+// key piece (16 codes at 16 c4) goes to chunks 2 c4, 2 c4 + 1 of group 8.
+template <int kSwz, int kTid0>
+struct LoaderInt4Wide {
+  static constexpr int kLoads = 8;       // load instructions per tile
+  static constexpr int kPage = kBlock * 480;
+  u32x4 n[4] = {};
+  floatx4 sq = {}, zq = {};  // scales / zeros 4 c4 .. 4 c4 + 3 of the token (transposed in commit)
+  u32x4 kc = {};
+  floatx2 ks = {};
+
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = wide_tok<kTid0>(), c4 = ltid<kTid0>() & 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    const int row = (t0 % kBlock) + tok;
+    const uint8_t* pg = page_base(a, page, ok, kPage);
+    const uint8_t* nib = pg + row * 256 + 16 * c4;
+    asm_ld16_nt<0>(n[0], nib);
+    asm_ld16_nt<64>(n[1], nib);
+    asm_ld16_nt<128>(n[2], nib);
+    asm_ld16_nt<192>(n[3], nib);
+    asm_ld16_nt<0>(kc, pg + 64 * 256 + row * 64 + 16 * c4);
+    const uint8_t* meta = pg + 64 * 256 + 64 * 64;
+    asm_ld16<0>(sq, meta + row * 64 + 16 * c4);
+    asm_ld16<0>(zq, meta + 64 * 64 + row * 64 + 16 * c4);
+    asm_ld8<0>(ks, meta + 2 * 64 * 64 + row * 32 + 8 * c4);
+    return page >= 0;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) settle(n[i]);
+    settle(sq);
+    settle(zq);
+    settle(kc);
+    settle(ks);
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    const int tok = wide_tok<kTid0>(), c4 = ltid<kTid0>() & 3;
+    const bool swap = c4 >= 2;
+    // All-ones for swapping threads; opaque, so that the choice below stays a
+    // bitwise blend (one v_bfi) instead of becoming a runtime array index.
+    uint32_t blend = swap ? ~0u : 0u;
+    asm volatile("" : "+v"(blend));
+    char* dst[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = lds_buf + swz<kSwz>(tok, 4 * (c4 & 1) + (j ^ (swap ? 2 : 0))) + 128 * (c4 >> 1);
+    // Block c4 + 4 i's scale is component c4 of quad lane i's sq: a 4 x 4
+    // transpose within the quad.
+    const floatx4 st = quad_transpose(sq, c4), zt = quad_transpose(zq, c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 sh = (_Float16)st[i], zh = (_Float16)zt[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (n[i][j] & ~blend) | (n[i][j ^ 2] & blend);
+        *reinterpret_cast<u32x4*>(dst[j] + 256 * i) = nib8_to_f16(w, half2v{sh, sh}, half2v{zh, zh});
+      }
+    }
+    const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
+    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4) + 128 * 8) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4 + 1) + 128 * 8) = u32x4{b0[0], b0[1], b1[0], b1[1]};
   }
 };
 
@@ -874,22 +1174,34 @@ __device__ __forceinline__ void h16_stage(const DecodeArgs& a, const ItemRange& 
     fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
+    // Every step commits and issues unconditionally (tiles past the end load
+    // the zero page and land in the idle buffer).  The loads are the loaders'
+    // tied assembly loads, so the waits are explicit: a commit waits until only
+    // the other loader's tile is in flight.
     Loader ld0, ld1;
     ld0.issue(a, ptab[0], seg0, seg1);
+    wait_vm<0>();
+    ld0.settle_all();
     ld0.commit(lds);
-    if (n_tiles > 1) ld1.issue(a, ptab[1], seg0 + kTile16, seg1);
-    if (n_tiles > 2) ld0.issue(a, ptab[2], seg0 + 2 * kTile16, seg1);
+    ld1.issue(a, n_tiles > 1 ? ptab[1] : -1, seg0 + kTile16, seg1);
+    ld0.issue(a, n_tiles > 2 ? ptab[2] : -1, seg0 + 2 * kTile16, seg1);
     auto stage_step = [&](int s, Loader& ldn) {
       __syncthreads();
-      if (s + 1 < n_tiles) {
-        ldn.commit(lds + ((s + 1) & 1) * kBuf16);
-        if (s + 3 < n_tiles) ldn.issue(a, ptab[s + 3], seg0 + (s + 3) * kTile16, seg1);
-      }
+      // The page id is read before the tile's LDS stores are issued, so that
+      // waiting for it does not wait for them to drain.
+      const int next_page = s + 3 < n_tiles ? ptab[s + 3] : -1;
+      wait_vm<Loader::kLoads>();           // the other loader's tile stays in flight
+      ldn.settle_all();
+      ldn.commit(lds + ((s + 1) & 1) * kBuf16);
+      ldn.issue(a, next_page, seg0 + (s + 3) * kTile16, seg1);
     };
+    // Pairs of steps (an odd tile count gets one idle step, matched by an extra
+    // barrier in the compute waves).
     for (int s = 0; s < n_tiles; s += 2) {
       stage_step(s, ld1);
-      if (s + 1 < n_tiles) stage_step(s + 1, ld0);
+      stage_step(s + 1, ld0);
     }
+    wait_vm<0>();                          // the last (zero-page) tiles
   }
 }
 
@@ -1023,6 +1335,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
         o[tile] = mfma16x16x16(av, p, o[tile]);
       }
     }
+    if (n_tiles & 1) __syncthreads();      // the staging waves' idle step
   }
 
   // ---- merge the four waves (each saw a quarter of every page) ----
@@ -1079,9 +1392,9 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-using H16Bf16 = LoaderBf16Reg<kTile16, kSwz16, 256>;   // the staging waves are threads 256..511
-using H16Int8 = LoaderInt8Reg<kTile16, kSwz16, 256>;
-using H16Int4 = LoaderInt4Reg<kTile16, kSwz16, 256>;
+using H16Bf16 = LoaderBf16Wide<kSwz16, 256>;   // the staging waves are threads 256..511
+using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
+using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
