@@ -31,16 +31,25 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
                                                       float* __restrict__ lse_out, int H) {
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int r0 = offsets[b], r1 = offsets[b + 1];
+  // The maximum in batches of eight independent loads.
   float m = -INFINITY;
-  for (int j = r0; j < r1; ++j) m = fmaxf(m, lse_part[(int64_t)j * H + h]);
+  for (int j = r0; j < r1; j += 8) {
+    float lb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float lv = lse_part[(int64_t)min(j + k, r1 - 1) * H + h];
+      lb[k] = j + k < r1 ? lv : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, lb[k]);
+  }
   floatx4 acc = floatx4{};
   float wsum = 0.f;
   if (m != -INFINITY) {
-    // Four splits per round: their rows are loaded together, then weighted; an
-    // empty split (lse = -inf) contributes nothing, whatever its row holds.
-    for (int j0 = r0; j0 < r1; j0 += 4) {
-      floatx4 x[4];
-      float l[4];
+    // Four splits per round, in order: a round's rows are loaded while the round
+    // before is weighted; an empty split (lse = -inf) contributes nothing,
+    // whatever its row holds.
+    auto load = [&](int j0, floatx4 (&x)[4], float (&l)[4]) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int j = min(j0 + k, r1 - 1);
@@ -48,12 +57,25 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
         x[k] = __builtin_convertvector(*reinterpret_cast<const half4*>(o_part + ((int64_t)j * H + h) * kDc + 4 * threadIdx.x),
                                       floatx4);
       }
+    };
+    floatx4 x[4];
+    float l[4];
+    load(r0, x, l);
+    for (int j0 = r0; j0 < r1; j0 += 4) {
+      floatx4 xn[4];
+      float ln[4];
+      load(j0 + 4, xn, ln);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bool empty = l[k] == -INFINITY;      // skipped outright, as if not loaded
         const float w = empty ? 0.f : expf(l[k] - m);
         wsum += w;
         acc += w * (empty ? floatx4{} : x[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[k] = xn[k];
+        l[k] = ln[k];
       }
     }
   }
@@ -172,7 +194,10 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
   const int b0 = ((blockIdx.x / H) % n_bc) * kCoB;
   const int d0 = (blockIdx.x / (H * n_bc)) * kDPart;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int grp = t >> 6;                           // sequence group of the merge
+  // Sequence group of the merge: one per wave, made wave-uniform so that the
+  // split offsets below come through scalar loads (a vector load of them,
+  // queued behind the W_UV loads, made the split rows wait for W_UV).
+  const int grp = __builtin_amdgcn_readfirstlane(t >> 6);
 
   // A operand of the expansion: W_UV[h][d0 + 16 wave + lane % 16][32 ks + 8 (lane / 16) .. +7].
   u32x4 wr[16];
@@ -191,19 +216,25 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
     r0[i] = b < B ? offsets[b] : 0;
     r1[i] = b < B ? offsets[b + 1] : 0;
   }
+  // Every split row is loaded without a branch, from an index clamped into the
+  // sequence's rows (row 0 for an empty one), and masked afterwards: a load
+  // under a branch left its value to be copied at the join, and each copy
+  // waited for its load.  With no split row at all (every sequence empty) the
+  // loads read W_UV instead, which is always there; their values are masked.
+  const bool any_rows = offsets[B] > 0;
+  const uint16_t* op = any_rows ? o_part : w_uv;
+  const float* lp = any_rows ? lse_part : reinterpret_cast<const float*>(w_uv);
+  auto row_of = [&](int j, int i) { return max(min(j, r1[i] - 1), 0); };
   float l[kCoSeq][kCoRound];
   half8 x[kCoSeq][kCoRound];
 #pragma unroll
   for (int i = 0; i < kCoSeq; ++i)
 #pragma unroll
     for (int k = 0; k < kCoRound; ++k) {
-      const int j = r0[i] + k;
-      l[i][k] = -INFINITY;
-      x[i][k] = half8{};
-      if (j < r1[i]) {
-        l[i][k] = lse_part[(int64_t)j * H + h];
-        x[i][k] = *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8);
-      }
+      const int j = r0[i] + k, jc = row_of(j, i);
+      const float lv = lp[(int64_t)jc * H + h];
+      x[i][k] = *reinterpret_cast<const half8*>(op + ((int64_t)jc * H + h) * kDc + 8 * c8);
+      l[i][k] = j < r1[i] ? lv : -INFINITY;
     }
 #pragma unroll
   for (int i = 0; i < kCoSeq; ++i) {
@@ -214,23 +245,38 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
     float m = -INFINITY, wsum = 0.f;
 #pragma unroll
     for (int k = 0; k < kCoRound; ++k) m = fmaxf(m, l[i][k]);
-    for (int j = r0[i] + kCoRound; j < r1[i]; ++j) m = fmaxf(m, lse_part[(int64_t)j * H + h]);
+    // The rest of the maximum in batches of eight independent loads (a long
+    // sequence of a ragged batch has dozens of splits).
+    for (int j = r0[i] + kCoRound; j < r1[i]; j += 8) {
+      float lb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float lv = lp[(int64_t)row_of(j + k, i) * H + h];
+        lb[k] = j + k < r1[i] ? lv : -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, lb[k]);
+    }
     floatx4 acc0 = floatx4{}, acc1 = floatx4{};
     if (m != -INFINITY) {
+      // Rounds of kCoRound splits in order; each round's rows are loaded while
+      // the round before is summed.
+      float lr[kCoRound];
+      half8 xr[kCoRound];
+#pragma unroll
+      for (int k = 0; k < kCoRound; ++k) {
+        lr[k] = l[i][k];
+        xr[k] = x[i][k];
+      }
       for (int j0 = r0[i]; j0 < r1[i]; j0 += kCoRound) {
-        float lr[kCoRound];
-        half8 xr[kCoRound];
+        float ln[kCoRound];
+        half8 xn[kCoRound];
 #pragma unroll
         for (int k = 0; k < kCoRound; ++k) {
-          if (j0 == r0[i]) {
-            lr[k] = l[i][k];
-            xr[k] = x[i][k];
-          } else {
-            const int j = j0 + k;
-            lr[k] = j < r1[i] ? lse_part[(int64_t)j * H + h] : -INFINITY;
-            xr[k] = j < r1[i] ? *reinterpret_cast<const half8*>(o_part + ((int64_t)j * H + h) * kDc + 8 * c8)
-                              : half8{};
-          }
+          const int j = j0 + kCoRound + k, jc = row_of(j, i);
+          const float lv = lp[(int64_t)jc * H + h];
+          xn[k] = *reinterpret_cast<const half8*>(op + ((int64_t)jc * H + h) * kDc + 8 * c8);
+          ln[k] = j < r1[i] ? lv : -INFINITY;
         }
 #pragma unroll
         for (int k = 0; k < kCoRound; ++k) {
@@ -241,6 +287,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void combine_out_proj_kernel(
           const floatx4 hi = __builtin_convertvector(__builtin_shufflevector(xr[k], xr[k], 4, 5, 6, 7), floatx4);
           acc0 += w * (empty ? floatx4{} : lo);
           acc1 += w * (empty ? floatx4{} : hi);
+        }
+#pragma unroll
+        for (int k = 0; k < kCoRound; ++k) {
+          lr[k] = ln[k];
+          xr[k] = xn[k];
         }
       }
     }
