@@ -493,7 +493,7 @@ __device__ __forceinline__ void settle(T& r) { asm volatile("" : "+v"(r)); }
 // Value of x in lane kLane of this lane's quad (lanes 4q .. 4q + 3), by DPP.
 template <int kLane>
 __device__ __forceinline__ float quad_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kLane * 0x55, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kLane * 0x55, 0xf, 0xf, false));
 }
 
 // 4 x 4 transpose within a quad: lane r (= r) of the quad returns
