@@ -203,6 +203,30 @@ def test_fused_merge_expand_matches_separate(H):
         assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_merge_with_no_split_rows(H):
+    """Split offsets that give no sequence any row (a caller's plan with no work
+    items): both merges write zeros and lse = -inf and read none of the partial
+    rows, which here hold NaNs and huge lse values."""
+    B = 40
+    cfg = api.config(H, 0, 0.07)
+    o_part = torch.full((1, H, 512), float("nan"), dtype=torch.float16, device=DEV)
+    lse_part = torch.full((1, H), 1e30, dtype=torch.float32, device=DEV)
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device=DEV)
+    w_uv = torch.randn(H, 128, 512, device=DEV).to(torch.bfloat16)
+    out = torch.full((B, H, 128), 1.0, dtype=torch.bfloat16, device=DEV)
+    o_lat = torch.full((B, H, 512), 1.0, dtype=torch.float32, device=DEV)
+    lse = torch.zeros(B, H, dtype=torch.float32, device=DEV)
+    api.decode_combine_out_proj(cfg, o_part, lse_part, offsets, w_uv, out, o_lat, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(o_lat == 0) and torch.all(torch.isneginf(lse))
+    o_lat.fill_(1.0)
+    lse.zero_()
+    api.decode_combine(cfg, o_part, lse_part, offsets, o_lat, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o_lat == 0) and torch.all(torch.isneginf(lse))
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_output_projection_with_wo(fused):
     """V2-Lite layer shapes: one sequence of 26 tokens, H=16, W_O to hidden 2048."""
