@@ -19,6 +19,12 @@ by itself, so append can be done token by token) are:
       q     = clamp(rint((x - mn) / scale), 0, 15);  scale == 0 -> q = 0
       dequant: q * scale + zero (float32, two roundings)
       byte j of a token holds element 2j in bits 0-3 and 2j+1 in bits 4-7.
+  INT4 symmetric (a variant the report does not measure; the analogue of the
+  INT8 reading with 4 bits), group of 32:
+      amax = max |x|, scale = amax / 7      (float32)
+      q = clamp(rint(x / scale), -7, 7);  amax == 0 -> scale 0, q 0
+      stored as the nibble q + 8 (1..15), same byte order as INT4
+      dequant: (nibble - 8) * scale (float32, one rounding)
 
 Every step is evaluated in numpy float32 with float32 constants, so the codes and
 scales are defined bit for bit; the GPU's quantise-on-append must reproduce them
@@ -31,13 +37,15 @@ Page layouts (64 tokens a page, bytes):
   int4 : [64][256] packed latent nibbles | [64][64] int8 RoPE-key codes
          | [64][16] f32 scales | [64][16] f32 zeros
          | [64][8] f32 RoPE-key scales                                 30,720
+  int4s: as int4 without the zeros                                    26,624
 
 Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
 INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
 unclamped element is at most half a step; zero groups round-trip exactly;
 the rounding rule is checked on hand-made ties; page bytes round-trip through
-unpack_page.  The page's own error figures need the real latents and are not
-reproduced ("parity unpinned" for those numbers).
+unpack_page; a symmetric INT4 group's absmax element maps to nibble 8 +- 7.  The
+page's own error figures need the real latents and are not reproduced ("parity
+unpinned" for those numbers).
 """
 from __future__ import annotations
 
@@ -49,9 +57,10 @@ D_R = 64
 G_C = 32      # latent channels per group
 G_R = 8       # RoPE-key channels per group
 
-CACHE_BF16, CACHE_INT8, CACHE_INT4 = 0, 1, 2
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM = 0, 1, 2, 3
 _F127 = np.float32(127.0)
 _F15 = np.float32(15.0)
+_F7 = np.float32(7.0)
 
 
 def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -105,6 +114,26 @@ def dequant_int4(q: np.ndarray, scale: np.ndarray, zero: np.ndarray, group: int 
     return (prod + zero[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
 
 
+def quant_int4_sym(x_bits: np.ndarray, group: int = G_C):
+    """Symmetric INT4 per group: returns nibbles uint8 [..., C] (q + 8, 1..15) and scale float32."""
+    x = _bf16_to_f32(x_bits)
+    shp = x.shape
+    xg = x.reshape(shp[:-1] + (shp[-1] // group, group))
+    amax = np.max(np.abs(xg), axis=-1)
+    scale = (amax / _F7).astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    q = np.rint((xg / safe[..., None]).astype(np.float32))
+    q = np.clip(q, -7, 7)
+    q = np.where(scale[..., None] == 0, 0, q)
+    return (q + 8).astype(np.uint8).reshape(shp), scale
+
+
+def dequant_int4_sym(nib: np.ndarray, scale: np.ndarray, group: int = G_C) -> np.ndarray:
+    shp = nib.shape
+    qg = (nib.astype(np.float32) - np.float32(8.0)).reshape(shp[:-1] + (shp[-1] // group, group))
+    return (qg * scale[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
+
+
 def pack_nibbles(q: np.ndarray) -> np.ndarray:
     """[..., 2n] values 0..15 -> [..., n] bytes: element 2j low nibble, 2j+1 high."""
     q = q.astype(np.uint8)
@@ -122,7 +151,8 @@ def token_bytes(dtype: int) -> int:
     """Cache bytes per token including scales and zero points."""
     return {CACHE_BF16: 576 * 2,
             CACHE_INT8: 576 + (D_C // G_C) * 4 + (D_R // G_R) * 4,
-            CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4}[dtype]
+            CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4,
+            CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4}[dtype]
 
 
 def page_bytes(dtype: int) -> int:
@@ -137,6 +167,9 @@ def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
     if dtype == CACHE_INT8:
         cc, cs = quant_int8_sym(c_bits, G_C)
         return {"codes": np.concatenate([cc, rc], axis=-1), "c_scale": cs, "r_scale": rs}
+    if dtype == CACHE_INT4_SYM:
+        q, s = quant_int4_sym(c_bits, G_C)
+        return {"nib": pack_nibbles(q), "r_codes": rc, "c_scale": s, "r_scale": rs}
     q, s, z = quant_int4_asym(c_bits, G_C)
     return {"nib": pack_nibbles(q), "r_codes": rc, "c_scale": s, "c_zero": z, "r_scale": rs}
 
@@ -163,7 +196,8 @@ def pack_page(dtype: int, fields: dict) -> np.ndarray:
         off = put(0, fields["nib"], 256)
         off = put(off, fields["r_codes"], 64)
         off = put(off, fields["c_scale"], 64)
-        off = put(off, fields["c_zero"], 64)
+        if dtype == CACHE_INT4:
+            off = put(off, fields["c_zero"], 64)
         put(off, fields["r_scale"], 32)
     return out
 
@@ -187,6 +221,9 @@ def unpack_page(dtype: int, page: np.ndarray) -> dict:
     nib, off = get(0, 256, np.uint8, 256)
     rc, off = get(off, 64, np.int8, 64)
     cs, off = get(off, 64, np.float32, 16)
+    if dtype == CACHE_INT4_SYM:
+        rs, _ = get(off, 32, np.float32, 8)
+        return {"nib": nib, "r_codes": rc, "c_scale": cs, "r_scale": rs}
     cz, off = get(off, 64, np.float32, 16)
     rs, _ = get(off, 32, np.float32, 8)
     return {"nib": nib, "r_codes": rc, "c_scale": cs, "c_zero": cz, "r_scale": rs}
@@ -201,7 +238,10 @@ def dequant_fields(dtype: int, f: dict):
         c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C)
         r = dequant_int8(f["codes"][..., D_C:], f["r_scale"], G_R)
         return c, r
-    c = dequant_int4(unpack_nibbles(f["nib"]), f["c_scale"], f["c_zero"], G_C)
+    if dtype == CACHE_INT4_SYM:
+        c = dequant_int4_sym(unpack_nibbles(f["nib"]), f["c_scale"], G_C)
+    else:
+        c = dequant_int4(unpack_nibbles(f["nib"]), f["c_scale"], f["c_zero"], G_C)
     r = dequant_int8(f["r_codes"], f["r_scale"], G_R)
     return c, r
 

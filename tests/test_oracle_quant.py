@@ -1,6 +1,7 @@
 """Pins of the quantiser oracle ([Report] "DeepSeek-V2-Lite MLA 吸收式 KV 缓存优化
 — 完整实验报告", §3.2 and §4.1: INT8 with 32-element blocks, asymmetric INT4 with
-32-element blocks, RoPE key INT8 with 8-element blocks).
+32-element blocks, RoPE key INT8 with 8-element blocks; plus a symmetric INT4
+variant the report does not measure).
 
 The page fixes the scheme, not the arithmetic; the oracle's reading is pinned
 by properties every correct implementation of that reading has: the extreme
@@ -90,6 +91,39 @@ def test_int4_constant_group_and_ties_to_even():
     assert list(q[0, 32:37]) == [0, 15, 2, 4, 0]
 
 
+def test_int4_sym_absmax_to_7_and_error_within_half_step():
+    """Symmetric INT4 (nibble = q + 8): a group's largest-magnitude element lands on
+    8 +- 7, every element is within half a step, and the nibble 8 means zero."""
+    rng = np.random.default_rng(4)
+    xb = _draw(rng, (300, 512))
+    nib, s = quant.quant_int4_sym(xb, 32)
+    x = bf16_bits_to_f32(xb).reshape(300, 16, 32)
+    ng = nib.reshape(300, 16, 32).astype(np.int32)
+    am = np.argmax(np.abs(x), axis=-1)
+    ext = np.take_along_axis(ng, am[..., None], -1)[..., 0]
+    sgn = np.sign(np.take_along_axis(x, am[..., None], -1)[..., 0]).astype(np.int32)
+    assert np.array_equal(ext, 8 + 7 * sgn)
+    assert ng.min() >= 1 and ng.max() <= 15
+    assert np.array_equal(s, (np.abs(x).max(-1) / np.float32(7)).astype(np.float32))
+    xh = quant.dequant_int4_sym(nib, s, 32).reshape(300, 16, 32).astype(np.float64)
+    bound = s[..., None].astype(np.float64) * 0.5 * (1 + 2 ** -20) + 2 * np.spacing(np.abs(x))
+    assert np.all(np.abs(xh - x) <= bound)
+
+
+def test_int4_sym_zero_group_and_ties_to_even():
+    x = np.zeros((1, 64), np.float32)                # group 0 all zero -> scale 0, nibbles 8
+    x[0, 32] = 7.0                                   # group 1: amax 7 -> scale exactly 1
+    x[0, 33] = 2.5
+    x[0, 34] = -3.5
+    x[0, 35] = 0.5
+    x[0, 36] = -7.0
+    nib, s = quant.quant_int4_sym(_bf16(x), 32)
+    assert s[0, 0] == 0 and np.all(nib[0, :32] == 8)
+    assert np.all(quant.dequant_int4_sym(nib, s, 32)[0, :32] == 0)
+    assert s[0, 1] == np.float32(1.0)
+    assert list(nib[0, 32:37].astype(int) - 8) == [7, 2, -4, 0, -7]
+
+
 def test_nibble_order_low_first():
     q = np.array([[1, 2, 15, 0]], np.uint8)
     b = quant.pack_nibbles(q)
@@ -102,10 +136,11 @@ def test_token_and_page_bytes():
     assert quant.token_bytes(quant.CACHE_BF16) == 1152
     assert quant.token_bytes(quant.CACHE_INT8) == 512 + 64 + 16 * 4 + 8 * 4 == 672
     assert quant.token_bytes(quant.CACHE_INT4) == 256 + 64 + 16 * 4 * 2 + 8 * 4 == 480
-    assert [quant.page_bytes(d) for d in (0, 1, 2)] == [73728, 43008, 30720]
+    assert quant.token_bytes(quant.CACHE_INT4_SYM) == 256 + 64 + 16 * 4 + 8 * 4 == 416
+    assert [quant.page_bytes(d) for d in (0, 1, 2, 3)] == [73728, 43008, 30720, 26624]
 
 
-@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
 def test_page_roundtrip(dtype):
     rng = np.random.default_rng(3 + dtype)
     c = _draw(rng, (50, 512))
@@ -125,7 +160,7 @@ def test_pool_dequant_matches_field_dequant():
     c = _draw(rng, (L, 512))
     r = _draw(rng, (L, 64))
     bt = np.array([5, 0, 3])
-    for dt in (0, 1, 2):
+    for dt in (0, 1, 2, 3):
         pool = quant.pack_pool(dt, 6, [(c, r, bt)])
         cc, rr = quant.dequant_pool_seq(dt, pool, bt, L)
         f = quant.encode_tokens(dt, c, r)
