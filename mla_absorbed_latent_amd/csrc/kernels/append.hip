@@ -12,6 +12,8 @@
 //   INT8: scale = amax / 127, code = clamp(rint(x / scale), -127, 127); amax 0 -> 0.
 //   INT4: zero = min, scale = (max - min) / 15, q = clamp(rint((x - min) / scale), 0, 15);
 //         scale 0 -> q 0; two codes a byte, element 2j in the low nibble.
+//   INT4 symmetric (a variant the report does not measure): scale = amax / 7,
+//         q = clamp(rint(x / scale), -7, 7), stored as the nibble q + 8; amax 0 -> 8.
 //
 // One thread per 16-byte chunk (bf16) or per quantisation group; slots outside
 // [0, num_pages * 64) are skipped.
@@ -25,6 +27,7 @@ namespace {
 constexpr int kPageBf16 = kBlock * kRowBytesBf16;        // 73,728
 constexpr int kPageInt8 = kBlock * 672;                  // 43,008
 constexpr int kPageInt4 = kBlock * 480;                  // 30,720
+constexpr int kPageInt4Sym = kBlock * 416;               // 26,624
 
 __device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_pages) {
   return slot >= 0 && slot < num_pages * kBlock;
@@ -147,6 +150,56 @@ __global__ __launch_bounds__(256) void append_int4(uint8_t* pool, int64_t num_pa
   }
 }
 
+// 24 groups a token: 16 symmetric INT4 latent groups of 32, then 8 INT8 RoPE-key groups.
+__global__ __launch_bounds__(256) void append_int4s(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                    const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tok = gid / 24;
+  const int grp = (int)(gid % 24);
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * kPageInt4Sym;
+  const int off = (int)(slot % kBlock);
+  // page regions: nibbles [64][256] | rope codes [64][64] | scales [64][16] | rope scales [64][8]
+  uint8_t* nib = page;
+  int8_t* rcodes = reinterpret_cast<int8_t*>(page + 64 * 256);
+  float* scales = reinterpret_cast<float*>(page + 64 * 256 + 64 * 64);
+  float* rscales = scales + 64 * 16;
+  if (grp < 16) {
+    const uint16_t* x = c_kv + tok * kDc + grp * 32;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_to_f32(x[i]);
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const float scale = __fdiv_rn(amax, 7.0f);
+    uint8_t bytes[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int q0 = 0, q1 = 0;
+      if (scale != 0.f) {
+        q0 = (int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * j], scale)), -7.f), 7.f);
+        q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * j + 1], scale)), -7.f), 7.f);
+      }
+      bytes[j] = (uint8_t)((q0 + 8) | ((q1 + 8) << 4));
+    }
+    uint8_t* dst = nib + off * 256 + grp * 16;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[j] = bytes[j];
+    scales[off * 16 + grp] = scale;
+  } else {
+    const int j = grp - 16;
+    int8_t codes[8];
+    const float s = quant_sym8<8>(k_pe + tok * kDr + j * 8, codes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rcodes[off * 64 + j * 8 + i] = codes[i];
+    rscales[off * 8 + j] = s;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
@@ -162,8 +215,10 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
     const dim3 grid((unsigned)((work + 255) / 256));
     if (cache_dtype == 1)
       hipLaunchKernelGGL(append_int8, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
-    else
+    else if (cache_dtype == 2)
       hipLaunchKernelGGL(append_int4, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+    else
+      hipLaunchKernelGGL(append_int4s, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
   }
   return hipGetLastError();
 }

@@ -309,15 +309,18 @@ struct LoaderInt8Reg {
 
 // INT4 page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32 scales
 //            | [64][16] f32 zeros | [64][8] f32 key scales.
-template <int kTok, int kSwz, int kTid0 = 0>
+// Symmetric INT4 (kSym) drops the zeros: a nibble holds q + 8 and decodes to
+// (nibble - 8) * scale.
+template <int kTok, int kSwz, int kTid0 = 0, bool kSym = false>
 struct LoaderInt4Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 2;    // its staging registers leave room for two
-  static constexpr int kPage = kBlock * 480;
+  static constexpr int kPage = kBlock * (kSym ? 416 : 480);
+  static constexpr int kKeyScales = kSym ? 64 * 16 : 2 * 64 * 16;   // float offset of the key scales after the scales
   uint32_t n[8 * kPass];     // 8 nibbles (latent chunk k) per dword
   u32x2 kc[kPass];           // 8 key codes (chunk 8)
   float s[9 * kPass];        // scale per chunk (k = 8: key scale)
-  float z[8 * kPass];        // zero point per latent chunk
+  float z[kSym ? 1 : 8 * kPass];   // zero point per latent chunk (asymmetric only)
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = ltid<kTid0>() >> 3, c8 = ltid<kTid0>() & 7;
@@ -328,27 +331,34 @@ struct LoaderInt4Reg {
       const uint8_t* pg = page_base(a, page, ok, kPage);
       const float* scales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + row * 16 + (c8 >> 2);
       const float* zeros = scales + 64 * 16;
-      const float* kscales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + 2 * 64 * 16 + row * 8 + c8;
+      const float* kscales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + kKeyScales + row * 8 + c8;
       const uint8_t* nib = pg + row * 256 + 4 * c8;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         n[8 * p + k] = *reinterpret_cast<const uint32_t*>(nib + 32 * k);
         s[9 * p + k] = scales[2 * k];
-        z[8 * p + k] = zeros[2 * k];
+        if constexpr (!kSym) z[8 * p + k] = zeros[2 * k];
       }
       kc[p] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
       s[9 * p + 8] = kscales[0];
     }
     return page >= 0;
   }
-  // Byte j of nibble word w (elements 2j, 2j+1) -> two fp16 values q * s + z.
+  // Byte j of nibble word w (elements 2j, 2j+1) -> two fp16 values q * s + z
+  // (symmetric: (q - 8) * s).
   static __device__ __forceinline__ uint32_t nib2(uint32_t w, int j, half2v s2, half2v z2) {
-    const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    constexpr float kBias = kSym ? -1032.0f : -1024.0f;
+    const half2v bias = {(_Float16)kBias, (_Float16)kBias};
     const uint32_t byte = (w >> (8 * j)) & 0xffu;
     // (element 2j, element 2j+1) = (low nibble, high nibble) as fp16 1024 + q
     const uint32_t h = 0x64006400u | (byte & 0xfu) | ((byte >> 4) << 16);
     const half2v qv = __builtin_bit_cast(half2v, h) + bias;
-    return __builtin_bit_cast(uint32_t, qv * s2 + z2);
+    if constexpr (kSym) return __builtin_bit_cast(uint32_t, qv * s2);
+    else return __builtin_bit_cast(uint32_t, qv * s2 + z2);
+  }
+  __device__ __forceinline__ _Float16 zero_h(int i) const {
+    if constexpr (kSym) return (_Float16)0.0f;
+    else return (_Float16)z[i];
   }
   // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's page
   // and row; load_step<I> (after store_step<I>) reloads chunk I / 2 once its
@@ -370,10 +380,10 @@ struct LoaderInt4Reg {
       if constexpr (k < 8) {
         n[k] = *reinterpret_cast<const uint32_t*>(pg + row * 256 + 4 * c8 + 32 * k);
         s[k] = meta[row * 16 + (c8 >> 2) + 2 * k];
-        z[k] = meta[64 * 16 + row * 16 + (c8 >> 2) + 2 * k];
+        if constexpr (!kSym) z[k] = meta[64 * 16 + row * 16 + (c8 >> 2) + 2 * k];
       } else {
         kc[0] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
-        s[8] = meta[2 * 64 * 16 + row * 8 + c8];
+        s[8] = meta[kKeyScales + row * 8 + c8];
       }
     }
   }
@@ -386,7 +396,7 @@ struct LoaderInt4Reg {
     constexpr int kcx = I / 2, p = kcx / 9, k = kcx % 9;
     u32x2 cur;
     if constexpr (k < 8) {
-      const _Float16 sh = (_Float16)s[9 * p + k], zh = (_Float16)z[8 * p + k];
+      const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k);
       const half2v s2 = {sh, sh}, z2 = {zh, zh};
       const uint32_t w = n[8 * p + k];
       constexpr int j0 = 2 * (I % 2);
@@ -410,7 +420,7 @@ struct LoaderInt4Reg {
     for (int p = 0; p < kPass; ++p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const _Float16 sh = (_Float16)s[9 * p + k], zh = (_Float16)z[8 * p + k];
+        const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k);
         const half2v s2 = {sh, sh}, z2 = {zh, zh};
         const uint32_t w = n[8 * p + k];
         u32x4 v;
@@ -447,14 +457,21 @@ __device__ __forceinline__ int wide_tok() {
 // Eight packed nibbles (byte b: element 2b in its low nibble, 2b + 1 in its high
 // one) -> eight fp16 values q * s + z, as four fp16 pairs.  Byte permutes place
 // each nibble under the constant 0x64 high byte (fp16 1024 + q, exactly).
+// Symmetric INT4 (kSym): (q - 8) * s, no zero point.
+template <bool kSym = false>
 __device__ __forceinline__ u32x4 nib8_to_f16(uint32_t w, half2v s2, half2v z2) {
   const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
   const uint32_t x0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // lo.b0 hi.b0 lo.b1 hi.b1
   const uint32_t x1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // lo.b2 hi.b2 lo.b3 hi.b3
   // Each pair is formed in a scalar: hipcc's __builtin_bit_cast of a vector
   // element (r[j]) reads element 0 whatever the index.
-  const half2v bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  auto cv = [&](uint32_t h) { return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h) + bias) * s2 + z2); };
+  constexpr float kBias = kSym ? -1032.0f : -1024.0f;
+  const half2v bias = {(_Float16)kBias, (_Float16)kBias};
+  auto cv = [&](uint32_t h) {
+    const half2v q = __builtin_bit_cast(half2v, h) + bias;
+    if constexpr (kSym) return __builtin_bit_cast(uint32_t, q * s2);
+    else return __builtin_bit_cast(uint32_t, q * s2 + z2);
+  };
   return u32x4{cv(__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)), cv(__builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)),
                cv(__builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)), cv(__builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u))};
 }
@@ -647,10 +664,11 @@ struct LoaderInt8Wide {
 // Threads c4 >= 2 write their chunks in the order j ^ 2, so that the four
 // threads of a token write four different LDS bank groups at every store.  The
 // key piece (16 codes at 16 c4) goes to chunks 2 c4, 2 c4 + 1 of group 8.
-template <int kSwz, int kTid0>
+template <int kSwz, int kTid0, bool kSym = false>
 struct LoaderInt4Wide {
-  static constexpr int kLoads = 8;       // load instructions per tile
-  static constexpr int kPage = kBlock * 480;
+  static constexpr int kLoads = kSym ? 7 : 8;   // load instructions per tile
+  static constexpr int kPage = kBlock * (kSym ? 416 : 480);
+  static constexpr int kKeyScales = kSym ? 64 * 64 : 2 * 64 * 64;   // byte offset of the key scales after the scales
   u32x4 n[4] = {};
   floatx4 sq = {}, zq = {};  // scales / zeros 4 c4 .. 4 c4 + 3 of the token (transposed in commit)
   u32x4 kc = {};
@@ -669,15 +687,15 @@ struct LoaderInt4Wide {
     asm_ld16_nt<0>(kc, pg + 64 * 256 + row * 64 + 16 * c4);
     const uint8_t* meta = pg + 64 * 256 + 64 * 64;
     asm_ld16<0>(sq, meta + row * 64 + 16 * c4);
-    asm_ld16<0>(zq, meta + 64 * 64 + row * 64 + 16 * c4);
-    asm_ld8<0>(ks, meta + 2 * 64 * 64 + row * 32 + 8 * c4);
+    if constexpr (!kSym) asm_ld16<0>(zq, meta + 64 * 64 + row * 64 + 16 * c4);
+    asm_ld8<0>(ks, meta + kKeyScales + row * 32 + 8 * c4);
     return page >= 0;
   }
   __device__ __forceinline__ void settle_all() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) settle(n[i]);
     settle(sq);
-    settle(zq);
+    if constexpr (!kSym) settle(zq);
     settle(kc);
     settle(ks);
   }
@@ -693,14 +711,16 @@ struct LoaderInt4Wide {
     for (int j = 0; j < 4; ++j) dst[j] = lds_buf + swz<kSwz>(tok, 4 * (c4 & 1) + (j ^ (swap ? 2 : 0))) + 128 * (c4 >> 1);
     // Block c4 + 4 i's scale is component c4 of quad lane i's sq: a 4 x 4
     // transpose within the quad.
-    const floatx4 st = quad_transpose(sq, c4), zt = quad_transpose(zq, c4);
+    const floatx4 st = quad_transpose(sq, c4);
+    floatx4 zt = floatx4{};
+    if constexpr (!kSym) zt = quad_transpose(zq, c4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const _Float16 sh = (_Float16)st[i], zh = (_Float16)zt[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = (n[i][j] & ~blend) | (n[i][j ^ 2] & blend);
-        *reinterpret_cast<u32x4*>(dst[j] + 256 * i) = nib8_to_f16(w, half2v{sh, sh}, half2v{zh, zh});
+        *reinterpret_cast<u32x4*>(dst[j] + 256 * i) = nib8_to_f16<kSym>(w, half2v{sh, sh}, half2v{zh, zh});
       }
     }
     const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
@@ -1033,7 +1053,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   using Loader = typename std::conditional<
       kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
       typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128, kSwz128>,
-                                LoaderInt4Reg<kTile128, kSwz128>>::type>::type;
+                                LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3>>::type>::type;
   h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
                          overflow);
   if (__syncthreads_or(overflow)) {
@@ -1049,7 +1069,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   }
 
   // ---- per-head sums from the owning waves, then normalise and write ----
-  if constexpr (kCache == 2) {
+  if constexpr (kCache >= 2) {
     // INT4: o_part is stored straight from the accumulator layout (16-byte row
     // pieces): with the transposed write below, this kernel spills in its tile loop.
     const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
@@ -1395,6 +1415,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 using H16Bf16 = LoaderBf16Wide<kSwz16, 256>;   // the staging waves are threads 256..511
 using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
 using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
+using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
@@ -1403,12 +1424,14 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     if (cache_dtype == 0) hipLaunchKernelGGL(decode_h128<0>, grid, block, 0, stream, a);
     else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h128<1>, grid, block, 0, stream, a);
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
+    else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h128<3>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
     const dim3 block16(512);                       // 4 compute + 4 staging waves
     if (cache_dtype == 0) hipLaunchKernelGGL(decode_h16<H16Bf16>, grid, block16, 0, stream, a);
     else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<H16Int8>, grid, block16, 0, stream, a);
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h16<H16Int4Sym>, grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
