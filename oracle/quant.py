@@ -19,6 +19,8 @@ by itself, so append can be done token by token) are:
       q     = clamp(rint((x - mn) / scale), 0, 15);  scale == 0 -> q = 0
       dequant: q * scale + zero (float32, two roundings)
       byte j of a token holds element 2j in bits 0-3 and 2j+1 in bits 4-7.
+  INT8 per token (a variant the report does not measure): the INT8 reading
+  with one group of all 512 latent channels; the RoPE key as for INT8.
   INT4 symmetric (a variant the report does not measure; the analogue of the
   INT8 reading with 4 bits), group of 32:
       amax = max |x|, scale = amax / 7      (float32)
@@ -38,6 +40,8 @@ Page layouts (64 tokens a page, bytes):
          | [64][16] f32 scales | [64][16] f32 zeros
          | [64][8] f32 RoPE-key scales                                 30,720
   int4s: as int4 without the zeros                                    26,624
+  int8t: [64][576] int8 codes | [64] f32 latent scales
+         | [64][8] f32 RoPE-key scales                                 39,168
 
 Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
 INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
@@ -57,7 +61,7 @@ D_R = 64
 G_C = 32      # latent channels per group
 G_R = 8       # RoPE-key channels per group
 
-CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM = 0, 1, 2, 3
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK = 0, 1, 2, 3, 4
 _F127 = np.float32(127.0)
 _F15 = np.float32(15.0)
 _F7 = np.float32(7.0)
@@ -152,7 +156,8 @@ def token_bytes(dtype: int) -> int:
     return {CACHE_BF16: 576 * 2,
             CACHE_INT8: 576 + (D_C // G_C) * 4 + (D_R // G_R) * 4,
             CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4,
-            CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4}[dtype]
+            CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4,
+            CACHE_INT8_TOK: 576 + 4 + (D_R // G_R) * 4}[dtype]
 
 
 def page_bytes(dtype: int) -> int:
@@ -164,8 +169,8 @@ def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
     if dtype == CACHE_BF16:
         return {"rows": np.concatenate([c_bits, r_bits], axis=-1).astype(np.uint16)}
     rc, rs = quant_int8_sym(r_bits, G_R)
-    if dtype == CACHE_INT8:
-        cc, cs = quant_int8_sym(c_bits, G_C)
+    if dtype in (CACHE_INT8, CACHE_INT8_TOK):
+        cc, cs = quant_int8_sym(c_bits, G_C if dtype == CACHE_INT8 else D_C)
         return {"codes": np.concatenate([cc, rc], axis=-1), "c_scale": cs, "r_scale": rs}
     if dtype == CACHE_INT4_SYM:
         q, s = quant_int4_sym(c_bits, G_C)
@@ -188,9 +193,9 @@ def pack_page(dtype: int, fields: dict) -> np.ndarray:
 
     if dtype == CACHE_BF16:
         put(0, fields["rows"], 1152)
-    elif dtype == CACHE_INT8:
+    elif dtype in (CACHE_INT8, CACHE_INT8_TOK):
         off = put(0, fields["codes"], 576)
-        off = put(off, fields["c_scale"], 64)
+        off = put(off, fields["c_scale"], 64 if dtype == CACHE_INT8 else 4)
         put(off, fields["r_scale"], 32)
     else:
         off = put(0, fields["nib"], 256)
@@ -213,9 +218,9 @@ def unpack_page(dtype: int, page: np.ndarray) -> dict:
     if dtype == CACHE_BF16:
         rows, _ = get(0, 1152, np.uint16, 576)
         return {"rows": rows}
-    if dtype == CACHE_INT8:
+    if dtype in (CACHE_INT8, CACHE_INT8_TOK):
         codes, off = get(0, 576, np.int8, 576)
-        cs, off = get(off, 64, np.float32, 16)
+        cs, off = get(off, 64, np.float32, 16) if dtype == CACHE_INT8 else get(off, 4, np.float32, 1)
         rs, _ = get(off, 32, np.float32, 8)
         return {"codes": codes, "c_scale": cs, "r_scale": rs}
     nib, off = get(0, 256, np.uint8, 256)
@@ -234,8 +239,8 @@ def dequant_fields(dtype: int, f: dict):
     if dtype == CACHE_BF16:
         rows = _bf16_to_f32(f["rows"])
         return rows[..., :D_C], rows[..., D_C:]
-    if dtype == CACHE_INT8:
-        c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C)
+    if dtype in (CACHE_INT8, CACHE_INT8_TOK):
+        c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C if dtype == CACHE_INT8 else D_C)
         r = dequant_int8(f["codes"][..., D_C:], f["r_scale"], G_R)
         return c, r
     if dtype == CACHE_INT4_SYM:

@@ -27,10 +27,11 @@ def _draw(rng, shape, outliers=True):
     return _bf16(x)
 
 
-@pytest.mark.parametrize("group", [32, 8])
+@pytest.mark.parametrize("group", [32, 8, 512])
 def test_int8_extreme_element_hits_127_and_error_within_half_step(group):
+    """Group 512 is the per-token INT8 variant (one scale for the whole latent)."""
     rng = np.random.default_rng(1)
-    xb = _draw(rng, (300, 512 if group == 32 else 64))
+    xb = _draw(rng, (300, 64 if group == 8 else 512))
     codes, scales = quant.quant_int8_sym(xb, group)
     x = bf16_bits_to_f32(xb).reshape(300, -1, group)
     cg = codes.reshape(300, -1, group).astype(np.int32)
@@ -137,10 +138,24 @@ def test_token_and_page_bytes():
     assert quant.token_bytes(quant.CACHE_INT8) == 512 + 64 + 16 * 4 + 8 * 4 == 672
     assert quant.token_bytes(quant.CACHE_INT4) == 256 + 64 + 16 * 4 * 2 + 8 * 4 == 480
     assert quant.token_bytes(quant.CACHE_INT4_SYM) == 256 + 64 + 16 * 4 + 8 * 4 == 416
-    assert [quant.page_bytes(d) for d in (0, 1, 2, 3)] == [73728, 43008, 30720, 26624]
+    assert quant.token_bytes(quant.CACHE_INT8_TOK) == 512 + 64 + 4 + 8 * 4 == 612
+    assert [quant.page_bytes(d) for d in (0, 1, 2, 3, 4)] == [73728, 43008, 30720, 26624, 39168]
 
 
-@pytest.mark.parametrize("dtype", [0, 1, 2, 3])
+def test_int8_per_token_one_scale_for_the_latent():
+    """Per-token INT8: the latent's single scale is max|x| over all 512 channels / 127
+    and the RoPE key keeps its 8-element groups."""
+    rng = np.random.default_rng(5)
+    c, r = _draw(rng, (20, 512)), _draw(rng, (20, 64))
+    f = quant.encode_tokens(quant.CACHE_INT8_TOK, c, r)
+    x = bf16_bits_to_f32(c)
+    assert f["c_scale"].shape == (20, 1)
+    assert np.array_equal(f["c_scale"][:, 0], (np.abs(x).max(-1) / np.float32(127)).astype(np.float32))
+    assert np.array_equal(f["r_scale"], quant.quant_int8_sym(r, 8)[1])
+    assert np.all(np.abs(f["codes"][:, :512]).max(-1) == 127)
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4])
 def test_page_roundtrip(dtype):
     rng = np.random.default_rng(3 + dtype)
     c = _draw(rng, (50, 512))
@@ -160,7 +175,7 @@ def test_pool_dequant_matches_field_dequant():
     c = _draw(rng, (L, 512))
     r = _draw(rng, (L, 64))
     bt = np.array([5, 0, 3])
-    for dt in (0, 1, 2, 3):
+    for dt in (0, 1, 2, 3, 4):
         pool = quant.pack_pool(dt, 6, [(c, r, bt)])
         cc, rr = quant.dequant_pool_seq(dt, pool, bt, L)
         f = quant.encode_tokens(dt, c, r)
