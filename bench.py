@@ -38,7 +38,7 @@ WORKLOADS = {
     "v3_ragged": ("v3_ragged", "V3-shaped ragged decode: H=128, B=128, log-uniform lengths in [128, 65536]"),
     "v2lite_quant": ("v2lite_quant", "quantised latent cache, V2-Lite shapes: H=16, B=64, 16384 tokens/seq"),
 }
-DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3}
+DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3, "int8t": 4}
 
 
 def log(msg):
@@ -269,7 +269,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f16", 1: "i8/f16", 2: "i4/f16", 3: "i4s/f16"}[cache_dtype],
+        "dtype": {0: "f16", 1: "i8/f16", 2: "i4/f16", 3: "i4s/f16", 4: "i8t/f16"}[cache_dtype],
         "data": "synthetic (seeded; shapes and distributions of the workload, no checkpoint)",
         "config": {"workload": args.workload, "description": desc, "batch": case.B, "heads": case.H,
                    "cached_tokens": case.total_tokens, "cache_dtype": args.cache_dtype,

@@ -54,13 +54,14 @@ typedef enum {
   MLA_ERR_HIP = 7          /* a HIP call or launch failed                         */
 } mla_status;
 
-/* Latent-cache formats ([Report] §3.2 and §4.1; the symmetric INT4 variant is
- * not one the report measures). */
+/* Latent-cache formats ([Report] §3.2 and §4.1; the symmetric INT4 and the
+ * per-token INT8 variants are not ones the report measures). */
 typedef enum {
   MLA_CACHE_BF16 = 0,     /* c_kv and k_pe in bf16                                       */
   MLA_CACHE_INT8 = 1,     /* c_kv INT8, one fp32 scale per 32 channels; k_pe INT8 per 8   */
   MLA_CACHE_INT4 = 2,     /* c_kv asymmetric INT4, fp32 scale + zero per 32; k_pe INT8    */
-  MLA_CACHE_INT4_SYM = 3  /* c_kv symmetric INT4, fp32 scale per 32; k_pe INT8            */
+  MLA_CACHE_INT4_SYM = 3, /* c_kv symmetric INT4, fp32 scale per 32; k_pe INT8            */
+  MLA_CACHE_INT8_TOK = 4  /* c_kv INT8, one fp32 scale per token; k_pe INT8 per 8         */
 } mla_cache_dtype;
 
 /* Shape of one MLA layer.  Supported: num_heads in {16, 128}, qk_nope_dim = 128,
@@ -92,7 +93,7 @@ typedef struct {
  * Pure host functions; they return 0 for an invalid config.
  * Bytes per token include every scale and zero point the decode reads:
  *   bf16 1,152 ([Audit] §2.4: 576 elements x 2 B), INT8 672, INT4 480,
- *   symmetric INT4 416.
+ *   symmetric INT4 416, per-token INT8 612.
  * Page layouts (64 tokens, row = token):
  *   bf16: [64][576] bf16, latent in 0..511 then RoPE key in 512..575  (73,728 B)
  *   INT8: [64][576] int8 codes | [64][16] f32 latent scales
@@ -102,6 +103,8 @@ typedef struct {
  *         | [64][16] f32 zeros | [64][8] f32 RoPE-key scales          (30,720 B)
  *   INT4_SYM: as INT4 without the zeros; a nibble holds q + 8, q in -7..7
  *                                                                     (26,624 B)
+ *   INT8_TOK: [64][576] int8 codes | [64] f32 latent scales
+ *         | [64][8] f32 RoPE-key scales                               (39,168 B)
  * A pool of N pages is N * mla_cache_page_bytes() contiguous bytes.          */
 mla_status mla_config_check(const mla_config* cfg);
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
@@ -123,6 +126,7 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
  *   -127, 127) (round half to even); max|x| = 0 gives scale 0 and codes 0.
  * INT4: per group of 32 latent channels, zero = min, scale = (max-min)/15,
  *   q = clamp(rint((x-min)/scale), 0, 15); scale 0 gives q = 0.
+ * INT8_TOK: as INT8 with one group of all 512 latent channels.
  * INT4_SYM: per group of 32 latent channels, scale = max|x| / 7,
  *   q = clamp(rint(x/scale), -7, 7), stored as q + 8; max|x| = 0 gives scale 0
  *   and q = 0.  The RoPE key of both INT4 formats is INT8 as above.

@@ -12,6 +12,8 @@
 //   INT8: scale = amax / 127, code = clamp(rint(x / scale), -127, 127); amax 0 -> 0.
 //   INT4: zero = min, scale = (max - min) / 15, q = clamp(rint((x - min) / scale), 0, 15);
 //         scale 0 -> q 0; two codes a byte, element 2j in the low nibble.
+//   INT8 per token (a variant the report does not measure): the INT8 rule with one
+//         group of all 512 latent channels; RoPE key as INT8.
 //   INT4 symmetric (a variant the report does not measure): scale = amax / 7,
 //         q = clamp(rint(x / scale), -7, 7), stored as the nibble q + 8; amax 0 -> 8.
 //
@@ -28,6 +30,7 @@ constexpr int kPageBf16 = kBlock * kRowBytesBf16;        // 73,728
 constexpr int kPageInt8 = kBlock * 672;                  // 43,008
 constexpr int kPageInt4 = kBlock * 480;                  // 30,720
 constexpr int kPageInt4Sym = kBlock * 416;               // 26,624
+constexpr int kPageInt8Tok = kBlock * 612;               // 39,168
 
 __device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_pages) {
   return slot >= 0 && slot < num_pages * kBlock;
@@ -200,6 +203,50 @@ __global__ __launch_bounds__(256) void append_int4s(uint8_t* pool, int64_t num_p
   }
 }
 
+// One wave a token: lane l quantises latent channels 8 l .. 8 l + 7 against the
+// token's maximum (a wave reduction: the maximum is exact in any order); lanes
+// 0-7 also quantise RoPE-key group l.
+__global__ __launch_bounds__(256) void append_int8t(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                    const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // uniform per wave
+  const int lane = threadIdx.x & 63;
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * kPageInt8Tok;
+  const int off = (int)(slot % kBlock);
+  const uint16_t* x = c_kv + tok * kDc + 8 * lane;
+  float v[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = bf16_to_f32(x[i]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const float scale = __fdiv_rn(amax, 127.0f);
+  int8_t codes[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q = 0.f;
+    if (scale != 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(v[i], scale)), -127.f), 127.f);
+    codes[i] = (int8_t)(int)q;
+  }
+  int8_t* dst = reinterpret_cast<int8_t*>(page + off * 576 + 8 * lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = codes[i];
+  if (lane == 0) reinterpret_cast<float*>(page + 64 * 576)[off] = scale;
+  if (lane < 8) {
+    int8_t rc[8];
+    const float s = quant_sym8<8>(k_pe + tok * kDr + lane * 8, rc);
+    int8_t* rdst = reinterpret_cast<int8_t*>(page + off * 576 + 512 + lane * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rdst[i] = rc[i];
+    reinterpret_cast<float*>(page + 64 * 576 + 64 * 4)[off * 8 + lane] = s;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
@@ -209,6 +256,10 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
   if (cache_dtype == 0) {
     const int64_t work = (int64_t)n * 72;
     hipLaunchKernelGGL(append_bf16, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
+                       c_kv, k_pe, slots, n);
+  } else if (cache_dtype == 4) {
+    const int64_t work = (int64_t)n * 64;                  // one wave a token
+    hipLaunchKernelGGL(append_int8t, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
                        c_kv, k_pe, slots, n);
   } else {
     const int64_t work = (int64_t)n * 24;

@@ -228,13 +228,20 @@ __device__ __forceinline__ u32x2 int8x4_to_f16_perm(uint32_t c, half2v s) {
 }
 
 // INT8 page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key scales.
-template <int kTok, int kSwz, int kTid0 = 0>
+// Per-token INT8 (kTok1): [64][576] codes | [64] f32 latent scales | [64][8] f32
+// key scales; every latent chunk of a token takes the token's one scale.
+template <int kTok, int kSwz, int kTid0 = 0, bool kTok1 = false>
 struct LoaderInt8Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 3;
-  static constexpr int kPage = kBlock * 672;
+  static constexpr int kPage = kBlock * (kTok1 ? 612 : 672);
+  static constexpr int kKeyScales = 64 * 576 + (kTok1 ? 64 * 4 : 64 * 64);   // byte offset of the key scales
   u32x2 c[9 * kPass];
   float s[9 * kPass];
+  // Float index of latent chunk k's scale for (row, c8).
+  static __device__ __forceinline__ int scale_index(int row, int c8, int k) {
+    return kTok1 ? row : row * 16 + (c8 >> 2) + 2 * k;
+  }
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
     const int tok = ltid<kTid0>() >> 3, c8 = ltid<kTid0>() & 7;
@@ -244,12 +251,12 @@ struct LoaderInt8Reg {
       const int row = (t0 % kBlock) + 32 * p + tok;
       const uint8_t* pg = page_base(a, page, ok, kPage);
       const uint8_t* codes = pg + row * 576 + 8 * c8;
-      const float* cs = reinterpret_cast<const float*>(pg + 64 * 576) + row * 16 + (c8 >> 2);
-      const float* ks = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64) + row * 8 + c8;
+      const float* cs = reinterpret_cast<const float*>(pg + 64 * 576);
+      const float* ks = reinterpret_cast<const float*>(pg + kKeyScales) + row * 8 + c8;
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         c[9 * p + k] = *reinterpret_cast<const u32x2*>(codes + 64 * k);
-        s[9 * p + k] = k < 8 ? cs[2 * k] : ks[0];
+        s[9 * p + k] = k < 8 ? cs[scale_index(row, c8, k)] : ks[0];
       }
     }
     return page >= 0;
@@ -271,8 +278,8 @@ struct LoaderInt8Reg {
       constexpr int k = I / 2;
       const int c8 = ltid<kTid0>() & 7;
       c[k] = *reinterpret_cast<const u32x2*>(pg + row * 576 + 8 * c8 + 64 * k);
-      if constexpr (k < 8) s[k] = reinterpret_cast<const float*>(pg + 64 * 576)[row * 16 + (c8 >> 2) + 2 * k];
-      else s[k] = reinterpret_cast<const float*>(pg + 64 * 576 + 64 * 64)[row * 8 + c8];
+      if constexpr (k < 8) s[k] = reinterpret_cast<const float*>(pg + 64 * 576)[scale_index(row, c8, k)];
+      else s[k] = reinterpret_cast<const float*>(pg + kKeyScales)[row * 8 + c8];
     }
   }
   // Stepwise commit: step 2c dequantises the first four codes of chunk c, step
@@ -586,12 +593,16 @@ struct LoaderBf16Wide {
 // group i.  The four threads of a token (one quad of lanes) load its 16 latent
 // scales as four 16-byte pieces and pass them round by DPP: one load instead of
 // eight 4-byte ones, since load instructions, not bytes, pace the staging.
-template <int kSwz, int kTid0>
+// Per-token INT8 (kTok1): the token's one latent scale is a single 4-byte load
+// (every thread of the token loads it), no DPP.
+template <int kSwz, int kTid0, bool kTok1 = false>
 struct LoaderInt8Wide {
-  static constexpr int kPage = kBlock * 672;
+  static constexpr int kPage = kBlock * (kTok1 ? 612 : 672);
   static constexpr int kLoads = 11;      // load instructions per tile
+  static constexpr int kKeyScales = 64 * 576 + (kTok1 ? 64 * 4 : 64 * 64);   // byte offset of the key scales
   u32x4 c[9] = {};
   floatx4 sv = {};           // latent scales 4 c4 .. 4 c4 + 3 of the token
+  float st = 0.f;            // per token: the token's latent scale
   floatx2 ks = {};
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
@@ -609,19 +620,22 @@ struct LoaderInt8Wide {
     asm_ld16_nt<384>(c[6], codes);
     asm_ld16_nt<448>(c[7], codes);
     asm_ld16_nt<512>(c[8], codes);
-    asm_ld16<0>(sv, pg + 64 * 576 + row * 64 + 16 * c4);
-    asm_ld8<0>(ks, pg + 64 * 576 + 64 * 64 + row * 32 + 8 * c4);
+    if constexpr (kTok1) asm_ld4<0>(st, pg + 64 * 576 + row * 4);
+    else asm_ld16<0>(sv, pg + 64 * 576 + row * 64 + 16 * c4);
+    asm_ld8<0>(ks, pg + kKeyScales + row * 32 + 8 * c4);
     return page >= 0;
   }
   __device__ __forceinline__ void settle_all() {
 #pragma unroll
     for (int i = 0; i < 9; ++i) settle(c[i]);
-    settle(sv);
+    if constexpr (kTok1) settle(st);
+    else settle(sv);
     settle(ks);
   }
   // Scale of piece i < 8, block b = c4 / 2 + 2 i: component b % 4 of quad lane b / 4 = i / 2.
   template <int I>
   __device__ __forceinline__ float scale(bool upper) const {
+    if constexpr (kTok1) return st;
     const float lo = quad_bcast<I / 2>(sv[2 * (I % 2)]), hi = quad_bcast<I / 2>(sv[2 * (I % 2) + 1]);
     return upper ? hi : lo;
   }
@@ -1052,7 +1066,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
 
   using Loader = typename std::conditional<
       kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
-      typename std::conditional<kCache == 1, LoaderInt8Reg<kTile128, kSwz128>,
+      typename std::conditional<kCache == 1 || kCache == 4, LoaderInt8Reg<kTile128, kSwz128, 0, kCache == 4>,
                                 LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3>>::type>::type;
   h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
                          overflow);
@@ -1069,7 +1083,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   }
 
   // ---- per-head sums from the owning waves, then normalise and write ----
-  if constexpr (kCache >= 2) {
+  if constexpr (kCache == 2 || kCache == 3) {
     // INT4: o_part is stored straight from the accumulator layout (16-byte row
     // pieces): with the transposed write below, this kernel spills in its tile loop.
     const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
@@ -1416,6 +1430,7 @@ using H16Bf16 = LoaderBf16Wide<kSwz16, 256>;   // the staging waves are threads 
 using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
 using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
 using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
+using H16Int8Tok = LoaderInt8Wide<kSwz16, 256, true>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
@@ -1425,6 +1440,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h128<1>, grid, block, 0, stream, a);
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h128<3>, grid, block, 0, stream, a);
+    else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h128<4>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
     const dim3 block16(512);                       // 4 compute + 4 staging waves
@@ -1432,6 +1448,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h16<H16Int8>, grid, block16, 0, stream, a);
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block16, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h16<H16Int4Sym>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h16<H16Int8Tok>, grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
