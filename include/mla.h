@@ -246,6 +246,43 @@ mla_status mla_decode_combine_out_proj(const mla_config* cfg, const uint16_t* o_
                                        float* o_lat, float* lse, const uint16_t* w_o, int32_t hidden,
                                        uint16_t* y, float* out_f32, int32_t batch, hipStream_t stream);
 
+/* ------------------------------------------------------------------ layer front
+ * mla_layer_front: the projections that produce the hot path's inputs from a
+ * layer's hidden states, V2-Lite form ([Report] §1.1: the joint down projection
+ * yields the 512-wide latent and the 64-wide RoPE key; [Audit] §3.3: one query
+ * projection, and the down projection's output puts the latent first;
+ * [Tutorial] §三: the latent is RMS-normalised before caching, the RoPE key and
+ * the query's RoPE part are rotated by position):
+ *   q[t]   = W_q . x[t]                         (H x (128 + 64), head-major)
+ *   kv[t]  = W_DKV . x[t]                       (512 + 64)
+ *   c_kv[t] = kv[t][0:512] / sqrt(mean(kv[t][0:512]^2) + rms_eps)  (unit gain)
+ *   k_pe[t] = RoPE(kv[t][512:576], positions[t])
+ *   q_nope[t][h] = q[t][h][0:128],  q_pe[t][h] = RoPE(q[t][h][128:192], positions[t])
+ * RoPE rotates the pairs (v[2i], v[2i+1]) by positions[t] * rope_base^(-2i/64).
+ * Projections accumulate bf16 products in fp32; the norm and the rotation run
+ * in double precision; each output is rounded once to bf16 (round to nearest
+ * even).
+ *   x          device [n_tokens][hidden] bf16; hidden a positive multiple of 8
+ *   w_q        device [H*192][hidden] bf16
+ *   w_dkv      device [576][hidden] bf16
+ *   positions  device [n_tokens] int32 (any value: used only as an angle)
+ *   rms_eps    > 0;  rope_base > 1 (finite)
+ *   workspace  device f32, >= mla_layer_front_workspace_bytes(cfg, n_tokens)
+ *              bytes (given as workspace_bytes; MLA_ERR_WORKSPACE if smaller)
+ *   q_nope     device [n_tokens][H][128] bf16, written
+ *   q_pe       device [n_tokens][H][64] bf16, written
+ *   c_kv       device [n_tokens][512] bf16, written
+ *   k_pe       device [n_tokens][64] bf16, written
+ * c_kv and k_pe are what mla_cache_append takes; q_nope and q_pe what
+ * mla_absorb_q takes.  n_tokens == 0 is a no-op; n_tokens < 0 is
+ * MLA_ERR_VALUE.  The library's output is independent of cfg->cache_dtype.  */
+mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
+                           const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                           float* workspace, size_t workspace_bytes, uint16_t* q_nope, uint16_t* q_pe,
+                           uint16_t* c_kv, uint16_t* k_pe, int32_t n_tokens, hipStream_t stream);
+/* n_tokens * (576 + H * 192) * 4 bytes: the fp32 projection results.        */
+size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
+
 /* ------------------------------------------------------------------ errors */
 const char* mla_status_string(mla_status s);
 int32_t mla_last_hip_error(void);

@@ -198,3 +198,27 @@ def out_proj(cfg: Config, o_lat, w_uv, out, w_o=None, y=None, out_f32=None) -> N
     _check(L.load().mla_out_proj(C.byref(cfg), _dev(o_lat, "o_lat"), _dev(w_uv, "w_uv"), _dev(out, "out"),
                                  _dev(w_o, "w_o"), hidden, _dev(y, "y"), _dev(out_f32, "out_f32"), B, _stream()),
            "mla_out_proj")
+
+
+def layer_front_workspace_bytes(cfg: Config, n_tokens: int) -> int:
+    return int(L.load().mla_layer_front_workspace_bytes(C.byref(cfg), int(n_tokens)))
+
+
+def layer_front(cfg: Config, x, w_q, w_dkv, positions, workspace, q_nope, q_pe, c_kv, k_pe,
+                rms_eps: float = 1e-6, rope_base: float = 10000.0) -> None:
+    """Hidden states -> (q_nope, q_pe, c_kv, k_pe), bf16 (mla_layer_front)."""
+    T, hidden, H = int(x.shape[0]), int(x.shape[1]), cfg.num_heads
+    _need(x, "x", (T, hidden), 2)
+    _need(w_q, "w_q", (H * 192, hidden), 2)
+    _need(w_dkv, "w_dkv", (576, hidden), 2)
+    _need(positions, "positions", (T,), 4)
+    _need(q_nope, "q_nope", (T, H, 128), 2)
+    _need(q_pe, "q_pe", (T, H, 64), 2)
+    _need(c_kv, "c_kv", (T, 512), 2)
+    _need(k_pe, "k_pe", (T, 64), 2)
+    ws_bytes = int(workspace.numel()) * int(workspace.element_size())
+    _check(L.load().mla_layer_front(C.byref(cfg), _dev(x, "x"), hidden, _dev(w_q, "w_q"), _dev(w_dkv, "w_dkv"),
+                                    _dev(positions, "positions"), float(rms_eps), float(rope_base),
+                                    _dev(workspace, "workspace"), ws_bytes, _dev(q_nope, "q_nope"),
+                                    _dev(q_pe, "q_pe"), _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"), T, _stream()),
+           "mla_layer_front")

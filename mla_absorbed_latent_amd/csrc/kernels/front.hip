@@ -1,0 +1,127 @@
+// front.hip -- the layer front that produces the hot path's inputs from a
+// layer's hidden states (V2-Lite shapes):
+//   * one query projection and one joint down projection whose output puts the
+//     512-wide latent first, then the 64-wide RoPE key
+//     ("DeepSeek-V2-Lite MLA 吸收式 KV 缓存优化 — 完整实验报告" §1.1;
+//      "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界" §3.3);
+//   * the latent is RMS-normalised before it is cached, the RoPE key and the
+//     query's RoPE part are rotated by position
+//     ("手搓 MLA:从 MHA 到 weight absorption,看懂 DeepSeek 的 KV 压缩" §三).
+// Readings where the pages are silent: RMSNorm with unit gain; RoPE on
+// interleaved pairs (x[2i], x[2i+1]) rotated by pos * base^(-2i/64); every
+// output rounded once to bf16.
+//
+// Two kernels: rowdot (y[t][n] = sum_k W[n][k] x[t][k], bf16 in, fp32 sums;
+// weight-read-bound at the few tokens of a prefill or decode step, so it runs
+// on the vector ALUs with one wave per output feature), then front_finish (norm,
+// rotation, bf16 rounding; the norm and the angles in double precision).
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kTokChunk = 16;      // tokens accumulated together per pass over a weight row
+
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
+    s = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), s);
+  }
+  return s;
+}
+
+// One wave per output feature n (four per work-group); lane l reads the 16-byte
+// chunks 8 l + 512 j of the weight row and of each token's row.
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                     int K, int N, int T, float* __restrict__ y) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= N) return;
+  const uint16_t* wr = w + (int64_t)n * K;
+  for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+    float acc[kTokChunk];
+#pragma unroll
+    for (int i = 0; i < kTokChunk; ++i) acc[i] = 0.f;
+    for (int k = 8 * lane; k < K; k += 512) {
+      const u32x4 wv = ld16(wr + k);
+#pragma unroll
+      for (int i = 0; i < kTokChunk; ++i) {
+        const int t = t0 + i < T ? t0 + i : T - 1;     // rows past T are read again and dropped
+        acc[i] += dot8_bf16(wv, ld16(x + (int64_t)t * K + k));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTokChunk; ++i) {
+      float v = acc[i];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0 && t0 + i < T) y[(int64_t)(t0 + i) * N + n] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_of(double v) { return f32_to_bf16_rne((float)v); }
+
+// Work-group (t, 0): the latent and the RoPE key of token t; (t, 1 + h): head h
+// of its query.  64 threads.
+__global__ __launch_bounds__(64) void front_finish_kernel(const float* __restrict__ kv, const float* __restrict__ q,
+                                                          const int32_t* __restrict__ pos, int H, float eps,
+                                                          float base, uint16_t* __restrict__ q_nope,
+                                                          uint16_t* __restrict__ q_pe, uint16_t* __restrict__ c_kv,
+                                                          uint16_t* __restrict__ k_pe) {
+  const int t = blockIdx.x, part = blockIdx.y, lane = threadIdx.x;
+  const double p = (double)pos[t];
+  // pair i (lane < 32) of a 64-wide rotary vector: angle p * base^(-2i/64)
+  auto rotate = [&](const float* src, uint16_t* dst) {
+    if (lane < 32) {
+      const double ang = p * pow((double)base, -2.0 * lane / 64.0);
+      const double c = cos(ang), s = sin(ang);
+      const double xe = src[2 * lane], xo = src[2 * lane + 1];
+      dst[2 * lane] = bf16_of(xe * c - xo * s);
+      dst[2 * lane + 1] = bf16_of(xe * s + xo * c);
+    }
+  };
+  if (part == 0) {
+    const float* row = kv + (int64_t)t * (kDc + kDr);
+    double v[8], ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = row[8 * lane + i];
+      ss += v[i] * v[i];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const double inv = 1.0 / sqrt(ss / kDc + (double)eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c_kv[(int64_t)t * kDc + 8 * lane + i] = bf16_of(v[i] * inv);
+    rotate(row + kDc, k_pe + (int64_t)t * kDr);
+  } else {
+    const int h = part - 1;
+    const float* row = q + ((int64_t)t * H + h) * (kDn + kDr);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) q_nope[((int64_t)t * H + h) * kDn + 2 * lane + i] = bf16_of(row[2 * lane + i]);
+    rotate(row + kDn, q_pe + ((int64_t)t * H + h) * kDr);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q, const uint16_t* w_dkv,
+                              const int32_t* positions, float rms_eps, float rope_base, float* workspace,
+                              uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
+                              hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  const int n_kv = kDc + kDr, n_q = num_heads * (kDn + kDr);
+  float* kv = workspace;
+  float* q = workspace + (int64_t)n_tokens * n_kv;
+  hipLaunchKernelGGL(rowdot_kernel, dim3((n_kv + 3) / 4), dim3(256), 0, stream, x, w_dkv, hidden, n_kv, n_tokens, kv);
+  hipLaunchKernelGGL(rowdot_kernel, dim3((n_q + 3) / 4), dim3(256), 0, stream, x, w_q, hidden, n_q, n_tokens, q);
+  hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens, 1 + num_heads), dim3(64), 0, stream, kv, q, positions,
+                     num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -25,4 +25,9 @@ hipError_t launch_combine_out_proj(int num_heads, const uint16_t* o_part, const 
 hipError_t launch_wo_proj(int in_features, const float* x, const uint16_t* w_o, int hidden, uint16_t* y,
                           int batch, hipStream_t stream);
 
+hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q, const uint16_t* w_dkv,
+                              const int32_t* positions, float rms_eps, float rope_base, float* workspace,
+                              uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
+                              hipStream_t stream);
+
 }  // namespace mla

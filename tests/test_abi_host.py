@@ -164,3 +164,26 @@ def test_product_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"\boracle\b", text.replace("no CPU fallback", "")), f
+
+
+def test_layer_front_validation(lib):
+    cfg = api.config(16)
+    assert api.layer_front_workspace_bytes(cfg, 26) == 26 * (576 + 16 * 192) * 4
+    assert api.layer_front_workspace_bytes(api.config(128), 3) == 3 * (576 + 128 * 192) * 4
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    ws = api.layer_front_workspace_bytes(cfg, 4)
+    f = lib.mla_layer_front
+
+    def call(x=fake, hidden=2048, eps=1e-6, base=1e4, wsb=ws, n=4, ws_ptr=fake):
+        return f(C.byref(cfg), x, hidden, fake, fake, fake, eps, base, ws_ptr, wsb, fake, fake, fake, fake, n, None)
+
+    assert call(hidden=2044) == L.MLA_ERR_VALUE          # not a multiple of 8
+    assert call(hidden=0) == L.MLA_ERR_VALUE
+    assert call(n=-1) == L.MLA_ERR_VALUE
+    assert call(eps=0.0) == L.MLA_ERR_VALUE
+    assert call(base=1.0) == L.MLA_ERR_VALUE
+    assert call(base=float("inf")) == L.MLA_ERR_VALUE
+    assert call(x=None) == L.MLA_ERR_NULL
+    assert call(x=odd) == L.MLA_ERR_ALIGN
+    assert call(wsb=ws - 4) == L.MLA_ERR_WORKSPACE
+    assert call(x=None, ws_ptr=None, n=0) == L.MLA_OK        # no-op
