@@ -283,6 +283,37 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
 /* n_tokens * (576 + H * 192) * 4 bytes: the fp32 projection results.        */
 size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
 
+/* ------------------------------------------------------------------ prefill
+ * mla_prefill_attn: causal attention of a chunk of T queries in the unabsorbed
+ * form, the one engines use for prefill ([Tutorial] §四; the computation is
+ * [Tutorial] §三's: each head's key and value rebuilt from the latent).  The
+ * chunk is the last T of L positions of one sequence; query i sits at position
+ * p_i = L - T + i and attends to positions 0..p_i:
+ *   K_h[j] = [W_UK[h] c_j ; k_pe_j],  V_h[j] = W_UV[h] c_j,
+ *   out[i][h] = sum_{j<=p_i} softmax_j(scale q_i,h . K_h[j]) V_h[j],
+ *   lse[i][h] = ln sum_{j<=p_i} exp(scale q_i,h . K_h[j]).
+ * K and V are formed in fp32 and kept in the workspace as fp16; the attention
+ * products take fp16 operands (q widened exactly from bf16, P rounded) with
+ * fp32 sums and softmax state.
+ *   q_nope     device [T][H][128] bf16 (queries of positions L-T .. L-1)
+ *   q_pe       device [T][H][64] bf16 (RoPE applied)
+ *   n_queries  T, 0 <= T <= seq_len (0: no-op)
+ *   c_kv, k_pe device [L][512], [L][64] bf16: every position of the sequence,
+ *              the chunk's own included (as mla_layer_front writes them)
+ *   seq_len    L >= 1 (when T > 0)
+ *   w_uk, w_uv device [H][128][512] bf16 ("hdc")
+ *   workspace  device, >= mla_prefill_workspace_bytes(cfg, L) bytes (given as
+ *              workspace_bytes; MLA_ERR_WORKSPACE if smaller)
+ *   out        device [T][H][128] bf16, written
+ *   lse        device [T][H] f32, written when not NULL
+ * The result does not depend on cfg->cache_dtype (the latent comes in as bf16). */
+mla_status mla_prefill_attn(const mla_config* cfg, const uint16_t* q_nope, const uint16_t* q_pe, int32_t n_queries,
+                            const uint16_t* c_kv, const uint16_t* k_pe, int32_t seq_len, const uint16_t* w_uk,
+                            const uint16_t* w_uv, void* workspace, size_t workspace_bytes, uint16_t* out,
+                            float* lse, hipStream_t stream);
+/* H * Lp * 512 bytes, Lp = seq_len rounded up to a multiple of 64.          */
+size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t seq_len);
+
 /* ------------------------------------------------------------------ errors */
 const char* mla_status_string(mla_status s);
 int32_t mla_last_hip_error(void);

@@ -13,11 +13,12 @@ The five steps of one decode, in order:
     out_proj       -> expand through W_UV (and optionally W_O)
 plus the host-side planner plan_splits, and decode_combine_out_proj, which
 runs the last two in one pass.  layer_front produces the inputs of the first
-two steps from a layer's hidden states (projections, RMSNorm, RoPE).
+two steps from a layer's hidden states (projections, RMSNorm, RoPE), and
+prefill_attn runs a prompt chunk's causal attention in the unabsorbed form.
 """
 from .api import (  # noqa: F401
     MlaError, Config, config, cache_bytes_per_token, cache_page_bytes, decode_workspace_bytes,
     plan_splits, cache_append, absorb_q, decode_attn, decode_combine, out_proj, decode_combine_out_proj, status_string,
-    layer_front, layer_front_workspace_bytes,
+    layer_front, layer_front_workspace_bytes, prefill_attn, prefill_workspace_bytes,
     CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK,
 )

@@ -222,3 +222,26 @@ def layer_front(cfg: Config, x, w_q, w_dkv, positions, workspace, q_nope, q_pe, 
                                     _dev(workspace, "workspace"), ws_bytes, _dev(q_nope, "q_nope"),
                                     _dev(q_pe, "q_pe"), _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"), T, _stream()),
            "mla_layer_front")
+
+
+def prefill_workspace_bytes(cfg: Config, seq_len: int) -> int:
+    return int(L.load().mla_prefill_workspace_bytes(C.byref(cfg), int(seq_len)))
+
+
+def prefill_attn(cfg: Config, q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, workspace, out, lse=None) -> None:
+    """Causal unabsorbed attention of the last T of L positions (mla_prefill_attn)."""
+    T, H, Lq = int(q_nope.shape[0]), cfg.num_heads, int(c_kv.shape[0])
+    _need(q_nope, "q_nope", (T, H, 128), 2)
+    _need(q_pe, "q_pe", (T, H, 64), 2)
+    _need(c_kv, "c_kv", (Lq, 512), 2)
+    _need(k_pe, "k_pe", (Lq, 64), 2)
+    _need(w_uk, "w_uk", (H, 128, 512), 2)
+    _need(w_uv, "w_uv", (H, 128, 512), 2)
+    _need(out, "out", (T, H, 128), 2)
+    if lse is not None:
+        _need(lse, "lse", (T, H), 4)
+    ws_bytes = int(workspace.numel()) * int(workspace.element_size())
+    _check(L.load().mla_prefill_attn(C.byref(cfg), _dev(q_nope, "q_nope"), _dev(q_pe, "q_pe"), T,
+                                     _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"), Lq, _dev(w_uk, "w_uk"),
+                                     _dev(w_uv, "w_uv"), _dev(workspace, "workspace"), ws_bytes, _dev(out, "out"),
+                                     _dev(lse, "lse"), _stream()), "mla_prefill_attn")

@@ -216,6 +216,29 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
                                           workspace, q_nope, q_pe, c_kv, k_pe, n_tokens, stream));
 }
 
+size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t seq_len) {
+  if (mla_config_check(cfg) != MLA_OK || seq_len < 0) return 0;
+  return (size_t)cfg->num_heads * (size_t)mla::prefill_padded_len(seq_len) * 512u;
+}
+
+mla_status mla_prefill_attn(const mla_config* cfg, const uint16_t* q_nope, const uint16_t* q_pe, int32_t n_queries,
+                            const uint16_t* c_kv, const uint16_t* k_pe, int32_t seq_len, const uint16_t* w_uk,
+                            const uint16_t* w_uv, void* workspace, size_t workspace_bytes, uint16_t* out,
+                            float* lse, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (n_queries < 0 || seq_len < 0 || n_queries > seq_len) return MLA_ERR_VALUE;
+  if (n_queries == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !c_kv || !k_pe || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
+    return MLA_ERR_ALIGN;
+  if (workspace_bytes < mla_prefill_workspace_bytes(cfg, seq_len)) return MLA_ERR_WORKSPACE;
+  if ((s = check_device()) != MLA_OK) return s;
+  return launched(mla::launch_prefill_attn(cfg->num_heads, cfg->softmax_scale, q_nope, q_pe, n_queries, c_kv, k_pe,
+                                           seq_len, w_uk, w_uv, workspace, out, lse, stream));
+}
+
 const char* mla_status_string(mla_status st) {
   switch (st) {
     case MLA_OK: return "ok";

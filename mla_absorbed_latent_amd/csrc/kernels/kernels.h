@@ -30,4 +30,12 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
                               uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
                               hipStream_t stream);
 
+// Workspace of launch_prefill_attn: K_nope [H][Lp][128] and V^T [H][128][Lp]
+// fp16, Lp = seq_len rounded up to 64.
+int64_t prefill_padded_len(int seq_len);
+hipError_t launch_prefill_attn(int num_heads, float softmax_scale, const uint16_t* q_nope, const uint16_t* q_pe,
+                               int n_queries, const uint16_t* c_kv, const uint16_t* k_pe, int seq_len,
+                               const uint16_t* w_uk, const uint16_t* w_uv, void* workspace, uint16_t* out,
+                               float* lse, hipStream_t stream);
+
 }  // namespace mla

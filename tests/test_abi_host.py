@@ -187,3 +187,22 @@ def test_layer_front_validation(lib):
     assert call(x=odd) == L.MLA_ERR_ALIGN
     assert call(wsb=ws - 4) == L.MLA_ERR_WORKSPACE
     assert call(x=None, ws_ptr=None, n=0) == L.MLA_OK        # no-op
+
+
+def test_prefill_validation(lib):
+    cfg = api.config(16)
+    assert api.prefill_workspace_bytes(cfg, 26) == 16 * 64 * 512
+    assert api.prefill_workspace_bytes(cfg, 128) == 16 * 128 * 512
+    assert api.prefill_workspace_bytes(api.config(128), 65) == 128 * 128 * 512
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    ws = api.prefill_workspace_bytes(cfg, 100)
+
+    def call(T=10, L=100, q=fake, lse=None, wsb=ws):
+        return lib.mla_prefill_attn(C.byref(cfg), q, fake, T, fake, fake, L, fake, fake, fake, wsb, fake, lse, None)
+
+    assert call(T=101) == L.MLA_ERR_VALUE                # more queries than positions
+    assert call(T=-1) == L.MLA_ERR_VALUE
+    assert call(q=None) == L.MLA_ERR_NULL
+    assert call(lse=odd) == L.MLA_ERR_ALIGN
+    assert call(wsb=ws - 1) == L.MLA_ERR_WORKSPACE
+    assert call(T=0, q=None) == L.MLA_OK                 # no-op
