@@ -3,6 +3,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload v3_decode] [--cache-dtype bf16]
 
+(--workload v2lite_prefill / v3_prefill times the prefill attention instead:
+one mla_prefill_attn call over a 4,096-position prompt per step, in TFLOP/s.)
+
 One step = one pass of the whole decode hot path over one batch, all inputs
 already resident in HBM: append the batch's new tokens (quantising if the cache
 is quantised), absorb W_UK into the queries, split-KV attention over the paged
@@ -37,6 +40,12 @@ WORKLOADS = {
     "v2lite_decode": ("v2lite_decode", "V2-Lite-shaped decode attention: H=16, B=32, 4096 tokens/seq, contiguous"),
     "v3_ragged": ("v3_ragged", "V3-shaped ragged decode: H=128, B=128, log-uniform lengths in [128, 65536]"),
     "v2lite_quant": ("v2lite_quant", "quantised latent cache, V2-Lite shapes: H=16, B=64, 16384 tokens/seq"),
+}
+PREFILL_WORKLOADS = {
+    "v2lite_prefill": ("v2lite_prefill", "V2-Lite-shaped prompt chunk: H=16, 4096 positions, no cached prefix, "
+                                         "causal unabsorbed attention"),
+    "v3_prefill": ("v3_prefill", "V3-shaped prompt chunk: H=128, 4096 positions, no cached prefix, "
+                                 "causal unabsorbed attention"),
 }
 DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3, "int8t": 4}
 
@@ -75,6 +84,104 @@ def cpu_baseline(case, cache_dtype, budget_s=15.0):
             "kind": "oracle",
             "sample": "%d of %d sequences (%d tokens), fp64 numpy absorbed decode incl. W_UK/W_UV, %.1f s"
                       % (seqs, case.B, done_tokens, t_total)}
+
+
+def prefill_flops(case):
+    """Algorithmic FLOPs of one mla_prefill_attn call: the K/V expansion
+    (2 x 512 x 256 per position and head) and the attention (2 x (192 + 128) per
+    query, visible key and head)."""
+    pos = case.L - case.T + np.arange(case.T, dtype=np.int64)
+    return case.H * (2.0 * 512 * 256 * case.L + 640.0 * float(np.sum(pos + 1)))
+
+
+def cpu_baseline_prefill(case, budget_s=15.0):
+    """Time the oracle's prefill (fp64 numpy) on leading sub-chunks of the prompt
+    (positions 0..n-1, n doubling from 64) until ~budget_s; report TFLOP/s."""
+    from oracle import mla_ref, prefill
+    f = mla_ref.bf16_to_f64
+    wk, wv = f(case.w_uk), f(case.w_uv)
+    n, t_total, flops, done = 64, 0.0, 0.0, []
+    while n <= case.L:
+        t0 = time.perf_counter()
+        prefill.prefill_unabsorbed(f(case.q_nope[:n]), f(case.q_pe[:n]), f(case.c[:n]), f(case.r[:n]), wk, wv,
+                                   case.softmax_scale)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        flops += case.H * (2.0 * 512 * 256 * n + 640.0 * n * (n + 1) / 2)
+        done.append(n)
+        n *= 2
+        if t_total + 3 * dt > 2 * budget_s:         # the next size costs about 2-4x this one
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "fp64 numpy prefill of the prompt's first n positions, n in %s, %.1f s" % (done, t_total)}
+
+
+def bench_prefill(args):
+    import torch
+    import mla_synth
+    from mla_absorbed_latent_amd import api
+
+    gen, desc = PREFILL_WORKLOADS[args.workload]
+    case = getattr(mla_synth, gen)()
+    dev = torch.device("cuda:0")
+    cfg = api.config(case.H, 0, case.softmax_scale)
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_nope, q_pe, c, r = bits(case.q_nope), bits(case.q_pe), bits(case.c), bits(case.r)
+    w_uk, w_uv = bits(case.w_uk), bits(case.w_uv)
+    ws = torch.empty(api.prefill_workspace_bytes(cfg, case.L), dtype=torch.uint8, device=dev)
+    out = torch.empty(case.T, case.H, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(case.T, case.H, dtype=torch.float32, device=dev)
+
+    def step():
+        api.prefill_attn(cfg, q_nope, q_pe, c, r, w_uk, w_uv, ws, out, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    flops = prefill_flops(case)
+    tf = flops / (call_ms * 1e-3) / 1e12
+    line = {
+        "metric": "MLA prefill attention (unabsorbed, causal): TFLOP/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no checkpoint)",
+        "config": {"workload": args.workload, "description": desc, "heads": case.H, "queries": case.T,
+                   "positions": case.L},
+        "tokens_per_s": round(case.T / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "mla_prefill_attn (expand_kv + prefill_attn)",
+                     "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS_16, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_PEAK_TFLOPS_16, 4), "traffic": None, "launch_ms": round(call_ms, 5),
+                     "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline_prefill(case)
+    print(json.dumps(line), flush=True)
 
 
 def measured_peaks(torch, dev):
@@ -135,7 +242,7 @@ def main():
     # after some tens of milliseconds of sustained load: warm up for ~0.3 s.
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="v3_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="v3_decode", choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--cache-dtype", default="bf16", choices=sorted(DTYPES))
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,6 +262,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode shards by sequence "
               "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in PREFILL_WORKLOADS:
+        return bench_prefill(args)
 
     import torch
     import mla_synth

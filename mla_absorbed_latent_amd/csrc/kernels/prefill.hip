@@ -11,9 +11,10 @@
 //
 // Two kernels, both on the matrix cores (fp32 sums):
 //   expand_kv_kernel: K_nope [H][Lp][128] and V^T [H][128][Lp] (fp16, Lp = L
-//     rounded up to 64, pad positions zero) from c_kv and W_UK / W_UV (bf16 MFMA);
-//   prefill_attn_kernel: flash attention per (64 queries, head), S^T = K Q^T and
-//     O^T = V^T P^T on v_mfma_f32_16x16x32_f16, streaming softmax in fp32.
+//     rounded up to 64, pad positions zero) from c_kv and W_UK / W_UV, a tiled
+//     bf16 MFMA GEMM;
+//   prefill_attn_kernel: flash attention per (128 queries, head), S^T = K Q^T
+//     and O^T = V^T P^T on v_mfma_f32_16x16x32_f16, streaming softmax in fp32.
 // The operands of the attention products are fp16 (bf16 inputs widen exactly);
 // P is rounded to fp16, its fp32 sum taken before rounding.
 #include "common.h"
@@ -31,61 +32,139 @@ __device__ __forceinline__ floatx4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two fp16 (round to nearest even), packed low | high.
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
-// Grid (Lp / 64, H, 2); z = 0 writes K_nope, z = 1 writes V^T.  Wave w covers
-// positions 64 bx + 16 w .. +15; its latent fragments (512 channels, the same
-// register layout serves as A or B) stay in registers while it walks the 128
-// output features of head h in tiles of 16.
+// Grid (ceil(Lp / 128), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
+// work-group computes 128 positions x the 128 output features of head h as a
+// tiled GEMM over the 512 latent channels: chunks of 64 channels of the latent
+// rows and of the weight rows are staged in LDS (double-buffered, 16-byte chunk
+// c of row r at c ^ (r & 7)), and wave (wm, wn) computes 64 positions x 64
+// features from them (4 x 4 tiles of 16 x 16).  Both operands are rows of 64
+// channels with the same fragment layout, so the weight is the A operand for
+// K_nope (D[feature][position]: four consecutive features per lane and store)
+// and the B operand for V^T (D[position][feature]: four consecutive positions).
+constexpr int kXT = 128;                  // positions per work-group
+constexpr int kXChunk = 64;               // channels per LDS chunk
+constexpr int kXRow = kXChunk * 2;        // 128 B
+constexpr int kXBuf = 2 * kXT * kXRow;    // latent + weight tiles, 32 KB
+
 __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
                                                         const uint16_t* __restrict__ w_uk,
                                                         const uint16_t* __restrict__ w_uv, int L, int Lp,
                                                         uint16_t* __restrict__ k_nope, uint16_t* __restrict__ v_t) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, is_v = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kXBuf];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int j0 = blockIdx.x * 64 + wave * 16;
-  const int j = j0 + li;
-  u32x4 cf[kDc / 32];
-#pragma unroll
-  for (int ks = 0; ks < kDc / 32; ++ks)
-    cf[ks] = j < L ? ld16(c_kv + (int64_t)j * kDc + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+  const int wm = wave >> 1, wn = wave & 1;          // positions 64 wm.., features 64 wn..
+  const int h = blockIdx.y, is_v = blockIdx.z;
+  const int j0 = blockIdx.x * kXT;
   const uint16_t* w = (is_v ? w_uv : w_uk) + (int64_t)h * kDn * kDc;
-  for (int mt = 0; mt < kDn / 16; ++mt) {
-    const uint16_t* wr = w + (int64_t)(16 * mt + li) * kDc + 8 * g;
-    u32x4 wf[kDc / 32];
+
+  // staging: rows 0..127 latent, 128..255 weight; 8 chunks per row; 8 per thread
+  u32x4 st[8];
+  auto load = [&](int kc) {
 #pragma unroll
-    for (int ks = 0; ks < kDc / 32; ++ks) wf[ks] = ld16(wr + 32 * ks);
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (!is_v) {
-      // D[feature 16 mt + 4 g + r][position j0 + li]
+    for (int n = 0; n < 8; ++n) {
+      const int idx = tid + 256 * n, row = idx >> 3, ch = idx & 7;
+      if (row < kXT) {
+        const int j = j0 + row;
+        st[n] = j < L ? ld16(c_kv + (int64_t)j * kDc + kc * kXChunk + 8 * ch) : u32x4{0, 0, 0, 0};
+      } else {
+        st[n] = ld16(w + (int64_t)(row - kXT) * kDc + kc * kXChunk + 8 * ch);
+      }
+    }
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-      for (int ks = 0; ks < kDc / 32; ++ks)
-        acc = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[ks]), __builtin_bit_cast(bf16x8, cf[ks]), acc);
-      u32x2 o = {pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(k_nope + ((int64_t)h * Lp + j) * kDn + 16 * mt + 4 * g) = o;
-    } else {
-      // D[position j0 + 4 g + r][feature 16 mt + li]
+    for (int n = 0; n < 8; ++n) {
+      const int idx = tid + 256 * n, row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(lds + buf * kXBuf + row * kXRow + 16 * (ch ^ (row & 7))) = st[n];
+    }
+  };
+
+  floatx4 acc[4][4];
 #pragma unroll
-      for (int ks = 0; ks < kDc / 32; ++ks)
-        acc = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, cf[ks]), __builtin_bit_cast(bf16x8, wf[ks]), acc);
-      u32x2 o = {pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 16 * mt + li) * Lp + j0 + 4 * g) = o;
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  store(0);
+  __syncthreads();
+  constexpr int kChunks = kDc / kXChunk;
+  for (int kc = 0; kc < kChunks; ++kc) {
+    if (kc + 1 < kChunks) load(kc + 1);
+    const char* buf = lds + (kc & 1) * kXBuf;
+#pragma unroll
+    for (int ks = 0; ks < kXChunk / 32; ++ks) {
+      u32x4 pf[4], wf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pr = 64 * wm + 16 * t + li, wr = kXT + 64 * wn + 16 * t + li;
+        pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * ((4 * ks + g) ^ (pr & 7)));
+        wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * ((4 * ks + g) ^ (wr & 7)));
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          // a: position tile, b: feature tile
+          if (!is_v)
+            acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[b]), __builtin_bit_cast(bf16x8, pf[a]),
+                                          acc[a][b]);
+          else
+            acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf[a]), __builtin_bit_cast(bf16x8, wf[b]),
+                                          acc[a][b]);
+        }
+    }
+    if (kc + 1 < kChunks) {
+      store((kc + 1) & 1);
+      __syncthreads();
     }
   }
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const u32x2 o = {pack_f16(acc[a][b][0], acc[a][b][1]), pack_f16(acc[a][b][2], acc[a][b][3])};
+      if (!is_v) {
+        // D[feature 64 wn + 16 b + 4 g + r][position 64 wm + 16 a + li]
+        const int j = j0 + 64 * wm + 16 * a + li;
+        if (j < Lp) *reinterpret_cast<u32x2*>(k_nope + ((int64_t)h * Lp + j) * kDn + 64 * wn + 16 * b + 4 * g) = o;
+      } else {
+        // D[position 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]
+        const int j = j0 + 64 * wm + 16 * a + 4 * g;
+        if (j < Lp)
+          *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 64 * wn + 16 * b + li) * Lp + j) = o;
+      }
+    }
 }
 
-// Grid (ceil(T / 64), H), 256 threads; the query blocks run last-first (the
-// longest causal ranges start first).  Wave w owns queries i = 64 qb + 16 w +
-// (lane % 16).  Per 64-key block: S^T[key][query] (4 key tiles x 6 k-steps),
-// softmax per query column (its 64 keys sit in the four lanes l % 16 = q),
-// then O^T[vdim][query] += V^T P^T (8 vdim tiles x 2 k-steps).  P^T feeds the
+// Grid (ceil(T / 128), H), 256 threads; the query blocks run last-first (the
+// longest causal ranges start first).  Wave w owns queries i = 128 qb + 32 w +
+// 16 u + (lane % 16), u = 0, 1.  Per 64-key block: S^T[key][query] (4 key tiles
+// x 6 k-steps, each K fragment read once for both query groups), softmax per
+// query column (its 64 keys sit in the four lanes l % 16 = q), then
+// O^T[vdim][query] += V^T P^T (8 vdim tiles x 2 k-steps).  P^T feeds the
 // second product straight from the score registers: k index 8 g + e of a
 // k-step stands for key 32 ks + 4 g + e (e < 4) or 32 ks + 16 + 4 g + e - 4,
 // and V^T is read from LDS in the same order.
-__global__ __launch_bounds__(256) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
+constexpr int kU = 1;                     // 16-query groups per wave
+constexpr int kWaves = 8;                 // waves per work-group
+constexpr int kQW = 16 * kU;              // queries per wave
+constexpr int kQB = kWaves * kQW;         // queries per work-group
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKLoads = 64 * 24 / kThreads;   // K-tile chunks per thread
+constexpr int kVLoads = 128 * 8 / kThreads;   // V^T-tile chunks per thread
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
                                                            const uint16_t* __restrict__ q_pe,
                                                            const uint16_t* __restrict__ k_pe,
                                                            const uint16_t* __restrict__ k_nope,
@@ -96,33 +175,42 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) char v_lds[kVTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int h = blockIdx.y;
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int i_raw = qb * 64 + wave * 16 + li;
-  const int i = i_raw < T ? i_raw : T - 1;         // rows past T repeat the last query, never stored
-  const int qpos = L - T + i;
-  const int p_first = L - T + qb * 64;
-  const int p_last = L - T + min(qb * 64 + 63, T - 1);
+  // Work-groups are dealt to the 8 XCDs round robin by linear id.  With H a
+  // multiple of 8 (16 or 128), the k-th work-group of XCD x takes head
+  // x + 8 (k / nqb) and query block nqb - 1 - k % nqb: all query blocks of a
+  // head run on one XCD (its K/V stays in that L2), longest causal ranges first.
+  const int nqb = gridDim.x;
+  const int wg_id = blockIdx.x + nqb * blockIdx.y;
+  const int xcd = wg_id & 7, k_on_xcd = wg_id >> 3;
+  const int h = xcd + 8 * (k_on_xcd / nqb);
+  const int qb = nqb - 1 - k_on_xcd % nqb;
+  const int p_first = L - T + qb * kQB;
+  const int p_last = L - T + min(qb * kQB + kQB - 1, T - 1);
   const int n_blocks = p_last / 64 + 1;
 
-  // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (bf16 -> fp16, exact).
-  u32x4 qf[6];
-  {
+  int i_raw[kU], qpos[kU];
+  u32x4 qf[kU][6];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    i_raw[u] = qb * kQB + kQW * wave + 16 * u + li;
+    const int i = i_raw[u] < T ? i_raw[u] : T - 1;   // rows past T repeat the last query, never stored
+    qpos[u] = L - T + i;
+    // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (bf16 -> fp16, exact).
     const uint16_t* qn = q_nope + ((int64_t)i * H + h) * kDn + 8 * g;
     const uint16_t* qp = q_pe + ((int64_t)i * H + h) * kDr + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
+    for (int ks = 0; ks < 4; ++ks) qf[u][ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[4 + ks] = bf16x8_to_f16x8(ld16(qp + 32 * ks));
+    for (int ks = 0; ks < 2; ++ks) qf[u][4 + ks] = bf16x8_to_f16x8(ld16(qp + 32 * ks));
   }
 
   // Tile staging: 64 keys x 24 chunks of K (16 from K_nope, 8 from k_pe), and
   // 128 V^T rows x 8 chunks; six and four 16-byte loads per thread.
-  u32x4 kr[6], vr[4];
+  u32x4 kr[kKLoads], vr[kVLoads];
   auto load_tile = [&](int kb) {
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
-      const int idx = tid + 256 * n, key = idx / 24, ch = idx % 24;
+    for (int n = 0; n < kKLoads; ++n) {
+      const int idx = tid + kThreads * n, key = idx / 24, ch = idx % 24;
       const int j = kb * 64 + key;
       if (ch < 16) {
         kr[n] = ld16(k_nope + ((int64_t)h * Lp + j) * kDn + 8 * ch);
@@ -132,29 +220,36 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const uint16_t* __res
       }
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int idx = tid + 256 * n, d = idx >> 3, ch = idx & 7;
+    for (int n = 0; n < kVLoads; ++n) {
+      const int idx = tid + kThreads * n, d = idx >> 3, ch = idx & 7;
       vr[n] = ld16(v_t + ((int64_t)h * kDn + d) * Lp + kb * 64 + 8 * ch);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
-      const int idx = tid + 256 * n, key = idx / 24, ch = idx % 24;
+    for (int n = 0; n < kKLoads; ++n) {
+      const int idx = tid + kThreads * n, key = idx / 24, ch = idx % 24;
       *reinterpret_cast<u32x4*>(k_lds + key * kKRow + 16 * ch) = kr[n];
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int idx = tid + 256 * n, d = idx >> 3, ch = idx & 7;
+    for (int n = 0; n < kVLoads; ++n) {
+      const int idx = tid + kThreads * n, d = idx >> 3, ch = idx & 7;
       *reinterpret_cast<u32x2*>(v_lds + d * kVRow + 16 * ch) = u32x2{vr[n][0], vr[n][1]};
       *reinterpret_cast<u32x2*>(v_lds + d * kVRow + 16 * ch + 8) = u32x2{vr[n][2], vr[n][3]};
     }
   };
 
-  floatx4 o[8];
+  floatx4 o[kU][8];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[u][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[kU], l_run[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
 
   load_tile(0);
   for (int kb = 0; kb < n_blocks; ++kb) {
@@ -163,73 +258,98 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(const uint16_t* __res
     __syncthreads();
     if (kb + 1 < n_blocks) load_tile(kb + 1);
 
-    floatx4 s[4];
+    floatx4 s[kU][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kU; ++u) s[u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
       const char* krow = k_lds + (16 * kt + li) * kKRow + 16 * g;
 #pragma unroll
       for (int ks = 0; ks < 6; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 64 * ks);
-        s[kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[ks]), s[kt]);
+        const half8 a = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(krow + 64 * ks));
+#pragma unroll
+        for (int u = 0; u < kU; ++u) s[u][kt] = mfma16x16x32(a, __builtin_bit_cast(half8, qf[u][ks]), s[u][kt]);
       }
     }
-    // scores in log2 units; keys after the query (and pad keys) masked
-    const bool diag = kb * 64 + 63 > p_first;
-    float mb = -INFINITY;
+    // keys after the query (and pad keys) masked; only blocks that reach past
+    // the work-group's first query can hold such keys
+    if (kb * 64 + 63 > p_first) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[kt][r] * scale_log2;
-        if (diag && kb * 64 + 16 * kt + 4 * g + r > qpos) v = -INFINITY;
-        s[kt][r] = v;
-        mb = fmaxf(mb, v);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * 64 + 16 * kt + 4 * g + r > qpos[u]) s[u][kt][r] = -INFINITY;
+    }
+    // streaming softmax on raw scores: p = 2^(c s - c m) with c = scale log2(e)
+    u32x4 pb[kU][2];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float mb = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[u][kt][r]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float m_new = fmaxf(m_run[u], mb);       // finite: key 0 is in every query's range
+      const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * scale_log2);
+      m_run[u] = m_new;
+      const float neg_mc = -m_new * scale_log2;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[u][kt][r], scale_log2, neg_mc));
+          s[u][kt][r] = p;
+          lsum += p;
+        }
+      l_run[u] = l_run[u] * alpha + lsum;
+      // the running maximum of most columns stops moving after a few blocks:
+      // rescale only when some column's changed (alpha == 1 leaves o as it is)
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[u][mt] *= alpha;
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);            // finite: key 0 is in every query's range
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int ks = 0; ks < 2; ++ks)
+        pb[u][ks] = u32x4{pack_f16(s[u][2 * ks][0], s[u][2 * ks][1]), pack_f16(s[u][2 * ks][2], s[u][2 * ks][3]),
+                          pack_f16(s[u][2 * ks + 1][0], s[u][2 * ks + 1][1]),
+                          pack_f16(s[u][2 * ks + 1][2], s[u][2 * ks + 1][3])};
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[kt][r] - m_new);
-        s[kt][r] = p;
-        lsum += p;
-      }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pb = {pack_f16(s[2 * ks][0], s[2 * ks][1]), pack_f16(s[2 * ks][2], s[2 * ks][3]),
-                        pack_f16(s[2 * ks + 1][0], s[2 * ks + 1][1]), pack_f16(s[2 * ks + 1][2], s[2 * ks + 1][3])};
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const char* vrow = v_lds + (16 * mt + li) * kVRow + 2 * (32 * ks + 4 * g);
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        o[mt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, pb), o[mt]);
+        const half8 a = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(a, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
       }
-    }
   }
 
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (i_raw < T) {
-    const float inv = 1.f / l_run;
-    uint16_t* orow = out + ((int64_t)i * H + h) * kDn + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const uint32_t a = (uint32_t)f32_to_bf16_rne(o[mt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][1] * inv) << 16);
-      const uint32_t b = (uint32_t)f32_to_bf16_rne(o[mt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][3] * inv) << 16);
-      *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
+  for (int u = 0; u < kU; ++u) {
+    float l = l_run[u];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (i_raw[u] < T) {
+      const float inv = 1.f / l;
+      uint16_t* orow = out + ((int64_t)i_raw[u] * H + h) * kDn + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t a = (uint32_t)f32_to_bf16_rne(o[u][mt][0] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[u][mt][1] * inv) << 16);
+        const uint32_t b = (uint32_t)f32_to_bf16_rne(o[u][mt][2] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[u][mt][3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
+      }
+      if (lse != nullptr && g == 0) lse[(int64_t)i_raw[u] * H + h] = (m_run[u] * scale_log2 + __log2f(l)) * 0.6931471805599453f;
     }
-    if (lse != nullptr && g == 0) lse[(int64_t)i * H + h] = (m_run + log2f(l_run)) * 0.6931471805599453f;
   }
 }
 
@@ -245,9 +365,11 @@ hipError_t launch_prefill_attn(int num_heads, float softmax_scale, const uint16_
   const int64_t Lp = prefill_padded_len(seq_len);
   uint16_t* k_nope = static_cast<uint16_t*>(workspace);
   uint16_t* v_t = k_nope + (int64_t)num_heads * Lp * kDn;
-  hipLaunchKernelGGL(expand_kv_kernel, dim3((unsigned)(Lp / 64), num_heads, 2), dim3(256), 0, stream, c_kv, w_uk,
+  hipLaunchKernelGGL(expand_kv_kernel, dim3((unsigned)((Lp + kXT - 1) / kXT), num_heads, 2), dim3(256), 0, stream,
+                     c_kv, w_uk,
                      w_uv, seq_len, (int)Lp, k_nope, v_t);
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((n_queries + 63) / 64, num_heads), dim3(256), 0, stream, q_nope,
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((n_queries + kQB - 1) / kQB, num_heads), dim3(kThreads), 0, stream,
+                     q_nope,
                      q_pe, k_pe, k_nope, v_t, n_queries, seq_len, (int)Lp, num_heads,
                      softmax_scale * 1.4426950408889634f, out, lse);
   return hipGetLastError();
