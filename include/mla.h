@@ -300,7 +300,7 @@ size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
  *   n_queries  T, 0 <= T <= seq_len (0: no-op)
  *   c_kv, k_pe device [L][512], [L][64] bf16: every position of the sequence,
  *              the chunk's own included (as mla_layer_front writes them)
- *   seq_len    L >= 1 (when T > 0)
+ *   seq_len    L, 1 <= L <= 2^23 (when T > 0)
  *   w_uk, w_uv device [H][128][512] bf16 ("hdc")
  *   workspace  device, >= mla_prefill_workspace_bytes(cfg, L) bytes (given as
  *              workspace_bytes; MLA_ERR_WORKSPACE if smaller)

@@ -227,7 +227,7 @@ mla_status mla_prefill_attn(const mla_config* cfg, const uint16_t* q_nope, const
                             float* lse, hipStream_t stream) {
   mla_status s = mla_config_check(cfg);
   if (s != MLA_OK) return s;
-  if (n_queries < 0 || seq_len < 0 || n_queries > seq_len) return MLA_ERR_VALUE;
+  if (n_queries < 0 || seq_len < 0 || n_queries > seq_len || seq_len > (1 << 23)) return MLA_ERR_VALUE;
   if (n_queries == 0) return MLA_OK;
   if (!q_nope || !q_pe || !c_kv || !k_pe || !w_uk || !w_uv || !workspace || !out) return MLA_ERR_NULL;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(w_uk) ||

@@ -23,11 +23,6 @@
 namespace mla {
 namespace {
 
-constexpr int kKRow = 192 * 2 + 16;   // LDS bytes per key row (K_nope | k_pe, fp16) + 16 B pad
-constexpr int kVRow = 64 * 2 + 8;     // LDS bytes per V^T row (64 keys, fp16) + 8 B pad
-constexpr int kKTile = 64 * kKRow;    // 25,600 B
-constexpr int kVTile = 128 * kVRow;   // 17,408 B
-
 __device__ __forceinline__ floatx4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -147,32 +142,42 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
     }
 }
 
-// Grid (ceil(T / 128), H), 256 threads; the query blocks run last-first (the
-// longest causal ranges start first).  Wave w owns queries i = 128 qb + 32 w +
-// 16 u + (lane % 16), u = 0, 1.  Per 64-key block: S^T[key][query] (4 key tiles
-// x 6 k-steps, each K fragment read once for both query groups), softmax per
-// query column (its 64 keys sit in the four lanes l % 16 = q), then
-// O^T[vdim][query] += V^T P^T (8 vdim tiles x 2 k-steps).  P^T feeds the
-// second product straight from the score registers: k index 8 g + e of a
-// k-step stands for key 32 ks + 4 g + e (e < 4) or 32 ks + 16 + 4 g + e - 4,
-// and V^T is read from LDS in the same order.
-constexpr int kU = 1;                     // 16-query groups per wave
+// Grid (ceil(T / 128), H), 512 threads (8 waves).  Wave w owns queries
+// i = 128 qb + 16 w + (lane % 16).  Per 64-key block: S^T[key][query] (4 key
+// tiles x 6 k-steps), softmax per query column (its 64 keys sit in the four
+// lanes l % 16 = q), then O^T[vdim][query] += V^T P^T (8 vdim tiles x 2
+// k-steps).  P^T feeds the second product straight from the score registers:
+// k index 8 g + e of a k-step stands for key 32 ks + 4 g + e (e < 4) or
+// 32 ks + 16 + 4 g + e - 4, and V^T is read from LDS in the same order.
+//
+// Tiles go from global memory straight into LDS (global_load_lds_dwordx4: lane
+// i of a wave instruction writes bytes 16 i .. 16 i + 15 of a 1 KB segment),
+// double-buffered: the loads of block kb + 1 run under the products of block
+// kb, and one barrier per block separates the two.  Each lane picks the global
+// 16-byte chunk that belongs at its LDS slot, which gives the layouts
+//   K tile   [64 keys][24 chunks of 8] (128 K_nope dims fp16, then 64 k_pe dims
+//            kept in bf16), chunk c of key k at slot c ^ (k & 7);
+//   V^T tile [128 dims][8 chunks of 8 keys] fp16, chunk c of dim d at c ^ (d & 7);
+// the XOR spreads the 16 rows a fragment read touches over distinct banks.  The
+// RoPE part of the scores uses the bf16 matrix instruction on the bf16 q_pe and
+// k_pe (the products are exact either way).
 constexpr int kWaves = 8;                 // waves per work-group
-constexpr int kQW = 16 * kU;              // queries per wave
-constexpr int kQB = kWaves * kQW;         // queries per work-group
+constexpr int kQB = 16 * kWaves;          // queries per work-group
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKLoads = 64 * 24 / kThreads;   // K-tile chunks per thread
-constexpr int kVLoads = 128 * 8 / kThreads;   // V^T-tile chunks per thread
+constexpr int kKBytes = 64 * 24 * 16;     // 24,576
+constexpr int kVBytes = 128 * 8 * 16;     // 16,384
+constexpr int kBufBytes = kKBytes + kVBytes;
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
-                                                           const uint16_t* __restrict__ q_pe,
-                                                           const uint16_t* __restrict__ k_pe,
-                                                           const uint16_t* __restrict__ k_nope,
-                                                           const uint16_t* __restrict__ v_t, int T, int L, int Lp,
-                                                           int H, float scale_log2, uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char k_lds[kKTile];
-  __shared__ __attribute__((aligned(16))) char v_lds[kVTile];
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
+                                                                const uint16_t* __restrict__ q_pe,
+                                                                const uint16_t* __restrict__ k_pe,
+                                                                const uint16_t* __restrict__ k_nope,
+                                                                const uint16_t* __restrict__ v_t, int T, int L,
+                                                                int Lp, int H, float scale_log2,
+                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   // Work-groups are dealt to the 8 XCDs round robin by linear id.  With H a
@@ -188,168 +193,146 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int p_last = L - T + min(qb * kQB + kQB - 1, T - 1);
   const int n_blocks = p_last / 64 + 1;
 
-  int i_raw[kU], qpos[kU];
-  u32x4 qf[kU][6];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    i_raw[u] = qb * kQB + kQW * wave + 16 * u + li;
-    const int i = i_raw[u] < T ? i_raw[u] : T - 1;   // rows past T repeat the last query, never stored
-    qpos[u] = L - T + i;
-    // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (bf16 -> fp16, exact).
+  const int i_raw = qb * kQB + 16 * wave + li;
+  const int i = i_raw < T ? i_raw : T - 1;         // rows past T repeat the last query, never stored
+  const int qpos = L - T + i;
+  // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (q_nope widened to fp16,
+  // exact; q_pe stays bf16).
+  u32x4 qf[6];
+  {
     const uint16_t* qn = q_nope + ((int64_t)i * H + h) * kDn + 8 * g;
     const uint16_t* qp = q_pe + ((int64_t)i * H + h) * kDr + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[u][ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[u][4 + ks] = bf16x8_to_f16x8(ld16(qp + 32 * ks));
+    for (int ks = 0; ks < 2; ++ks) qf[4 + ks] = ld16(qp + 32 * ks);
   }
 
-  // Tile staging: 64 keys x 24 chunks of K (16 from K_nope, 8 from k_pe), and
-  // 128 V^T rows x 8 chunks; six and four 16-byte loads per thread.
-  u32x4 kr[kKLoads], vr[kVLoads];
-  auto load_tile = [&](int kb) {
+  // This lane's part of a tile: K segments wave, wave + 8, wave + 16 (LDS slot
+  // P = 64 segment + lane = 24 key + (chunk ^ (key & 7))), V^T segments wave,
+  // wave + 8 (P = 8 dim + (chunk ^ (dim & 7))).  Offsets are 32-bit, from
+  // per-head bases (a head's K_nope or V^T spans Lp * 128 < 2^31 elements).
+  const uint16_t* k_nope_h = k_nope + (int64_t)h * Lp * kDn;
+  const uint16_t* v_t_h = v_t + (int64_t)h * kDn * Lp;
+  int kslot[3], voff[2];
 #pragma unroll
-    for (int n = 0; n < kKLoads; ++n) {
-      const int idx = tid + kThreads * n, key = idx / 24, ch = idx % 24;
-      const int j = kb * 64 + key;
-      if (ch < 16) {
-        kr[n] = ld16(k_nope + ((int64_t)h * Lp + j) * kDn + 8 * ch);
-      } else {
-        const int jc = j < L ? j : L - 1;          // pad keys are masked; read a real row
-        kr[n] = bf16x8_to_f16x8(ld16(k_pe + (int64_t)jc * kDr + 8 * (ch - 16)));
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < kVLoads; ++n) {
-      const int idx = tid + kThreads * n, d = idx >> 3, ch = idx & 7;
-      vr[n] = ld16(v_t + ((int64_t)h * kDn + d) * Lp + kb * 64 + 8 * ch);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int n = 0; n < kKLoads; ++n) {
-      const int idx = tid + kThreads * n, key = idx / 24, ch = idx % 24;
-      *reinterpret_cast<u32x4*>(k_lds + key * kKRow + 16 * ch) = kr[n];
-    }
-#pragma unroll
-    for (int n = 0; n < kVLoads; ++n) {
-      const int idx = tid + kThreads * n, d = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x2*>(v_lds + d * kVRow + 16 * ch) = u32x2{vr[n][0], vr[n][1]};
-      *reinterpret_cast<u32x2*>(v_lds + d * kVRow + 16 * ch + 8) = u32x2{vr[n][2], vr[n][3]};
-    }
-  };
-
-  floatx4 o[kU][8];
-#pragma unroll
-  for (int u = 0; u < kU; ++u)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[u][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kU], l_run[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    m_run[u] = -INFINITY;
-    l_run[u] = 0.f;
+  for (int n = 0; n < 3; ++n) {
+    const int P = 64 * (wave + 8 * n) + lane, key = P / 24;
+    kslot[n] = key | (((P % 24) ^ (key & 7)) << 8);         // key | chunk << 8
   }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int P = 64 * (wave + 8 * n) + lane, d = P >> 3, ch = (P & 7) ^ (d & 7);
+    voff[n] = d * Lp + 8 * ch;
+  }
+  auto issue = [&](int kb, int buf) {
+    char* base = lds + buf * kBufBytes;
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+      const int j = kb * 64 + (kslot[n] & 255), ch = kslot[n] >> 8;
+      const uint16_t* src = ch < 16 ? k_nope_h + (j * kDn + 8 * ch)
+                                    : k_pe + ((j < L ? j : L - 1) * kDr + 8 * (ch - 16));   // pad keys: row L-1
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * (wave + 8 * n)), 16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      __builtin_amdgcn_global_load_lds(v_t_h + (voff[n] + kb * 64), (lds_void*)(base + kKBytes + 1024 * (wave + 8 * n)),
+                                       16, 0, 0);
+  };
 
-  load_tile(0);
+  floatx4 o[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  issue(0, 0);
   for (int kb = 0; kb < n_blocks; ++kb) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kb + 1 < n_blocks) load_tile(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                   // tile kb in LDS; block kb - 1 done by every wave
+    if (kb + 1 < n_blocks) issue(kb + 1, (kb + 1) & 1);
+    const char* kt_lds = lds + (kb & 1) * kBufBytes;
+    const char* vt_lds = kt_lds + kKBytes;
 
-    floatx4 s[kU][4];
+    floatx4 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) s[u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const char* krow = k_lds + (16 * kt + li) * kKRow + 16 * g;
+      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int key = 16 * kt + li;
+      const char* krow = kt_lds + key * 384;
 #pragma unroll
       for (int ks = 0; ks < 6; ++ks) {
-        const half8 a = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(krow + 64 * ks));
-#pragma unroll
-        for (int u = 0; u < kU; ++u) s[u][kt] = mfma16x16x32(a, __builtin_bit_cast(half8, qf[u][ks]), s[u][kt]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * ks + g) ^ (key & 7)));
+        if (ks < 4)
+          s[kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[ks]), s[kt]);
+        else
+          s[kt] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), s[kt]);
       }
     }
     // keys after the query (and pad keys) masked; only blocks that reach past
     // the work-group's first query can hold such keys
     if (kb * 64 + 63 > p_first) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb * 64 + 16 * kt + 4 * g + r > qpos[u]) s[u][kt][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          if (kb * 64 + 16 * kt + 4 * g + r > qpos) s[kt][r] = -INFINITY;
     }
     // streaming softmax on raw scores: p = 2^(c s - c m) with c = scale log2(e)
-    u32x4 pb[kU][2];
+    float mb = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      float mb = -INFINITY;
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[kt][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float m_new = fmaxf(m_run, mb);           // finite: key 0 is in every query's range
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+    m_run = m_new;
+    const float neg_mc = -m_new * scale_log2;
+    float lsum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[u][kt][r]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float m_new = fmaxf(m_run[u], mb);       // finite: key 0 is in every query's range
-      const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * scale_log2);
-      m_run[u] = m_new;
-      const float neg_mc = -m_new * scale_log2;
-      float lsum = 0.f;
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[u][kt][r], scale_log2, neg_mc));
-          s[u][kt][r] = p;
-          lsum += p;
-        }
-      l_run[u] = l_run[u] * alpha + lsum;
-      // the running maximum of most columns stops moving after a few blocks:
-      // rescale only when some column's changed (alpha == 1 leaves o as it is)
-      if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[u][mt] *= alpha;
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, neg_mc));
+        s[kt][r] = p;
+        lsum += p;
       }
+    l_run = l_run * alpha + lsum;
+    // the running maximum of most columns stops moving after a few blocks:
+    // rescale only when some column's changed (alpha == 1 leaves o as it is)
+    if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pb[u][ks] = u32x4{pack_f16(s[u][2 * ks][0], s[u][2 * ks][1]), pack_f16(s[u][2 * ks][2], s[u][2 * ks][3]),
-                          pack_f16(s[u][2 * ks + 1][0], s[u][2 * ks + 1][1]),
-                          pack_f16(s[u][2 * ks + 1][2], s[u][2 * ks + 1][3])};
+      for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pb = {pack_f16(s[2 * ks][0], s[2 * ks][1]), pack_f16(s[2 * ks][2], s[2 * ks][3]),
+                        pack_f16(s[2 * ks + 1][0], s[2 * ks + 1][1]), pack_f16(s[2 * ks + 1][2], s[2 * ks + 1][3])};
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const char* vrow = v_lds + (16 * mt + li) * kVRow + 2 * (32 * ks + 4 * g);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32);
-        const half8 a = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(a, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
+        const int d = 16 * mt + li;
+        const char* vrow = vt_lds + d * 128 + 8 * (g & 1);
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + (g >> 1)) ^ (d & 7)));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + 2 + (g >> 1)) ^ (d & 7)));
+        const half8 av = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb), o[mt]);
       }
+    }
   }
 
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (i_raw < T) {
+    const float inv = 1.f / l_run;
+    uint16_t* orow = out + ((int64_t)i_raw * H + h) * kDn + 4 * g;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    float l = l_run[u];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (i_raw[u] < T) {
-      const float inv = 1.f / l;
-      uint16_t* orow = out + ((int64_t)i_raw[u] * H + h) * kDn + 4 * g;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const uint32_t a = (uint32_t)f32_to_bf16_rne(o[u][mt][0] * inv) |
-                           ((uint32_t)f32_to_bf16_rne(o[u][mt][1] * inv) << 16);
-        const uint32_t b = (uint32_t)f32_to_bf16_rne(o[u][mt][2] * inv) |
-                           ((uint32_t)f32_to_bf16_rne(o[u][mt][3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
-      }
-      if (lse != nullptr && g == 0) lse[(int64_t)i_raw[u] * H + h] = (m_run[u] * scale_log2 + __log2f(l)) * 0.6931471805599453f;
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint32_t a = (uint32_t)f32_to_bf16_rne(o[mt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][1] * inv) << 16);
+      const uint32_t b = (uint32_t)f32_to_bf16_rne(o[mt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][3] * inv) << 16);
+      *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
     }
+    if (lse != nullptr && g == 0) lse[(int64_t)i_raw * H + h] = (m_run * scale_log2 + __log2f(l_run)) * 0.6931471805599453f;
   }
 }
 
