@@ -283,6 +283,25 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
 /* n_tokens * (576 + H * 192) * 4 bytes: the fp32 projection results.        */
 size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
 
+/* ------------------------------------------------------------------ residual
+ * mla_out_residual: close a layer whose attention output is per head (as
+ * mla_prefill_attn writes it): the output projection and the residual sum,
+ *   x_out[t] = x_in[t] + W_O . concat_h(attn_out[t][h])     (fp32 sums) -> bf16
+ * (W_O as in mla_out_proj; [Audit] §3.3 lists the output projection among a
+ * V2-Lite layer's weights).  Stacked layers pass x_out on as the next layer's
+ * hidden states.
+ *   attn_out   device [n_tokens][H][128] bf16
+ *   w_o        device [hidden][H*128] bf16
+ *   x_in       device [n_tokens][hidden] bf16
+ *   x_out      device [n_tokens][hidden] bf16, written; may be x_in
+ *   workspace  device f32, >= n_tokens * hidden * 4 bytes (given as
+ *              workspace_bytes; MLA_ERR_WORKSPACE if smaller)
+ * hidden > 0; n_tokens == 0 is a no-op.  W_O runs on the vector ALUs, one
+ * pass over its rows per 16 tokens: sized for decode steps and short chunks. */
+mla_status mla_out_residual(const mla_config* cfg, const uint16_t* attn_out, const uint16_t* w_o, int32_t hidden,
+                            const uint16_t* x_in, uint16_t* x_out, float* workspace, size_t workspace_bytes,
+                            int32_t n_tokens, hipStream_t stream);
+
 /* ------------------------------------------------------------------ prefill
  * mla_prefill_attn: causal attention of a chunk of T queries in the unabsorbed
  * form, the one engines use for prefill ([Tutorial] §四; the computation is

@@ -245,3 +245,17 @@ def prefill_attn(cfg: Config, q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, workspace, o
                                      _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"), Lq, _dev(w_uk, "w_uk"),
                                      _dev(w_uv, "w_uv"), _dev(workspace, "workspace"), ws_bytes, _dev(out, "out"),
                                      _dev(lse, "lse"), _stream()), "mla_prefill_attn")
+
+
+def out_residual(cfg: Config, attn_out, w_o, x_in, x_out, workspace) -> None:
+    """x_out = x_in + W_O . concat_h(attn_out) in bf16 (mla_out_residual)."""
+    T, H = int(attn_out.shape[0]), cfg.num_heads
+    hidden = int(w_o.shape[0])
+    _need(attn_out, "attn_out", (T, H, 128), 2)
+    _need(w_o, "w_o", (hidden, H * 128), 2)
+    _need(x_in, "x_in", (T, hidden), 2)
+    _need(x_out, "x_out", (T, hidden), 2)
+    ws_bytes = int(workspace.numel()) * int(workspace.element_size())
+    _check(L.load().mla_out_residual(C.byref(cfg), _dev(attn_out, "attn_out"), _dev(w_o, "w_o"), hidden,
+                                     _dev(x_in, "x_in"), _dev(x_out, "x_out"), _dev(workspace, "workspace"),
+                                     ws_bytes, T, _stream()), "mla_out_residual")

@@ -216,6 +216,21 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
                                           workspace, q_nope, q_pe, c_kv, k_pe, n_tokens, stream));
 }
 
+mla_status mla_out_residual(const mla_config* cfg, const uint16_t* attn_out, const uint16_t* w_o, int32_t hidden,
+                            const uint16_t* x_in, uint16_t* x_out, float* workspace, size_t workspace_bytes,
+                            int32_t n_tokens, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (n_tokens < 0 || hidden <= 0) return MLA_ERR_VALUE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!attn_out || !w_o || !x_in || !x_out || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(attn_out) || !aligned16(w_o) || !aligned16(workspace)) return MLA_ERR_ALIGN;
+  if (workspace_bytes < (size_t)n_tokens * (size_t)hidden * sizeof(float)) return MLA_ERR_WORKSPACE;
+  if ((s = check_device()) != MLA_OK) return s;
+  return launched(mla::launch_out_residual(cfg->num_heads, attn_out, w_o, hidden, x_in, x_out, workspace, n_tokens,
+                                           stream));
+}
+
 size_t mla_prefill_workspace_bytes(const mla_config* cfg, int32_t seq_len) {
   if (mla_config_check(cfg) != MLA_OK || seq_len < 0) return 0;
   return (size_t)cfg->num_heads * (size_t)mla::prefill_padded_len(seq_len) * 512u;

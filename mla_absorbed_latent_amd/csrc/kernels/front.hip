@@ -11,6 +11,9 @@
 // interleaved pairs (x[2i], x[2i+1]) rotated by pos * base^(-2i/64); every
 // output rounded once to bf16.
 //
+// launch_out_residual closes a layer: x += W_O . attention output, with the
+// same rowdot kernel for W_O and an elementwise residual kernel.
+//
 // Two kernels: rowdot (y[t][n] = sum_k W[n][k] x[t][k], bf16 in, fp32 sums;
 // weight-read-bound at the few tokens of a prefill or decode step, so it runs
 // on the vector ALUs with one wave per output feature), then front_finish (norm,
@@ -107,7 +110,28 @@ __global__ __launch_bounds__(64) void front_finish_kernel(const float* __restric
   }
 }
 
+// x_out[t][n] = bf16(x_in[t][n] + y[t][n]) (fp32 sum, round to nearest even);
+// x_out may be x_in.
+__global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x_in, const float* __restrict__ y,
+                                                       uint16_t* x_out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    x_out[i] = f32_to_bf16_rne(bf16_to_f32(x_in[i]) + y[i]);
+}
+
 }  // namespace
+
+hipError_t launch_out_residual(int num_heads, const uint16_t* attn_out, const uint16_t* w_o, int hidden,
+                               const uint16_t* x_in, uint16_t* x_out, float* workspace, int n_tokens,
+                               hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowdot_kernel, dim3((hidden + 3) / 4), dim3(256), 0, stream, attn_out, w_o, num_heads * kDn,
+                     hidden, n_tokens, workspace);
+  const int64_t n = (int64_t)n_tokens * hidden;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(residual_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, x_in,
+                     workspace, x_out, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q, const uint16_t* w_dkv,
                               const int32_t* positions, float rms_eps, float rope_base, float* workspace,

@@ -30,6 +30,10 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
                               uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
                               hipStream_t stream);
 
+hipError_t launch_out_residual(int num_heads, const uint16_t* attn_out, const uint16_t* w_o, int hidden,
+                               const uint16_t* x_in, uint16_t* x_out, float* workspace, int n_tokens,
+                               hipStream_t stream);
+
 // Workspace of launch_prefill_attn: K_nope [H][Lp][128] and V^T [H][128][Lp]
 // fp16, Lp = seq_len rounded up to 64.
 int64_t prefill_padded_len(int seq_len);

@@ -91,3 +91,34 @@ class DecodeRunner:
             self.combine()
             self.project(w_uv, w_o, y, out_f32)
         return self.out
+
+
+class PrefillLayer:
+    """One MLA layer over a chunk of T positions with no cached prefix, the way
+    a prompt is processed: mla_layer_front -> mla_prefill_attn ->
+    mla_out_residual, four C-ABI calls on the current stream.  Buffers are
+    allocated once here (torch), never inside the library."""
+
+    def __init__(self, cfg: api.Config, T: int, hidden: int, device="cuda:0"):
+        import torch
+        self.cfg, self.T, self.hidden = cfg, T, hidden
+        H = cfg.num_heads
+        dev = torch.device(device)
+        self.front_ws = torch.empty(api.layer_front_workspace_bytes(cfg, T) // 4, dtype=torch.float32, device=dev)
+        self.attn_ws = torch.empty(api.prefill_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+        self.res_ws = torch.empty(T * hidden, dtype=torch.float32, device=dev)
+        self.q_nope = torch.empty(T, H, 128, dtype=torch.bfloat16, device=dev)
+        self.q_pe = torch.empty(T, H, 64, dtype=torch.bfloat16, device=dev)
+        self.c_kv = torch.empty(T, 512, dtype=torch.bfloat16, device=dev)
+        self.k_pe = torch.empty(T, 64, dtype=torch.bfloat16, device=dev)
+        self.attn = torch.empty(T, H, 128, dtype=torch.bfloat16, device=dev)
+        self.positions = torch.arange(T, dtype=torch.int32, device=dev)
+
+    def forward(self, x, w_q, w_dkv, w_uk, w_uv, w_o, x_out, rms_eps=1e-6, rope_base=10000.0):
+        """x_out = x + W_O . attention(front(x)); x_out may be x.  c_kv / k_pe
+        keep the layer's latent rows (what a decode step would append)."""
+        api.layer_front(self.cfg, x, w_q, w_dkv, self.positions, self.front_ws, self.q_nope, self.q_pe,
+                        self.c_kv, self.k_pe, rms_eps, rope_base)
+        api.prefill_attn(self.cfg, self.q_nope, self.q_pe, self.c_kv, self.k_pe, w_uk, w_uv, self.attn_ws, self.attn)
+        api.out_residual(self.cfg, self.attn, w_o, x, x_out, self.res_ws)
+        return x_out
