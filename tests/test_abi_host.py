@@ -206,3 +206,19 @@ def test_prefill_validation(lib):
     assert call(lse=odd) == L.MLA_ERR_ALIGN
     assert call(wsb=ws - 1) == L.MLA_ERR_WORKSPACE
     assert call(T=0, q=None) == L.MLA_OK                 # no-op
+
+
+def test_out_residual_validation(lib):
+    cfg = api.config(16)
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    f = lib.mla_out_residual
+
+    def call(attn=fake, hidden=2048, ws=64 * 2048 * 4, n=64, x=fake):
+        return f(C.byref(cfg), attn, fake, hidden, x, x, fake, ws, n, None)
+
+    assert call(hidden=0) == L.MLA_ERR_VALUE
+    assert call(n=-1) == L.MLA_ERR_VALUE
+    assert call(attn=None) == L.MLA_ERR_NULL
+    assert call(attn=odd) == L.MLA_ERR_ALIGN
+    assert call(ws=64 * 2048 * 4 - 1) == L.MLA_ERR_WORKSPACE
+    assert call(attn=None, x=None, n=0) == L.MLA_OK
