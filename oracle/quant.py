@@ -27,6 +27,13 @@ by itself, so append can be done token by token) are:
       q = clamp(rint(x / scale), -7, 7);  amax == 0 -> scale 0, q 0
       stored as the nibble q + 8 (1..15), same byte order as INT4
       dequant: (nibble - 8) * scale (float32, one rounding)
+  FP8 per token (e4m3; a cache format the pages name but do not specify):
+      amax = max |x| over the token's 512 latent channels (8 for each RoPE-key
+      group), scale = amax / 448 (float32; 448 is the largest e4m3 value)
+      code = e4m3(x / scale): round to nearest, ties to even, onto the e4m3
+      grid (bias 7, 3 mantissa bits, subnormal step 2^-9, no infinities),
+      saturating at +-448; the sign bit is the sign bit of x / scale
+      amax == 0 -> scale 0, codes 0;  dequant: value(code) * scale (float32)
 
 Every step is evaluated in numpy float32 with float32 constants, so the codes and
 scales are defined bit for bit; the GPU's quantise-on-append must reproduce them
@@ -42,12 +49,16 @@ Page layouts (64 tokens a page, bytes):
   int4s: as int4 without the zeros                                    26,624
   int8t: [64][576] int8 codes | [64] f32 latent scales
          | [64][8] f32 RoPE-key scales                                 39,168
+  fp8t : as int8t with e4m3 codes                                     39,168
 
 Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
 INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
 unclamped element is at most half a step; zero groups round-trip exactly;
 the rounding rule is checked on hand-made ties; page bytes round-trip through
-unpack_page; a symmetric INT4 group's absmax element maps to nibble 8 +- 7.  The
+unpack_page; a symmetric INT4 group's absmax element maps to nibble 8 +- 7;
+the e4m3 encoder agrees with torch's float8_e4m3fn conversion, returns every
+one of the 254 finite codes from its own value, rounds hand-made midpoints to
+the even code, and maps a group's absmax element to +-448.  The
 page's own error figures need the real latents and are not reproduced ("parity
 unpinned" for those numbers).
 """
@@ -61,7 +72,8 @@ D_R = 64
 G_C = 32      # latent channels per group
 G_R = 8       # RoPE-key channels per group
 
-CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK = 0, 1, 2, 3, 4
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK = 0, 1, 2, 3, 4, 5
+_F448 = np.float32(448.0)
 _F127 = np.float32(127.0)
 _F15 = np.float32(15.0)
 _F7 = np.float32(7.0)
@@ -92,6 +104,47 @@ def dequant_int8(codes: np.ndarray, scales: np.ndarray, group: int) -> np.ndarra
     shp = codes.shape
     cg = codes.astype(np.float32).reshape(shp[:-1] + (shp[-1] // group, group))
     return (cg * scales[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
+
+
+def fp8_e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """float32 -> e4m3 code bytes: nearest grid value (ties to even), saturating at 448."""
+    y = np.asarray(y, np.float32)
+    a = np.abs(y)
+    _, k = np.frexp(a)                                       # a = f 2^k, 0.5 <= f < 1
+    e = np.maximum(k.astype(np.int32) - 1, -6)               # 2^e <= a < 2^(e+1) for normals
+    sub = a < np.float32(2.0 ** -6)
+    q_sub = np.rint(a * np.float32(512.0))                   # multiples of 2^-9 (exact scaling)
+    q_nrm = np.rint(np.ldexp(a, 3 - e).astype(np.float32))   # 8..16: 1.mmm in units of 1/8
+    code = np.where(sub, q_sub, (e + 7) * 8 + (q_nrm - 8))   # q = 16 carries into the exponent
+    code = np.minimum(code, 126).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, np.uint8).astype(np.int32)
+    E, M = (c >> 3) & 15, c & 7
+    v = np.where(E == 0, M * np.float32(2.0 ** -9),
+                 np.ldexp(np.float32(1.0) + M.astype(np.float32) / np.float32(8.0), E - 7)).astype(np.float32)
+    return np.where(c >> 7 == 1, -v, v).astype(np.float32)
+
+
+def quant_fp8(x_bits: np.ndarray, group: int):
+    """e4m3 codes per group of `group` channels with scale = amax / 448."""
+    x = _bf16_to_f32(x_bits)
+    shp = x.shape
+    xg = x.reshape(shp[:-1] + (shp[-1] // group, group))
+    amax = np.max(np.abs(xg), axis=-1)
+    scale = (amax / _F448).astype(np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    codes = fp8_e4m3_encode((xg / safe[..., None]).astype(np.float32))
+    codes = np.where(scale[..., None] == 0, np.uint8(0), codes).astype(np.uint8)
+    return codes.reshape(shp), scale
+
+
+def dequant_fp8(codes: np.ndarray, scales: np.ndarray, group: int) -> np.ndarray:
+    shp = codes.shape
+    v = fp8_e4m3_decode(codes).reshape(shp[:-1] + (shp[-1] // group, group))
+    return (v * scales[..., None].astype(np.float32)).astype(np.float32).reshape(shp)
 
 
 def quant_int4_asym(x_bits: np.ndarray, group: int = G_C):
@@ -157,7 +210,8 @@ def token_bytes(dtype: int) -> int:
             CACHE_INT8: 576 + (D_C // G_C) * 4 + (D_R // G_R) * 4,
             CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4,
             CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4,
-            CACHE_INT8_TOK: 576 + 4 + (D_R // G_R) * 4}[dtype]
+            CACHE_INT8_TOK: 576 + 4 + (D_R // G_R) * 4,
+            CACHE_FP8_TOK: 576 + 4 + (D_R // G_R) * 4}[dtype]
 
 
 def page_bytes(dtype: int) -> int:
@@ -168,6 +222,10 @@ def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
     """Quantise (or copy) n token rows into their per-field arrays."""
     if dtype == CACHE_BF16:
         return {"rows": np.concatenate([c_bits, r_bits], axis=-1).astype(np.uint16)}
+    if dtype == CACHE_FP8_TOK:
+        cc, cs = quant_fp8(c_bits, D_C)
+        rc, rs = quant_fp8(r_bits, G_R)
+        return {"codes": np.concatenate([cc, rc], axis=-1), "c_scale": cs, "r_scale": rs}
     rc, rs = quant_int8_sym(r_bits, G_R)
     if dtype in (CACHE_INT8, CACHE_INT8_TOK):
         cc, cs = quant_int8_sym(c_bits, G_C if dtype == CACHE_INT8 else D_C)
@@ -193,7 +251,7 @@ def pack_page(dtype: int, fields: dict) -> np.ndarray:
 
     if dtype == CACHE_BF16:
         put(0, fields["rows"], 1152)
-    elif dtype in (CACHE_INT8, CACHE_INT8_TOK):
+    elif dtype in (CACHE_INT8, CACHE_INT8_TOK, CACHE_FP8_TOK):
         off = put(0, fields["codes"], 576)
         off = put(off, fields["c_scale"], 64 if dtype == CACHE_INT8 else 4)
         put(off, fields["r_scale"], 32)
@@ -218,8 +276,8 @@ def unpack_page(dtype: int, page: np.ndarray) -> dict:
     if dtype == CACHE_BF16:
         rows, _ = get(0, 1152, np.uint16, 576)
         return {"rows": rows}
-    if dtype in (CACHE_INT8, CACHE_INT8_TOK):
-        codes, off = get(0, 576, np.int8, 576)
+    if dtype in (CACHE_INT8, CACHE_INT8_TOK, CACHE_FP8_TOK):
+        codes, off = get(0, 576, np.uint8 if dtype == CACHE_FP8_TOK else np.int8, 576)
         cs, off = get(off, 64, np.float32, 16) if dtype == CACHE_INT8 else get(off, 4, np.float32, 1)
         rs, _ = get(off, 32, np.float32, 8)
         return {"codes": codes, "c_scale": cs, "r_scale": rs}
@@ -239,6 +297,8 @@ def dequant_fields(dtype: int, f: dict):
     if dtype == CACHE_BF16:
         rows = _bf16_to_f32(f["rows"])
         return rows[..., :D_C], rows[..., D_C:]
+    if dtype == CACHE_FP8_TOK:
+        return dequant_fp8(f["codes"][..., :D_C], f["c_scale"], D_C), dequant_fp8(f["codes"][..., D_C:], f["r_scale"], G_R)
     if dtype in (CACHE_INT8, CACHE_INT8_TOK):
         c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C if dtype == CACHE_INT8 else D_C)
         r = dequant_int8(f["codes"][..., D_C:], f["r_scale"], G_R)

@@ -139,7 +139,8 @@ def test_token_and_page_bytes():
     assert quant.token_bytes(quant.CACHE_INT4) == 256 + 64 + 16 * 4 * 2 + 8 * 4 == 480
     assert quant.token_bytes(quant.CACHE_INT4_SYM) == 256 + 64 + 16 * 4 + 8 * 4 == 416
     assert quant.token_bytes(quant.CACHE_INT8_TOK) == 512 + 64 + 4 + 8 * 4 == 612
-    assert [quant.page_bytes(d) for d in (0, 1, 2, 3, 4)] == [73728, 43008, 30720, 26624, 39168]
+    assert quant.token_bytes(quant.CACHE_FP8_TOK) == 612
+    assert [quant.page_bytes(d) for d in (0, 1, 2, 3, 4, 5)] == [73728, 43008, 30720, 26624, 39168, 39168]
 
 
 def test_int8_per_token_one_scale_for_the_latent():
@@ -155,7 +156,7 @@ def test_int8_per_token_one_scale_for_the_latent():
     assert np.all(np.abs(f["codes"][:, :512]).max(-1) == 127)
 
 
-@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4, 5])
 def test_page_roundtrip(dtype):
     rng = np.random.default_rng(3 + dtype)
     c = _draw(rng, (50, 512))
@@ -175,7 +176,7 @@ def test_pool_dequant_matches_field_dequant():
     c = _draw(rng, (L, 512))
     r = _draw(rng, (L, 64))
     bt = np.array([5, 0, 3])
-    for dt in (0, 1, 2, 3, 4):
+    for dt in (0, 1, 2, 3, 4, 5):
         pool = quant.pack_pool(dt, 6, [(c, r, bt)])
         cc, rr = quant.dequant_pool_seq(dt, pool, bt, L)
         f = quant.encode_tokens(dt, c, r)
@@ -201,3 +202,51 @@ def test_quant_error_scale_on_outlier_data():
     e4 = np.abs(quant.dequant_int4(q4, s4, z4, 32) - xf).mean() / np.abs(xf).mean()
     assert 3e-3 < e8 < 3e-2
     assert 3e-2 < e4 < 3e-1
+
+
+# ------------------------------------------------------------------ FP8 (e4m3) per token
+def test_fp8_encoder_matches_torch_float8_e4m3fn():
+    """Round to nearest even onto the e4m3 grid is what torch's float8_e4m3fn
+    conversion does for values within +-448 (a library routine, independent of
+    the oracle)."""
+    import torch
+    rng = np.random.default_rng(11)
+    y = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+                        rng.standard_normal(20000) * 1e-3, [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -6]])
+    y = y.astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(quant.fp8_e4m3_encode(y), ref)
+
+
+def test_fp8_every_finite_code_round_trips_and_values_are_the_e4m3_grid():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)       # 254 finite codes
+    v = quant.fp8_e4m3_decode(codes)
+    assert np.array_equal(quant.fp8_e4m3_encode(v), codes)
+    pos = np.sort(v[(codes < 0x80)])
+    assert pos[0] == 0 and pos[1] == 2.0 ** -9 and pos[8] == 2.0 ** -6 and pos[-1] == 448.0
+    assert v[codes == 0x38][0] == 1.0 and v[codes == 0x39][0] == 1.125        # 2^0 (1 + m/8)
+
+
+def test_fp8_ties_to_even_and_saturation():
+    mids = np.array([1.0625, 1.1875, 2.0 ** -9 * 1.5, 2.0 ** -9 * 2.5, 464.0, 500.0, -1.0625], np.float32)
+    got = quant.fp8_e4m3_decode(quant.fp8_e4m3_encode(mids))
+    assert list(got) == [1.0, 1.25, 2.0 ** -9 * 2, 2.0 ** -9 * 2, 448.0, 448.0, -1.0]
+
+
+def test_fp8_per_token_absmax_to_448_and_error_within_half_step():
+    rng = np.random.default_rng(12)
+    c, r = _draw(rng, (30, 512)), _draw(rng, (30, 64))
+    f = quant.encode_tokens(quant.CACHE_FP8_TOK, c, r)
+    x = bf16_bits_to_f32(c)
+    s = f["c_scale"][:, 0]
+    assert np.array_equal(s, (np.abs(x).max(-1) / np.float32(448)).astype(np.float32))
+    assert np.all((f["codes"][:, :512] & 0x7F).max(-1) == 0x7E)                  # +-448
+    deq, _ = quant.dequant_fields(quant.CACHE_FP8_TOK, f)
+    y = np.abs(x / s[:, None])
+    err = np.abs(deq / s[:, None] - x / s[:, None])
+    normal = y >= 2.0 ** -6
+    assert np.all(err[normal] <= y[normal] * 2.0 ** -4 * (1 + 1e-6))            # half of a 3-bit step
+    assert np.all(err[~normal] <= 2.0 ** -10 * (1 + 1e-6))
+    z = np.zeros((1, 512), np.uint16)
+    fz = quant.encode_tokens(quant.CACHE_FP8_TOK, z, np.zeros((1, 64), np.uint16))
+    assert fz["c_scale"][0, 0] == 0 and not fz["codes"].any()
