@@ -54,14 +54,17 @@ typedef enum {
   MLA_ERR_HIP = 7          /* a HIP call or launch failed                         */
 } mla_status;
 
-/* Latent-cache formats ([Report] §3.2 and §4.1; the symmetric INT4 and the
- * per-token INT8 variants are not ones the report measures). */
+/* Latent-cache formats ([Report] §3.2 and §4.1; the symmetric INT4, the
+ * per-token INT8 and the FP8 variants are not ones the report measures; FP8
+ * latent caches are named in [Audit] §6.1 and [Tutorial] §六 without a scaling
+ * rule). */
 typedef enum {
   MLA_CACHE_BF16 = 0,     /* c_kv and k_pe in bf16                                       */
   MLA_CACHE_INT8 = 1,     /* c_kv INT8, one fp32 scale per 32 channels; k_pe INT8 per 8   */
   MLA_CACHE_INT4 = 2,     /* c_kv asymmetric INT4, fp32 scale + zero per 32; k_pe INT8    */
   MLA_CACHE_INT4_SYM = 3, /* c_kv symmetric INT4, fp32 scale per 32; k_pe INT8            */
-  MLA_CACHE_INT8_TOK = 4  /* c_kv INT8, one fp32 scale per token; k_pe INT8 per 8         */
+  MLA_CACHE_INT8_TOK = 4, /* c_kv INT8, one fp32 scale per token; k_pe INT8 per 8         */
+  MLA_CACHE_FP8_TOK = 5   /* c_kv e4m3 FP8, one fp32 scale per token; k_pe e4m3 per 8     */
 } mla_cache_dtype;
 
 /* Shape of one MLA layer.  Supported: num_heads in {16, 128}, qk_nope_dim = 128,
@@ -105,6 +108,7 @@ typedef struct {
  *                                                                     (26,624 B)
  *   INT8_TOK: [64][576] int8 codes | [64] f32 latent scales
  *         | [64][8] f32 RoPE-key scales                               (39,168 B)
+ *   FP8_TOK: as INT8_TOK with e4m3 codes                              (39,168 B)
  * A pool of N pages is N * mla_cache_page_bytes() contiguous bytes.          */
 mla_status mla_config_check(const mla_config* cfg);
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
@@ -127,6 +131,11 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
  * INT4: per group of 32 latent channels, zero = min, scale = (max-min)/15,
  *   q = clamp(rint((x-min)/scale), 0, 15); scale 0 gives q = 0.
  * INT8_TOK: as INT8 with one group of all 512 latent channels.
+ * FP8_TOK: per token, scale = max|x| / 448 over the 512 latent channels (and
+ *   over each 8-channel RoPE-key group); code = x / scale rounded to the
+ *   nearest e4m3 value (OCP E4M3: bias 7, 3 mantissa bits, subnormals, no
+ *   infinities), ties to even, saturating at +-448, sign bit of x / scale;
+ *   max|x| = 0 gives scale 0 and codes 0.
  * INT4_SYM: per group of 32 latent channels, scale = max|x| / 7,
  *   q = clamp(rint(x/scale), -7, 7), stored as q + 8; max|x| = 0 gives scale 0
  *   and q = 0.  The RoPE key of both INT4 formats is INT8 as above.

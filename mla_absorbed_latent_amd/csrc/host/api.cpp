@@ -55,7 +55,7 @@ mla_status mla_config_check(const mla_config* cfg) {
   if (cfg->qk_nope_dim != 128 || cfg->kv_lora_rank != 512 || cfg->rope_dim != 64 || cfg->v_head_dim != 128 ||
       cfg->block_size != 64)
     return MLA_ERR_SHAPE;
-  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_INT8_TOK) return MLA_ERR_VALUE;
+  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_FP8_TOK) return MLA_ERR_VALUE;
   if (!(cfg->softmax_scale > 0.f) || !std::isfinite(cfg->softmax_scale)) return MLA_ERR_VALUE;
   return MLA_OK;
 }

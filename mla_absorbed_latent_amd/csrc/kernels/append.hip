@@ -71,6 +71,40 @@ __device__ __forceinline__ float quant_sym8(const uint16_t* x, int8_t* codes) {
   return scale;
 }
 
+// e4m3 code of a finite y with |y| <= 448 (up to float rounding): nearest value
+// of the e4m3 grid (bias 7, 3 mantissa bits, subnormal step 2^-9), ties to even,
+// saturating at 448; the sign bit is y's.  Scaling by powers of two is exact, so
+// rintf does the rounding: below 2^-6 in steps of 2^-9, above it in steps of
+// 2^(e-3) with q = 1.mmm in eighths (q = 16 carries into the exponent field).
+__device__ __forceinline__ uint8_t fp8_e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  int code;
+  if (a < 0.015625f) {
+    code = (int)rintf(a * 512.0f);
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    code = (e + 7) * 8 + (int)rintf(ldexpf(a, 3 - e)) - 8;
+  }
+  return (uint8_t)(min(code, 126) | (int)sign);
+}
+
+// e4m3 codes of `kG` consecutive bf16 values with scale = amax / 448.
+template <int kG>
+__device__ __forceinline__ float quant_fp8(const uint16_t* x, uint8_t* codes) {
+  float v[kG];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    v[i] = bf16_to_f32(x[i]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const float scale = __fdiv_rn(amax, 448.0f);
+#pragma unroll
+  for (int i = 0; i < kG; ++i) codes[i] = scale != 0.f ? fp8_e4m3_code(__fdiv_rn(v[i], scale)) : (uint8_t)0;
+  return scale;
+}
+
 // 24 groups a token: 16 latent groups of 32, then 8 RoPE-key groups of 8.
 __global__ __launch_bounds__(256) void append_int8(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
                                                    const uint16_t* k_pe, const int64_t* slots, int n) {
@@ -247,6 +281,41 @@ __global__ __launch_bounds__(256) void append_int8t(uint8_t* pool, int64_t num_p
   }
 }
 
+// FP8 per token: the layout of append_int8t with e4m3 codes and scale = amax / 448.
+__global__ __launch_bounds__(256) void append_fp8t(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                   const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // uniform per wave
+  const int lane = threadIdx.x & 63;
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * kPageInt8Tok;
+  const int off = (int)(slot % kBlock);
+  const uint16_t* x = c_kv + tok * kDc + 8 * lane;
+  float v[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = bf16_to_f32(x[i]);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const float scale = __fdiv_rn(amax, 448.0f);
+  uint8_t* dst = page + off * 576 + 8 * lane;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = scale != 0.f ? fp8_e4m3_code(__fdiv_rn(v[i], scale)) : (uint8_t)0;
+  if (lane == 0) reinterpret_cast<float*>(page + 64 * 576)[off] = scale;
+  if (lane < 8) {
+    uint8_t rc[8];
+    const float s = quant_fp8<8>(k_pe + tok * kDr + lane * 8, rc);
+    uint8_t* rdst = page + off * 576 + 512 + lane * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rdst[i] = rc[i];
+    reinterpret_cast<float*>(page + 64 * 576 + 64 * 4)[off * 8 + lane] = s;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
@@ -257,10 +326,10 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
     const int64_t work = (int64_t)n * 72;
     hipLaunchKernelGGL(append_bf16, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
                        c_kv, k_pe, slots, n);
-  } else if (cache_dtype == 4) {
+  } else if (cache_dtype == 4 || cache_dtype == 5) {
     const int64_t work = (int64_t)n * 64;                  // one wave a token
-    hipLaunchKernelGGL(append_int8t, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
-                       c_kv, k_pe, slots, n);
+    hipLaunchKernelGGL(cache_dtype == 4 ? append_int8t : append_fp8t, dim3((unsigned)((work + 255) / 256)),
+                       dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
   } else {
     const int64_t work = (int64_t)n * 24;
     const dim3 grid((unsigned)((work + 255) / 256));

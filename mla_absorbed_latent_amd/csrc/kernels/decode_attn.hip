@@ -227,10 +227,43 @@ __device__ __forceinline__ u32x2 int8x4_to_f16_perm(uint32_t c, half2v s) {
                __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, h1) + bias) * s)};
 }
 
+// Four e4m3 codes -> four fp16 values value(code) * s256 / 256.  Placing byte b in
+// bits 8-15 of a 16-bit lane and shifting its low seven bits down by one gives
+// (b & 0x7f) << 7 | (b & 0x80) << 8: sign, exponent and mantissa fields line up
+// with fp16's, and with the exponent biases 7 and 15 that bit pattern is the fp16
+// number value(b) * 2^-8, exactly, subnormals included.  s256 is the scale times
+// 256.
+__device__ __forceinline__ uint32_t fp8x2_f16_bits(uint32_t t) {
+  return ((t >> 1) & 0x3f803f80u) | (t & 0x80008000u);
+}
+__device__ __forceinline__ u32x2 fp8x4_to_f16(uint32_t c, half2v s256) {
+  const uint32_t t0 = __builtin_amdgcn_perm(0u, c, 0x010c000cu);   // (0, b0, 0, b1)
+  const uint32_t t1 = __builtin_amdgcn_perm(0u, c, 0x030c020cu);   // (0, b2, 0, b3)
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, fp8x2_f16_bits(t0)) * s256),
+               __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, fp8x2_f16_bits(t1)) * s256)};
+}
+// Codes of the byte-coded formats -> fp16 (kFp8: e4m3, else int8), and the fp16
+// factor their scale s becomes.
+template <bool kFp8>
+__device__ __forceinline__ u32x2 codes4_to_f16(uint32_t c, half2v s) {
+  if constexpr (kFp8) return fp8x4_to_f16(c, s);
+  else return int8x4_to_f16(c, s);
+}
+template <bool kFp8>
+__device__ __forceinline__ u32x2 codes4_to_f16_perm(uint32_t c, half2v s) {
+  if constexpr (kFp8) return fp8x4_to_f16(c, s);
+  else return int8x4_to_f16_perm(c, s);
+}
+template <bool kFp8>
+__device__ __forceinline__ _Float16 code_scale_h(float s) {
+  return (_Float16)(kFp8 ? s * 256.f : s);
+}
+
 // INT8 page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key scales.
 // Per-token INT8 (kTok1): [64][576] codes | [64] f32 latent scales | [64][8] f32
 // key scales; every latent chunk of a token takes the token's one scale.
-template <int kTok, int kSwz, int kTid0 = 0, bool kTok1 = false>
+// FP8 per token (kFp8, with kTok1): the same page with e4m3 codes.
+template <int kTok, int kSwz, int kTid0 = 0, bool kTok1 = false, bool kFp8 = false>
 struct LoaderInt8Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 3;
@@ -289,12 +322,12 @@ struct LoaderInt8Reg {
   template <int I>
   __device__ __forceinline__ void store_step(char* lds_buf) {
     constexpr int kc = I / 2, p = kc / 9, k = kc % 9;
-    const _Float16 sh = (_Float16)s[kc];
+    const _Float16 sh = code_scale_h<kFp8>(s[kc]);
     const half2v s2 = {sh, sh};
     if constexpr (I % 2 == 0) {
-      part = int8x4_to_f16(c[kc][0], s2);
+      part = codes4_to_f16<kFp8>(c[kc][0], s2);
     } else {
-      const u32x2 hi = int8x4_to_f16(c[kc][1], s2);
+      const u32x2 hi = codes4_to_f16<kFp8>(c[kc][1], s2);
       *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(ltid<kTid0>() >> 3, ltid<kTid0>() & 7) + 32 * p * kRowLds + 128 * k) =
           u32x4{part[0], part[1], hi[0], hi[1]};
     }
@@ -306,9 +339,9 @@ struct LoaderInt8Reg {
     for (int p = 0; p < kPass; ++p)
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
-        const _Float16 sh = (_Float16)s[9 * p + k];
+        const _Float16 sh = code_scale_h<kFp8>(s[9 * p + k]);
         const half2v s2 = {sh, sh};
-        const u32x2 lo = int8x4_to_f16(c[9 * p + k][0], s2), hi = int8x4_to_f16(c[9 * p + k][1], s2);
+        const u32x2 lo = codes4_to_f16<kFp8>(c[9 * p + k][0], s2), hi = codes4_to_f16<kFp8>(c[9 * p + k][1], s2);
         *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
   }
@@ -594,8 +627,9 @@ struct LoaderBf16Wide {
 // scales as four 16-byte pieces and pass them round by DPP: one load instead of
 // eight 4-byte ones, since load instructions, not bytes, pace the staging.
 // Per-token INT8 (kTok1): the token's one latent scale is a single 4-byte load
-// (every thread of the token loads it), no DPP.
-template <int kSwz, int kTid0, bool kTok1 = false>
+// (every thread of the token loads it), no DPP.  FP8 per token (kFp8, with
+// kTok1): the same page with e4m3 codes.
+template <int kSwz, int kTid0, bool kTok1 = false, bool kFp8 = false>
 struct LoaderInt8Wide {
   static constexpr int kPage = kBlock * (kTok1 ? 612 : 672);
   static constexpr int kLoads = 11;      // load instructions per tile
@@ -648,9 +682,9 @@ struct LoaderInt8Wide {
       f0 = ks[0];
       f1 = ks[1];
     }
-    const _Float16 s0 = (_Float16)f0, s1 = (_Float16)f1;
-    const u32x2 a0 = int8x4_to_f16_perm(c[I][0], half2v{s0, s0}), a1 = int8x4_to_f16_perm(c[I][1], half2v{s0, s0});
-    const u32x2 b0 = int8x4_to_f16_perm(c[I][2], half2v{s1, s1}), b1 = int8x4_to_f16_perm(c[I][3], half2v{s1, s1});
+    const _Float16 s0 = code_scale_h<kFp8>(f0), s1 = code_scale_h<kFp8>(f1);
+    const u32x2 a0 = codes4_to_f16_perm<kFp8>(c[I][0], half2v{s0, s0}), a1 = codes4_to_f16_perm<kFp8>(c[I][1], half2v{s0, s0});
+    const u32x2 b0 = codes4_to_f16_perm<kFp8>(c[I][2], half2v{s1, s1}), b1 = codes4_to_f16_perm<kFp8>(c[I][3], half2v{s1, s1});
     *reinterpret_cast<u32x4*>(d0 + 128 * I) = u32x4{a0[0], a0[1], a1[0], a1[1]};
     *reinterpret_cast<u32x4*>(d1 + 128 * I) = u32x4{b0[0], b0[1], b1[0], b1[1]};
   }
@@ -1066,7 +1100,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
 
   using Loader = typename std::conditional<
       kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
-      typename std::conditional<kCache == 1 || kCache == 4, LoaderInt8Reg<kTile128, kSwz128, 0, kCache == 4>,
+      typename std::conditional<kCache == 1 || kCache >= 4, LoaderInt8Reg<kTile128, kSwz128, 0, kCache >= 4, kCache == 5>,
                                 LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3>>::type>::type;
   h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
                          overflow);
@@ -1431,6 +1465,7 @@ using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
 using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
 using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
 using H16Int8Tok = LoaderInt8Wide<kSwz16, 256, true>;
+using H16Fp8Tok = LoaderInt8Wide<kSwz16, 256, true, true>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
@@ -1441,6 +1476,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h128<3>, grid, block, 0, stream, a);
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h128<4>, grid, block, 0, stream, a);
+    else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h128<5>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
     const dim3 block16(512);                       // 4 compute + 4 staging waves
@@ -1449,6 +1485,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block16, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h16<H16Int4Sym>, grid, block16, 0, stream, a);
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h16<H16Int8Tok>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h16<H16Fp8Tok>, grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
