@@ -268,7 +268,8 @@ mla_status mla_decode_combine_out_proj(const mla_config* cfg, const uint16_t* o_
  *   k_pe[t] = RoPE(kv[t][512:576], positions[t])
  *   q_nope[t][h] = q[t][h][0:128],  q_pe[t][h] = RoPE(q[t][h][128:192], positions[t])
  * RoPE rotates the pairs (v[2i], v[2i+1]) by positions[t] * rope_base^(-2i/64).
- * Projections accumulate bf16 products in fp32; the norm and the rotation run
+ * Projections accumulate bf16 products in fp32 (on the matrix cores for 64
+ * tokens or more with hidden a multiple of 64); the norm and the rotation run
  * in double precision; each output is rounded once to bf16 (round to nearest
  * even).
  *   x          device [n_tokens][hidden] bf16; hidden a positive multiple of 8
@@ -305,8 +306,9 @@ size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
  *   x_out      device [n_tokens][hidden] bf16, written; may be x_in
  *   workspace  device f32, >= n_tokens * hidden * 4 bytes (given as
  *              workspace_bytes; MLA_ERR_WORKSPACE if smaller)
- * hidden > 0; n_tokens == 0 is a no-op.  W_O runs on the vector ALUs, one
- * pass over its rows per 16 tokens: sized for decode steps and short chunks. */
+ * hidden > 0; n_tokens == 0 is a no-op.  W_O runs on the matrix cores for
+ * 64 tokens or more, else on the vector ALUs (one pass over its rows per 16
+ * tokens); the sums are fp32 either way.                                     */
 mla_status mla_out_residual(const mla_config* cfg, const uint16_t* attn_out, const uint16_t* w_o, int32_t hidden,
                             const uint16_t* x_in, uint16_t* x_out, float* workspace, size_t workspace_bytes,
                             int32_t n_tokens, hipStream_t stream);

@@ -14,10 +14,12 @@
 // launch_out_residual closes a layer: x += W_O . attention output, with the
 // same rowdot kernel for W_O and an elementwise residual kernel.
 //
-// Two kernels: rowdot (y[t][n] = sum_k W[n][k] x[t][k], bf16 in, fp32 sums;
-// weight-read-bound at the few tokens of a prefill or decode step, so it runs
-// on the vector ALUs with one wave per output feature), then front_finish (norm,
-// rotation, bf16 rounding; the norm and the angles in double precision).
+// The projections y[t][n] = sum_k W[n][k] x[t][k] (bf16 in, fp32 sums) take one
+// of two kernels: rowdot for a few tokens (a decode step: weight-read-bound, on
+// the vector ALUs with one wave per output feature) and gemm_nt for chunks of
+// 64 tokens or more (a prompt: compute-bound, on the matrix cores); then
+// front_finish applies the norm, the rotation and the bf16 rounding (the norm
+// and the angles in double precision).
 #include "common.h"
 #include "kernels.h"
 
@@ -64,6 +66,103 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
       if (lane == 0 && t0 + i < T) y[(int64_t)(t0 + i) * N + n] = v;
     }
   }
+}
+
+// y[t][n] = sum_k x[t][k] w[n][k] on the matrix cores, for chunks of many
+// tokens: a work-group computes 128 tokens x 128 features from 64-channel
+// chunks of both operands staged in LDS (double-buffered, 16-byte chunk c of
+// row r at c ^ (r & 7)); wave (wm, wn) holds 64 x 64 of the result as 4 x 4
+// tiles of v_mfma_f32_16x16x32_bf16.  K a multiple of 64; rows past T or N
+// read as zero and are not stored.
+constexpr int kGT = 128;
+constexpr int kGChunk = 64;
+constexpr int kGRow = kGChunk * 2;               // 128 B
+constexpr int kGBuf = 2 * kGT * kGRow;           // 32 KB
+
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                      int K, int N, int T, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kGBuf];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
+  u32x4 st[8];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+      const int k = kc * kGChunk + 8 * ch;
+      if (row < kGT) {
+        const int t = t0 + row;
+        st[i] = t < T ? ld16(x + (int64_t)t * K + k) : u32x4{0, 0, 0, 0};
+      } else {
+        const int n = n0 + row - kGT;
+        st[i] = n < N ? ld16(w + (int64_t)n * K + k) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(lds + buf * kGBuf + row * kGRow + 16 * (ch ^ (row & 7))) = st[i];
+    }
+  };
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int n_chunks = K / kGChunk;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < n_chunks; ++kc) {
+    if (kc + 1 < n_chunks) load(kc + 1);
+    const char* buf = lds + (kc & 1) * kGBuf;
+#pragma unroll
+    for (int ks = 0; ks < kGChunk / 32; ++ks) {
+      u32x4 xf[4], wf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int xr = 64 * wm + 16 * i + li, wr = kGT + 64 * wn + 16 * i + li;
+        xf[i] = *reinterpret_cast<const u32x4*>(buf + xr * kGRow + 16 * ((4 * ks + g) ^ (xr & 7)));
+        wf[i] = *reinterpret_cast<const u32x4*>(buf + wr * kGRow + 16 * ((4 * ks + g) ^ (wr & 7)));
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[a]),
+                                                              __builtin_bit_cast(bf16x8, wf[b]), acc[a][b], 0, 0, 0);
+    }
+    if (kc + 1 < n_chunks) {
+      store((kc + 1) & 1);
+      __syncthreads();
+    }
+  }
+  // D[token 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = n0 + 64 * wn + 16 * b + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 64 * wm + 16 * a + 4 * g + r;
+        if (t < T && n < N) y[(int64_t)t * N + n] = acc[a][b][r];
+      }
+    }
+}
+
+// y = x . w^T through the matrix-core tiles for chunks of 64 tokens or more
+// (K a multiple of 64), else through rowdot.
+void project(const uint16_t* x, const uint16_t* w, int K, int N, int T, float* y, hipStream_t stream) {
+  if (T >= 64 && K % kGChunk == 0)
+    hipLaunchKernelGGL(gemm_nt_kernel, dim3((N + kGT - 1) / kGT, (T + kGT - 1) / kGT), dim3(256), 0, stream, x, w,
+                       K, N, T, y);
+  else
+    hipLaunchKernelGGL(rowdot_kernel, dim3((N + 3) / 4), dim3(256), 0, stream, x, w, K, N, T, y);
 }
 
 __device__ __forceinline__ uint16_t bf16_of(double v) { return f32_to_bf16_rne((float)v); }
@@ -124,8 +223,7 @@ hipError_t launch_out_residual(int num_heads, const uint16_t* attn_out, const ui
                                const uint16_t* x_in, uint16_t* x_out, float* workspace, int n_tokens,
                                hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowdot_kernel, dim3((hidden + 3) / 4), dim3(256), 0, stream, attn_out, w_o, num_heads * kDn,
-                     hidden, n_tokens, workspace);
+  project(attn_out, w_o, num_heads * kDn, hidden, n_tokens, workspace, stream);
   const int64_t n = (int64_t)n_tokens * hidden;
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(residual_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, x_in,
@@ -141,8 +239,8 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
   const int n_kv = kDc + kDr, n_q = num_heads * (kDn + kDr);
   float* kv = workspace;
   float* q = workspace + (int64_t)n_tokens * n_kv;
-  hipLaunchKernelGGL(rowdot_kernel, dim3((n_kv + 3) / 4), dim3(256), 0, stream, x, w_dkv, hidden, n_kv, n_tokens, kv);
-  hipLaunchKernelGGL(rowdot_kernel, dim3((n_q + 3) / 4), dim3(256), 0, stream, x, w_q, hidden, n_q, n_tokens, q);
+  project(x, w_dkv, hidden, n_kv, n_tokens, kv, stream);
+  project(x, w_q, hidden, n_q, n_tokens, q, stream);
   hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens, 1 + num_heads), dim3(64), 0, stream, kv, q, positions,
                      num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe);
   return hipGetLastError();

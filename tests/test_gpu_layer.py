@@ -1,5 +1,8 @@
 """The layer front on the GPU and one whole V2-Lite layer through the C ABI.
 
+Chunks under 64 tokens (or a width that is not a multiple of 64) take the
+vector-ALU projection, longer ones the matrix-core GEMM; both are covered.
+
 mla_layer_front (projections, RMSNorm, RoPE) is compared with oracle.layer's
 layer_front element by element.  Both sides round each output once to bf16; the
 GPU's projection sums are fp32 where the oracle's are fp64, so an element may
@@ -39,7 +42,8 @@ def _gpu_front(case, cache_dtype=0):
     return cfg, outs
 
 
-@pytest.mark.parametrize("T,H,hidden", [(26, 16, 2048), (1, 16, 2048), (17, 16, 520), (40, 128, 1024)])
+@pytest.mark.parametrize("T,H,hidden", [(26, 16, 2048), (1, 16, 2048), (17, 16, 520), (40, 128, 1024),
+                                          (200, 16, 2048), (64, 128, 1024), (100, 16, 520)])
 def test_layer_front(T, H, hidden):
     case = mla_synth.v2lite_layer(T=T, H=H, hidden=hidden, case_id=31)
     print("front T=%d H=%d hidden=%d" % (T, H, hidden), flush=True)
