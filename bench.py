@@ -46,6 +46,8 @@ PREFILL_WORKLOADS = {
                                          "causal unabsorbed attention"),
     "v3_prefill": ("v3_prefill", "V3-shaped prompt chunk: H=128, 4096 positions, no cached prefix, "
                                  "causal unabsorbed attention"),
+    "v2lite_prompt_layer": ("v2lite_layer", "one V2-Lite layer over a 4096-token prompt: front (projections, "
+                                            "RMSNorm, RoPE), causal unabsorbed attention, W_O + residual"),
 }
 DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3, "int8t": 4, "fp8t": 5}
 
@@ -123,21 +125,36 @@ def bench_prefill(args):
     from mla_absorbed_latent_amd import api
 
     gen, desc = PREFILL_WORKLOADS[args.workload]
-    case = getattr(mla_synth, gen)()
     dev = torch.device("cuda:0")
-    cfg = api.config(case.H, 0, case.softmax_scale)
 
     def bits(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    q_nope, q_pe, c, r = bits(case.q_nope), bits(case.q_pe), bits(case.c), bits(case.r)
-    w_uk, w_uv = bits(case.w_uk), bits(case.w_uv)
-    ws = torch.empty(api.prefill_workspace_bytes(cfg, case.L), dtype=torch.uint8, device=dev)
-    out = torch.empty(case.T, case.H, 128, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(case.T, case.H, dtype=torch.float32, device=dev)
+    if args.workload == "v2lite_prompt_layer":
+        from mla_absorbed_latent_amd.runner import PrefillLayer
+        case = mla_synth.v2lite_layer(T=4096)
+        case.L = case.T
+        cfg = api.config(case.H, 0, case.softmax_scale)
+        layer = PrefillLayer(cfg, case.T, case.hidden, dev)
+        x0 = bits(case.x)
+        x1 = torch.empty_like(x0)
+        w = [bits(a) for a in (case.w_q, case.w_dkv, case.w_uk, case.w_uv, case.w_o)]
+        proj = 2.0 * case.T * case.hidden * (case.H * 192 + 576 + case.H * 128)
 
-    def step():
-        api.prefill_attn(cfg, q_nope, q_pe, c, r, w_uk, w_uv, ws, out, lse)
+        def step():
+            layer.forward(x0, *w, x1)
+    else:
+        case = getattr(mla_synth, gen)()
+        cfg = api.config(case.H, 0, case.softmax_scale)
+        q_nope, q_pe, c, r = bits(case.q_nope), bits(case.q_pe), bits(case.c), bits(case.r)
+        w_uk, w_uv = bits(case.w_uk), bits(case.w_uv)
+        ws = torch.empty(api.prefill_workspace_bytes(cfg, case.L), dtype=torch.uint8, device=dev)
+        out = torch.empty(case.T, case.H, 128, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(case.T, case.H, dtype=torch.float32, device=dev)
+        proj = 0.0
+
+        def step():
+            api.prefill_attn(cfg, q_nope, q_pe, c, r, w_uk, w_uv, ws, out, lse)
 
     for _ in range(args.warmup):
         step()
@@ -155,10 +172,11 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
-    flops = prefill_flops(case)
+    flops = prefill_flops(case) + proj
     tf = flops / (call_ms * 1e-3) / 1e12
     line = {
-        "metric": "MLA prefill attention (unabsorbed, causal): TFLOP/s",
+        "metric": ("MLA prompt layer (front, unabsorbed causal attention, W_O): TFLOP/s" if proj
+                   else "MLA prefill attention (unabsorbed, causal): TFLOP/s"),
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -173,12 +191,13 @@ def bench_prefill(args):
         "config": {"workload": args.workload, "description": desc, "heads": case.H, "queries": case.T,
                    "positions": case.L},
         "tokens_per_s": round(case.T / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "mfma", "kernel": "mla_prefill_attn (expand_kv + prefill_attn)",
+        "roofline": {"bound": "mfma", "kernel": ("PrefillLayer.forward (front, prefill, W_O + residual)" if proj
+                                                 else "mla_prefill_attn (expand_kv + prefill_attn)"),
                      "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS_16, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_PEAK_TFLOPS_16, 4), "traffic": None, "launch_ms": round(call_ms, 5),
                      "flops_per_launch": flops},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not proj:
         log("timing the CPU oracle on a sample ...")
         line["cpu_baseline"] = cpu_baseline_prefill(case)
     print(json.dumps(line), flush=True)
