@@ -96,7 +96,7 @@ class DecodeRunner:
 class PrefillLayer:
     """One MLA layer over a chunk of T positions with no cached prefix, the way
     a prompt is processed: mla_layer_front -> mla_prefill_attn ->
-    mla_out_residual, four C-ABI calls on the current stream.  Buffers are
+    mla_out_residual, three C-ABI calls on the current stream.  Buffers are
     allocated once here (torch), never inside the library."""
 
     def __init__(self, cfg: api.Config, T: int, hidden: int, device="cuda:0"):
