@@ -57,3 +57,41 @@ def test_later_keys_do_not_reach_earlier_rows():
     out2, lse2 = prefill.prefill_unabsorbed(qn, qp, c2, r2, wk, wv)
     assert np.array_equal(out2[:3], out[:3]) and np.array_equal(lse2[:3], lse[:3])
     assert not np.allclose(out2[3:], out[3:])
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _broken_prefill(mistake):
+    """prefill_unabsorbed with one planted mistake."""
+    def f(q_nope, q_pe, c, r, w_uk, w_uv, scale):
+        T, L = q_nope.shape[0], c.shape[0]
+        wk, wv = (w_uv, w_uk) if mistake == "swapped_up_projections" else (w_uk, w_uv)
+        k, v = mla_ref.expand_kv(c, 0 * r if mistake == "dropped_rope_key" else r, wk, wv)
+        q = np.concatenate([q_nope, q_pe], axis=-1)
+        s = scale * np.einsum("thk,hlk->htl", q, k)
+        pos = (np.arange(T) if mistake == "positions_without_prefix" else L - T + np.arange(T))
+        masked = (np.arange(L)[None, :] >= pos[:, None]) if mistake == "diagonal_masked" else \
+            (np.arange(L)[None, :] > pos[:, None])
+        s = np.where(masked[None], -np.inf, s)
+        e = np.exp(s - s.max(-1, keepdims=True))
+        e = np.nan_to_num(e)
+        den = np.maximum(e.sum(-1, keepdims=True), 1e-300)
+        return np.einsum("htl,hld->thd", e / den, v), None
+    return f
+
+
+def _row_pin_holds(fn):
+    qn, qp, c, r, wk, wv = _inputs(5, 12, 2, seed=77)
+    out, _ = fn(qn, qp, c, r, wk, wv, 0.07)
+    for i in range(5):
+        p = 12 - 5 + i
+        o_a, _, _ = mla_ref.absorbed_decode(qn[i], qp[i], c[:p + 1], r[:p + 1], wk, wv, 0.07)
+        if not np.allclose(out[i], o_a, rtol=1e-9, atol=1e-12):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("mistake", ["swapped_up_projections", "dropped_rope_key", "positions_without_prefix",
+                                     "diagonal_masked"])
+def test_planted_mistakes_fail_the_row_pin(mistake):
+    assert _row_pin_holds(prefill.prefill_unabsorbed)
+    assert not _row_pin_holds(_broken_prefill(mistake))

@@ -250,3 +250,39 @@ def test_fp8_per_token_absmax_to_448_and_error_within_half_step():
     z = np.zeros((1, 512), np.uint16)
     fz = quant.encode_tokens(quant.CACHE_FP8_TOK, z, np.zeros((1, 64), np.uint16))
     assert fz["c_scale"][0, 0] == 0 and not fz["codes"].any()
+
+
+def _broken_fp8_encode(mistake):
+    def enc(y):
+        y = np.asarray(y, np.float32)
+        a = np.abs(y).astype(np.float64)
+        _, k = np.frexp(a)
+        bias = 8 if mistake == "bias_8" else 7
+        e = np.maximum(k - 1, 1 - bias)
+        rnd = np.floor if mistake == "truncate" else (lambda v: np.floor(v + 0.5)) if mistake == "ties_away" else np.rint
+        sub = a < 2.0 ** (1 - bias)
+        q_sub = rnd(a * 2.0 ** (bias + 2))
+        if mistake == "flush_subnormals":
+            q_sub = 0 * q_sub
+        q = rnd(np.ldexp(a, 3 - e))
+        code = np.where(sub, q_sub, (e + bias) * 8 + (q - 8))
+        code = np.clip(code, 0, 126).astype(np.uint8)
+        return np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
+    return enc
+
+
+def _fp8_pins_hold(enc):
+    import torch
+    rng = np.random.default_rng(13)
+    y = np.concatenate([rng.uniform(-448, 448, 5000), rng.standard_normal(5000) * 0.01,
+                        [1.0625, 1.1875, 3 * 2.0 ** -10]]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    return np.array_equal(enc(y), ref) and np.array_equal(enc(quant.fp8_e4m3_decode(codes)), codes)
+
+
+@pytest.mark.parametrize("mistake", ["truncate", "ties_away", "flush_subnormals", "bias_8"])
+def test_planted_fp8_encoder_mistakes_fail_the_pins(mistake):
+    assert _fp8_pins_hold(quant.fp8_e4m3_encode)
+    assert _fp8_pins_hold(_broken_fp8_encode("none"))
+    assert not _fp8_pins_hold(_broken_fp8_encode(mistake))
