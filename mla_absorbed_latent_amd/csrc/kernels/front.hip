@@ -167,45 +167,51 @@ void project(const uint16_t* x, const uint16_t* w, int K, int N, int T, float* y
 
 __device__ __forceinline__ uint16_t bf16_of(double v) { return f32_to_bf16_rne((float)v); }
 
-// Work-group (t, 0): the latent and the RoPE key of token t; (t, 1 + h): head h
-// of its query.  64 threads.
-__global__ __launch_bounds__(64) void front_finish_kernel(const float* __restrict__ kv, const float* __restrict__ q,
-                                                          const int32_t* __restrict__ pos, int H, float eps,
-                                                          float base, uint16_t* __restrict__ q_nope,
-                                                          uint16_t* __restrict__ q_pe, uint16_t* __restrict__ c_kv,
-                                                          uint16_t* __restrict__ k_pe) {
-  const int t = blockIdx.x, part = blockIdx.y, lane = threadIdx.x;
-  const double p = (double)pos[t];
-  // pair i (lane < 32) of a 64-wide rotary vector: angle p * base^(-2i/64)
-  auto rotate = [&](const float* src, uint16_t* dst) {
-    if (lane < 32) {
-      const double ang = p * pow((double)base, -2.0 * lane / 64.0);
-      const double c = cos(ang), s = sin(ang);
-      const double xe = src[2 * lane], xo = src[2 * lane + 1];
-      dst[2 * lane] = bf16_of(xe * c - xo * s);
-      dst[2 * lane + 1] = bf16_of(xe * s + xo * c);
-    }
-  };
-  if (part == 0) {
-    const float* row = kv + (int64_t)t * (kDc + kDr);
+// One work-group (256 threads) per token t: the 32 rotation angles of its
+// position are evaluated once (double precision) into LDS and shared by the
+// RoPE key and the H query heads; wave 0 normalises the latent.
+__global__ __launch_bounds__(256) void front_finish_kernel(const float* __restrict__ kv, const float* __restrict__ q,
+                                                           const int32_t* __restrict__ pos, int H, float eps,
+                                                           float base, uint16_t* __restrict__ q_nope,
+                                                           uint16_t* __restrict__ q_pe, uint16_t* __restrict__ c_kv,
+                                                           uint16_t* __restrict__ k_pe) {
+  __shared__ double cs[32][2];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < 32) {
+    // pair i of a 64-wide rotary vector turns by pos * base^(-2i/64)
+    const double ang = (double)pos[t] * pow((double)base, -2.0 * tid / 64.0);
+    cs[tid][0] = cos(ang);
+    cs[tid][1] = sin(ang);
+  }
+  const float* kv_row = kv + (int64_t)t * (kDc + kDr);
+  if (tid < 64) {
     double v[8], ss = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      v[i] = row[8 * lane + i];
+      v[i] = kv_row[8 * tid + i];
       ss += v[i] * v[i];
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const double inv = 1.0 / sqrt(ss / kDc + (double)eps);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c_kv[(int64_t)t * kDc + 8 * lane + i] = bf16_of(v[i] * inv);
-    rotate(row + kDc, k_pe + (int64_t)t * kDr);
-  } else {
-    const int h = part - 1;
-    const float* row = q + ((int64_t)t * H + h) * (kDn + kDr);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) q_nope[((int64_t)t * H + h) * kDn + 2 * lane + i] = bf16_of(row[2 * lane + i]);
-    rotate(row + kDn, q_pe + ((int64_t)t * H + h) * kDr);
+    for (int i = 0; i < 8; ++i) c_kv[(int64_t)t * kDc + 8 * tid + i] = bf16_of(v[i] * inv);
+  }
+  const float* q_tok = q + (int64_t)t * H * (kDn + kDr);
+  for (int idx = tid; idx < H * kDn; idx += 256) {
+    const int h = idx >> 7, d = idx & (kDn - 1);
+    q_nope[((int64_t)t * H + h) * kDn + d] = bf16_of(q_tok[h * (kDn + kDr) + d]);
+  }
+  __syncthreads();
+  // rotations: index H * 32 + i is pair i of the RoPE key, h * 32 + i of head h
+  for (int idx = tid; idx < (H + 1) * 32; idx += 256) {
+    const int h = idx >> 5, i = idx & 31;
+    const float* src = h < H ? q_tok + h * (kDn + kDr) + kDn : kv_row + kDc;
+    uint16_t* dst = h < H ? q_pe + ((int64_t)t * H + h) * kDr : k_pe + (int64_t)t * kDr;
+    const double c = cs[i][0], sn = cs[i][1];
+    const double xe = src[2 * i], xo = src[2 * i + 1];
+    dst[2 * i] = bf16_of(xe * c - xo * sn);
+    dst[2 * i + 1] = bf16_of(xe * sn + xo * c);
   }
 }
 
@@ -241,7 +247,7 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
   float* q = workspace + (int64_t)n_tokens * n_kv;
   project(x, w_dkv, hidden, n_kv, n_tokens, kv, stream);
   project(x, w_q, hidden, n_q, n_tokens, q, stream);
-  hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens, 1 + num_heads), dim3(64), 0, stream, kv, q, positions,
+  hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens), dim3(256), 0, stream, kv, q, positions,
                      num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe);
   return hipGetLastError();
 }
