@@ -13,8 +13,9 @@
 //   expand_kv_kernel: K_nope [H][Lp][128] and V^T [H][128][Lp] (fp16, Lp = L
 //     rounded up to 64, pad positions zero) from c_kv and W_UK / W_UV, a tiled
 //     bf16 MFMA GEMM;
-//   prefill_attn_kernel: flash attention per (128 queries, head), S^T = K Q^T
-//     and O^T = V^T P^T on v_mfma_f32_16x16x32_f16, streaming softmax in fp32.
+//   prefill_attn_kernel: flash attention per (128 queries, head): 4 waves of
+//     32 queries, S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16
+//     (each LDS fragment feeds two products), streaming softmax in fp32.
 // The operands of the attention products are fp16 (bf16 inputs widen exactly);
 // P is rounded to fp16, its fp32 sum taken before rounding.
 #include "common.h"
@@ -142,8 +143,9 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
     }
 }
 
-// Grid (ceil(T / 128), H), 512 threads (8 waves).  Wave w owns queries
-// i = 128 qb + 16 w + (lane % 16).  Per 64-key block: S^T[key][query] (4 key
+// Grid (ceil(T / kQB), H), kWaves waves.  Wave w owns queries
+// i = kQB qb + 16 (kU w + u) + (lane % 16), u < kU; each K / V^T fragment read
+// from LDS feeds kU products.  Per 64-key block: S^T[key][query] (4 key
 // tiles x 6 k-steps), softmax per query column (its 64 keys sit in the four
 // lanes l % 16 = q), then O^T[vdim][query] += V^T P^T (8 vdim tiles x 2
 // k-steps).  P^T feeds the second product straight from the score registers:
@@ -161,8 +163,11 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
 // the XOR spreads the 16 rows a fragment read touches over distinct banks.  The
 // RoPE part of the scores uses the bf16 matrix instruction on the bf16 q_pe and
 // k_pe (the products are exact either way).
-constexpr int kWaves = 8;                 // waves per work-group
-constexpr int kQB = 16 * kWaves;          // queries per work-group
+constexpr int kWaves = 4;                 // waves per work-group
+constexpr int kU = 2;                     // 16-query groups per wave
+constexpr int kQB = 16 * kU * kWaves;     // queries per work-group
+constexpr int kKSeg = 24 / kWaves;        // 1 KB K-tile segments per wave
+constexpr int kVSeg = 16 / kWaves;        // 1 KB V^T-tile segments per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKBytes = 64 * 24 * 16;     // 24,576
 constexpr int kVBytes = 128 * 8 * 16;     // 16,384
@@ -170,7 +175,7 @@ constexpr int kBufBytes = kKBytes + kVBytes;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
                                                                 const uint16_t* __restrict__ q_pe,
                                                                 const uint16_t* __restrict__ k_pe,
                                                                 const uint16_t* __restrict__ k_nope,
@@ -193,19 +198,21 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* 
   const int p_last = L - T + min(qb * kQB + kQB - 1, T - 1);
   const int n_blocks = p_last / 64 + 1;
 
-  const int i_raw = qb * kQB + 16 * wave + li;
-  const int i = i_raw < T ? i_raw : T - 1;         // rows past T repeat the last query, never stored
-  const int qpos = L - T + i;
-  // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (q_nope widened to fp16,
-  // exact; q_pe stays bf16).
-  u32x4 qf[6];
-  {
+  int i_raw[kU], qpos[kU];
+  u32x4 qf[kU][6];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    i_raw[u] = qb * kQB + 16 * (kU * wave + u) + li;
+    const int i = i_raw[u] < T ? i_raw[u] : T - 1;   // rows past T repeat the last query, never stored
+    qpos[u] = L - T + i;
+    // Q^T fragments: dims 32 ks + 8 g .. +7 of query i (q_nope widened to fp16,
+    // exact; q_pe stays bf16).
     const uint16_t* qn = q_nope + ((int64_t)i * H + h) * kDn + 8 * g;
     const uint16_t* qp = q_pe + ((int64_t)i * H + h) * kDr + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
+    for (int ks = 0; ks < 4; ++ks) qf[u][ks] = bf16x8_to_f16x8(ld16(qn + 32 * ks));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[4 + ks] = ld16(qp + 32 * ks);
+    for (int ks = 0; ks < 2; ++ks) qf[u][4 + ks] = ld16(qp + 32 * ks);
   }
 
   // This lane's part of a tile: K segments wave, wave + 8, wave + 16 (LDS slot
@@ -214,36 +221,41 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* 
   // per-head bases (a head's K_nope or V^T spans Lp * 128 < 2^31 elements).
   const uint16_t* k_nope_h = k_nope + (int64_t)h * Lp * kDn;
   const uint16_t* v_t_h = v_t + (int64_t)h * kDn * Lp;
-  int kslot[3], voff[2];
+  int kslot[kKSeg], voff[kVSeg];
 #pragma unroll
-  for (int n = 0; n < 3; ++n) {
-    const int P = 64 * (wave + 8 * n) + lane, key = P / 24;
+  for (int n = 0; n < kKSeg; ++n) {
+    const int P = 64 * (wave + kWaves * n) + lane, key = P / 24;
     kslot[n] = key | (((P % 24) ^ (key & 7)) << 8);         // key | chunk << 8
   }
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int P = 64 * (wave + 8 * n) + lane, d = P >> 3, ch = (P & 7) ^ (d & 7);
+  for (int n = 0; n < kVSeg; ++n) {
+    const int P = 64 * (wave + kWaves * n) + lane, d = P >> 3, ch = (P & 7) ^ (d & 7);
     voff[n] = d * Lp + 8 * ch;
   }
   auto issue = [&](int kb, int buf) {
     char* base = lds + buf * kBufBytes;
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
+    for (int n = 0; n < kKSeg; ++n) {
       const int j = kb * 64 + (kslot[n] & 255), ch = kslot[n] >> 8;
       const uint16_t* src = ch < 16 ? k_nope_h + (j * kDn + 8 * ch)
                                     : k_pe + ((j < L ? j : L - 1) * kDr + 8 * (ch - 16));   // pad keys: row L-1
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * (wave + 8 * n)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * (wave + kWaves * n)), 16, 0, 0);
     }
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-      __builtin_amdgcn_global_load_lds(v_t_h + (voff[n] + kb * 64), (lds_void*)(base + kKBytes + 1024 * (wave + 8 * n)),
-                                       16, 0, 0);
+    for (int n = 0; n < kVSeg; ++n)
+      __builtin_amdgcn_global_load_lds(v_t_h + (voff[n] + kb * 64),
+                                       (lds_void*)(base + kKBytes + 1024 * (wave + kWaves * n)), 16, 0, 0);
   };
 
-  floatx4 o[8];
+  floatx4 o[kU][8];
+  float m_run[kU], l_run[kU];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int u = 0; u < kU; ++u) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[u][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
 
   issue(0, 0);
   for (int kb = 0; kb < n_blocks; ++kb) {
@@ -253,62 +265,76 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* 
     const char* kt_lds = lds + (kb & 1) * kBufBytes;
     const char* vt_lds = kt_lds + kKBytes;
 
-    floatx4 s[4];
+    floatx4 s[kU][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kU; ++u) s[u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
       const int key = 16 * kt + li;
       const char* krow = kt_lds + key * 384;
 #pragma unroll
       for (int ks = 0; ks < 6; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * ks + g) ^ (key & 7)));
-        if (ks < 4)
-          s[kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[ks]), s[kt]);
-        else
-          s[kt] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), s[kt]);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (ks < 4)
+            s[u][kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[u][ks]), s[u][kt]);
+          else
+            s[u][kt] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u][ks]),
+                                         s[u][kt]);
+        }
       }
     }
     // keys after the query (and pad keys) masked; only blocks that reach past
     // the work-group's first query can hold such keys
     if (kb * 64 + 63 > p_first) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb * 64 + 16 * kt + 4 * g + r > qpos) s[kt][r] = -INFINITY;
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * 64 + 16 * kt + 4 * g + r > qpos[u]) s[u][kt][r] = -INFINITY;
     }
     // streaming softmax on raw scores: p = 2^(c s - c m) with c = scale log2(e)
-    float mb = -INFINITY;
+    u32x4 pb[kU][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int u = 0; u < kU; ++u) {
+      float mb = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[kt][r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);           // finite: key 0 is in every query's range
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    m_run = m_new;
-    const float neg_mc = -m_new * scale_log2;
-    float lsum = 0.f;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[u][kt][r]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float m_new = fmaxf(m_run[u], mb);       // finite: key 0 is in every query's range
+      const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * scale_log2);
+      m_run[u] = m_new;
+      const float neg_mc = -m_new * scale_log2;
+      float lsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, neg_mc));
-        s[kt][r] = p;
-        lsum += p;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[u][kt][r], scale_log2, neg_mc));
+          s[u][kt][r] = p;
+          lsum += p;
+        }
+      l_run[u] = l_run[u] * alpha + lsum;
+      // the running maximum of most columns stops moving after a few blocks:
+      // rescale only when some column's changed (alpha == 1 leaves o as it is)
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[u][mt] *= alpha;
       }
-    l_run = l_run * alpha + lsum;
-    // the running maximum of most columns stops moving after a few blocks:
-    // rescale only when some column's changed (alpha == 1 leaves o as it is)
-    if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+      for (int ks = 0; ks < 2; ++ks)
+        pb[u][ks] = u32x4{pack_f16(s[u][2 * ks][0], s[u][2 * ks][1]), pack_f16(s[u][2 * ks][2], s[u][2 * ks][3]),
+                          pack_f16(s[u][2 * ks + 1][0], s[u][2 * ks + 1][1]),
+                          pack_f16(s[u][2 * ks + 1][2], s[u][2 * ks + 1][3])};
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pb = {pack_f16(s[2 * ks][0], s[2 * ks][1]), pack_f16(s[2 * ks][2], s[2 * ks][3]),
-                        pack_f16(s[2 * ks + 1][0], s[2 * ks + 1][1]), pack_f16(s[2 * ks + 1][2], s[2 * ks + 1][3])};
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const int d = 16 * mt + li;
@@ -316,23 +342,28 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(const uint16_t* 
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + (g >> 1)) ^ (d & 7)));
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + 2 + (g >> 1)) ^ (d & 7)));
         const half8 av = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb), o[mt]);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
       }
-    }
   }
 
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (i_raw < T) {
-    const float inv = 1.f / l_run;
-    uint16_t* orow = out + ((int64_t)i_raw * H + h) * kDn + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const uint32_t a = (uint32_t)f32_to_bf16_rne(o[mt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][1] * inv) << 16);
-      const uint32_t b = (uint32_t)f32_to_bf16_rne(o[mt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[mt][3] * inv) << 16);
-      *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
+  for (int u = 0; u < kU; ++u) {
+    float l = l_run[u];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (i_raw[u] < T) {
+      const float inv = 1.f / l;
+      uint16_t* orow = out + ((int64_t)i_raw[u] * H + h) * kDn + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t a = (uint32_t)f32_to_bf16_rne(o[u][mt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][mt][1] * inv) << 16);
+        const uint32_t b = (uint32_t)f32_to_bf16_rne(o[u][mt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][mt][3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(orow + 16 * mt) = u32x2{a, b};
+      }
+      if (lse != nullptr && g == 0)
+        lse[(int64_t)i_raw[u] * H + h] = (m_run[u] * scale_log2 + __log2f(l)) * 0.6931471805599453f;
     }
-    if (lse != nullptr && g == 0) lse[(int64_t)i_raw * H + h] = (m_run * scale_log2 + __log2f(l_run)) * 0.6931471805599453f;
   }
 }
 
