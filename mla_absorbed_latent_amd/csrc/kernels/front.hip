@@ -70,10 +70,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
 
 // y[t][n] = sum_k x[t][k] w[n][k] on the matrix cores, for chunks of many
 // tokens: a work-group computes 128 tokens x 128 features from 64-channel
-// chunks of both operands staged in LDS (double-buffered, 16-byte chunk c of
-// row r at c ^ (r & 7)); wave (wm, wn) holds 64 x 64 of the result as 4 x 4
-// tiles of v_mfma_f32_16x16x32_bf16.  K a multiple of 64; rows past T or N
-// read as zero and are not stored.
+// chunks of both operands loaded straight into LDS (double-buffered, 16-byte
+// chunk c of row r at c ^ (r & 7)); wave (wm, wn) holds 64 x 64 of the result
+// as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16.  K a multiple of 64; rows past T
+// or N are not stored.
 constexpr int kGT = 128;
 constexpr int kGChunk = 64;
 constexpr int kGRow = kGChunk * 2;               // 128 B
@@ -86,26 +86,25 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
   const int g = lane >> 4, li = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
-  u32x4 st[8];
-  auto load = [&](int kc) {
+  // rows 0..127 x, 128..255 w, 8 chunks of 16 B per row, straight into LDS
+  // (global_load_lds_dwordx4 fills a 1 KB segment, lane i bytes 16 i ..): 32
+  // segments, wave w issues w + 4 i, each lane the chunk that belongs at its
+  // slot.  Rows past T or N load row T - 1 or N - 1; their results are dropped.
+  auto issue = [&](int kc, int buf) {
+    char* base = lds + buf * kGBuf;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+      const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 3, ch = (P & 7) ^ (row & 7);
       const int k = kc * kGChunk + 8 * ch;
+      const uint16_t* src;
       if (row < kGT) {
         const int t = t0 + row;
-        st[i] = t < T ? ld16(x + (int64_t)t * K + k) : u32x4{0, 0, 0, 0};
+        src = x + (int64_t)(t < T ? t : T - 1) * K + k;
       } else {
         const int n = n0 + row - kGT;
-        st[i] = n < N ? ld16(w + (int64_t)n * K + k) : u32x4{0, 0, 0, 0};
+        src = w + (int64_t)(n < N ? n : N - 1) * K + k;
       }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(lds + buf * kGBuf + row * kGRow + 16 * (ch ^ (row & 7))) = st[i];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + 1024 * seg), 16, 0, 0);
     }
   };
   floatx4 acc[4][4];
@@ -114,11 +113,11 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int n_chunks = K / kGChunk;
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kc = 0; kc < n_chunks; ++kc) {
-    if (kc + 1 < n_chunks) load(kc + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                       // chunk kc in LDS; chunk kc - 1 read by every wave
+    if (kc + 1 < n_chunks) issue(kc + 1, (kc + 1) & 1);
     const char* buf = lds + (kc & 1) * kGBuf;
 #pragma unroll
     for (int ks = 0; ks < kGChunk / 32; ++ks) {
@@ -135,10 +134,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[a]),
                                                               __builtin_bit_cast(bf16x8, wf[b]), acc[a][b], 0, 0, 0);
-    }
-    if (kc + 1 < n_chunks) {
-      store((kc + 1) & 1);
-      __syncthreads();
     }
   }
   // D[token 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]

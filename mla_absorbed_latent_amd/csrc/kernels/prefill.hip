@@ -11,8 +11,8 @@
 //
 // Two kernels, both on the matrix cores (fp32 sums):
 //   expand_kv_kernel: K_nope [H][Lp][128] and V^T [H][128][Lp] (fp16, Lp = L
-//     rounded up to 64, pad positions zero) from c_kv and W_UK / W_UV, a tiled
-//     bf16 MFMA GEMM;
+//     rounded up to 64; pad positions repeat position L - 1, finite and always
+//     masked) from c_kv and W_UK / W_UV, a tiled bf16 MFMA GEMM;
 //   prefill_attn_kernel: flash attention per (128 queries, head): 4 waves of
 //     32 queries, S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16
 //     (each LDS fragment feeds two products), streaming softmax in fp32.
@@ -39,8 +39,8 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // Grid (ceil(Lp / 128), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
 // work-group computes 128 positions x the 128 output features of head h as a
 // tiled GEMM over the 512 latent channels: chunks of 64 channels of the latent
-// rows and of the weight rows are staged in LDS (double-buffered, 16-byte chunk
-// c of row r at c ^ (r & 7)), and wave (wm, wn) computes 64 positions x 64
+// rows and of the weight rows go straight into LDS (double-buffered, 16-byte
+// chunk c of row r at c ^ (r & 7)), and wave (wm, wn) computes 64 positions x 64
 // features from them (4 x 4 tiles of 16 x 16).  Both operands are rows of 64
 // channels with the same fragment layout, so the weight is the A operand for
 // K_nope (D[feature][position]: four consecutive features per lane and store)
@@ -62,25 +62,25 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
   const int j0 = blockIdx.x * kXT;
   const uint16_t* w = (is_v ? w_uv : w_uk) + (int64_t)h * kDn * kDc;
 
-  // staging: rows 0..127 latent, 128..255 weight; 8 chunks per row; 8 per thread
-  u32x4 st[8];
-  auto load = [&](int kc) {
+  // staging: rows 0..127 latent, 128..255 weight, 8 chunks of 16 B per row,
+  // straight into LDS (global_load_lds_dwordx4: lane i of a wave instruction
+  // fills bytes 16 i .. of a 1 KB segment): 32 segments, wave w issues w + 4 i.
+  // Each lane loads the chunk that belongs at its slot (chunk ch ^ (row & 7)).
+  // Positions past L load position L - 1: finite values, masked in attention.
+  auto issue = [&](int kc, int buf) {
+    char* base = lds + buf * kXBuf;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int idx = tid + 256 * n, row = idx >> 3, ch = idx & 7;
+    for (int i = 0; i < 8; ++i) {
+      const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 3, ch = (P & 7) ^ (row & 7);
+      const int k = kc * kXChunk + 8 * ch;
+      const uint16_t* src;
       if (row < kXT) {
         const int j = j0 + row;
-        st[n] = j < L ? ld16(c_kv + (int64_t)j * kDc + kc * kXChunk + 8 * ch) : u32x4{0, 0, 0, 0};
+        src = c_kv + (int64_t)(j < L ? j : L - 1) * kDc + k;
       } else {
-        st[n] = ld16(w + (int64_t)(row - kXT) * kDc + kc * kXChunk + 8 * ch);
+        src = w + (int64_t)(row - kXT) * kDc + k;
       }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int idx = tid + 256 * n, row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(lds + buf * kXBuf + row * kXRow + 16 * (ch ^ (row & 7))) = st[n];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + 1024 * seg), 16, 0, 0);
     }
   };
 
@@ -90,12 +90,12 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  store(0);
-  __syncthreads();
   constexpr int kChunks = kDc / kXChunk;
+  issue(0, 0);
   for (int kc = 0; kc < kChunks; ++kc) {
-    if (kc + 1 < kChunks) load(kc + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                       // chunk kc in LDS; chunk kc - 1 read by every wave
+    if (kc + 1 < kChunks) issue(kc + 1, (kc + 1) & 1);
     const char* buf = lds + (kc & 1) * kXBuf;
 #pragma unroll
     for (int ks = 0; ks < kXChunk / 32; ++ks) {
@@ -118,10 +118,6 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
             acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf[a]), __builtin_bit_cast(bf16x8, wf[b]),
                                           acc[a][b]);
         }
-    }
-    if (kc + 1 < kChunks) {
-      store((kc + 1) & 1);
-      __syncthreads();
     }
   }
 
