@@ -72,3 +72,20 @@ def test_scratch_stays_small(asm):
     text = "\n".join(asm)
     for m in re.finditer(r"\.name:\s+(_ZN3mla\d+decode_h\S+)\s*\n(?:.*\n){0,80}?\s+\.private_segment_fixed_size:\s+(\d+)", text):
         assert int(m.group(2)) <= 128, (m.group(1), m.group(2))
+
+
+@pytest.mark.parametrize("src", ["prefill.hip", "front.hip"])
+def test_prompt_path_kernels_use_no_scratch(src, tmp_path):
+    """The prompt-path kernels (K/V expansion, prefill attention, projections)
+    are sized to fit their registers; a spill there would be a silent
+    regression of the same kind as in the decode kernels."""
+    out = str(tmp_path / (src + ".s"))
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I" + KDIR, "-I" + os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-o", out, os.path.join(KDIR, src)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    text = open(out).read()
+    sizes = re.findall(r"\.name:\s+(_ZN\S+)\s*\n(?:.*\n){0,80}?\s+\.private_segment_fixed_size:\s+(\d+)", text)
+    assert sizes, src
+    for name, size in sizes:
+        assert int(size) == 0, (name, size)
