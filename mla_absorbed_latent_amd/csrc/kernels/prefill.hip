@@ -45,6 +45,16 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // channels with the same fragment layout, so the weight is the A operand for
 // K_nope (D[feature][position]: four consecutive features per lane and store)
 // and the B operand for V^T (D[position][feature]: four consecutive positions).
+// V^T keeps each 32-key block's positions in the order 0-3, 16-19, 4-7, 20-23,
+// 8-11, 24-27, 12-15, 28-31: the eight keys that lane group g of the value
+// product takes in a k-step (32 ks + 4 g .. +3 and 32 ks + 16 + 4 g .. +3) are
+// then one contiguous 16-byte chunk.  vt_pos maps a position j (a multiple of
+// 4) to its stored place.
+__device__ __forceinline__ int vt_pos(int j) {
+  const int q = (j & 31) >> 2;
+  return (j & ~31) + 4 * (q < 4 ? 2 * q : 2 * (q - 4) + 1);
+}
+
 constexpr int kXT = 128;                  // positions per work-group
 constexpr int kXChunk = 64;               // channels per LDS chunk
 constexpr int kXRow = kXChunk * 2;        // 128 B
@@ -131,10 +141,11 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
         const int j = j0 + 64 * wm + 16 * a + li;
         if (j < Lp) *reinterpret_cast<u32x2*>(k_nope + ((int64_t)h * Lp + j) * kDn + 64 * wn + 16 * b + 4 * g) = o;
       } else {
-        // D[position 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]
+        // D[position 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]; the four
+        // positions go to their place in the key order of vt_pos
         const int j = j0 + 64 * wm + 16 * a + 4 * g;
         if (j < Lp)
-          *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 64 * wn + 16 * b + li) * Lp + j) = o;
+          *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 64 * wn + 16 * b + li) * Lp + vt_pos(j)) = o;
       }
     }
 }
@@ -155,7 +166,9 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
 // 16-byte chunk that belongs at its LDS slot, which gives the layouts
 //   K tile   [64 keys][24 chunks of 8] (128 K_nope dims fp16, then 64 k_pe dims
 //            kept in bf16), chunk c of key k at slot c ^ (k & 7);
-//   V^T tile [128 dims][8 chunks of 8 keys] fp16, chunk c of dim d at c ^ (d & 7);
+//   V^T tile [128 dims][8 chunks of 8 keys] fp16 (keys in the order of vt_pos, so
+//            chunk 4 ks + g is exactly the eight keys lane group g needs in
+//            k-step ks), chunk c of dim d at c ^ (d & 7);
 // the XOR spreads the 16 rows a fragment read touches over distinct banks.  The
 // RoPE part of the scores uses the bf16 matrix instruction on the bf16 q_pe and
 // k_pe (the products are exact either way).
@@ -334,10 +347,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const int d = 16 * mt + li;
-        const char* vrow = vt_lds + d * 128 + 8 * (g & 1);
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + (g >> 1)) ^ (d & 7)));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * ((4 * ks + 2 + (g >> 1)) ^ (d & 7)));
-        const half8 av = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const half8 av = __builtin_bit_cast(
+            half8, *reinterpret_cast<const u32x4*>(vt_lds + d * 128 + 16 * ((4 * ks + g) ^ (d & 7))));
 #pragma unroll
         for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
       }
