@@ -27,6 +27,9 @@ by itself, so append can be done token by token) are:
       q = clamp(rint(x / scale), -7, 7);  amax == 0 -> scale 0, q 0
       stored as the nibble q + 8 (1..15), same byte order as INT4
       dequant: (nibble - 8) * scale (float32, one rounding)
+  INT4 symmetric with an INT4 RoPE key (a variant the report does not
+  measure): the latent as INT4 symmetric; the RoPE key by the same rule in
+  groups of 8 (scale = max|x| / 7, nibble q + 8, same byte order).
   FP8 per token (e4m3; a cache format the pages name but do not specify):
       amax = max |x| over the token's 512 latent channels (8 for each RoPE-key
       group), scale = amax / 448 (float32; 448 is the largest e4m3 value)
@@ -50,6 +53,8 @@ Page layouts (64 tokens a page, bytes):
   int8t: [64][576] int8 codes | [64] f32 latent scales
          | [64][8] f32 RoPE-key scales                                 39,168
   fp8t : as int8t with e4m3 codes                                     39,168
+  int4k4: [64][256] latent nibbles | [64][32] RoPE-key nibbles
+         | [64][16] f32 scales | [64][8] f32 RoPE-key scales           24,576
 
 Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
 INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
@@ -72,7 +77,7 @@ D_R = 64
 G_C = 32      # latent channels per group
 G_R = 8       # RoPE-key channels per group
 
-CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK = 0, 1, 2, 3, 4, 5
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4 = range(7)
 _F448 = np.float32(448.0)
 _F127 = np.float32(127.0)
 _F15 = np.float32(15.0)
@@ -211,7 +216,8 @@ def token_bytes(dtype: int) -> int:
             CACHE_INT4: D_C // 2 + D_R + (D_C // G_C) * 8 + (D_R // G_R) * 4,
             CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4,
             CACHE_INT8_TOK: 576 + 4 + (D_R // G_R) * 4,
-            CACHE_FP8_TOK: 576 + 4 + (D_R // G_R) * 4}[dtype]
+            CACHE_FP8_TOK: 576 + 4 + (D_R // G_R) * 4,
+            CACHE_INT4_SYM_K4: D_C // 2 + D_R // 2 + (D_C // G_C) * 4 + (D_R // G_R) * 4}[dtype]
 
 
 def page_bytes(dtype: int) -> int:
@@ -222,6 +228,10 @@ def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
     """Quantise (or copy) n token rows into their per-field arrays."""
     if dtype == CACHE_BF16:
         return {"rows": np.concatenate([c_bits, r_bits], axis=-1).astype(np.uint16)}
+    if dtype == CACHE_INT4_SYM_K4:
+        q, s = quant_int4_sym(c_bits, G_C)
+        rq, rs = quant_int4_sym(r_bits, G_R)
+        return {"nib": pack_nibbles(q), "r_nib": pack_nibbles(rq), "c_scale": s, "r_scale": rs}
     if dtype == CACHE_FP8_TOK:
         cc, cs = quant_fp8(c_bits, D_C)
         rc, rs = quant_fp8(r_bits, G_R)
@@ -255,6 +265,11 @@ def pack_page(dtype: int, fields: dict) -> np.ndarray:
         off = put(0, fields["codes"], 576)
         off = put(off, fields["c_scale"], 64 if dtype == CACHE_INT8 else 4)
         put(off, fields["r_scale"], 32)
+    elif dtype == CACHE_INT4_SYM_K4:
+        off = put(0, fields["nib"], 256)
+        off = put(off, fields["r_nib"], 32)
+        off = put(off, fields["c_scale"], 64)
+        put(off, fields["r_scale"], 32)
     else:
         off = put(0, fields["nib"], 256)
         off = put(off, fields["r_codes"], 64)
@@ -282,6 +297,11 @@ def unpack_page(dtype: int, page: np.ndarray) -> dict:
         rs, _ = get(off, 32, np.float32, 8)
         return {"codes": codes, "c_scale": cs, "r_scale": rs}
     nib, off = get(0, 256, np.uint8, 256)
+    if dtype == CACHE_INT4_SYM_K4:
+        rn, off = get(off, 32, np.uint8, 32)
+        cs, off = get(off, 64, np.float32, 16)
+        rs, _ = get(off, 32, np.float32, 8)
+        return {"nib": nib, "r_nib": rn, "c_scale": cs, "r_scale": rs}
     rc, off = get(off, 64, np.int8, 64)
     cs, off = get(off, 64, np.float32, 16)
     if dtype == CACHE_INT4_SYM:
@@ -303,6 +323,9 @@ def dequant_fields(dtype: int, f: dict):
         c = dequant_int8(f["codes"][..., :D_C], f["c_scale"], G_C if dtype == CACHE_INT8 else D_C)
         r = dequant_int8(f["codes"][..., D_C:], f["r_scale"], G_R)
         return c, r
+    if dtype == CACHE_INT4_SYM_K4:
+        return (dequant_int4_sym(unpack_nibbles(f["nib"]), f["c_scale"], G_C),
+                dequant_int4_sym(unpack_nibbles(f["r_nib"]), f["r_scale"], G_R))
     if dtype == CACHE_INT4_SYM:
         c = dequant_int4_sym(unpack_nibbles(f["nib"]), f["c_scale"], G_C)
     else:

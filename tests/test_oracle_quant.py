@@ -140,7 +140,8 @@ def test_token_and_page_bytes():
     assert quant.token_bytes(quant.CACHE_INT4_SYM) == 256 + 64 + 16 * 4 + 8 * 4 == 416
     assert quant.token_bytes(quant.CACHE_INT8_TOK) == 512 + 64 + 4 + 8 * 4 == 612
     assert quant.token_bytes(quant.CACHE_FP8_TOK) == 612
-    assert [quant.page_bytes(d) for d in (0, 1, 2, 3, 4, 5)] == [73728, 43008, 30720, 26624, 39168, 39168]
+    assert quant.token_bytes(quant.CACHE_INT4_SYM_K4) == 256 + 32 + 16 * 4 + 8 * 4 == 384
+    assert [quant.page_bytes(d) for d in (0, 1, 2, 3, 4, 5, 6)] == [73728, 43008, 30720, 26624, 39168, 39168, 24576]
 
 
 def test_int8_per_token_one_scale_for_the_latent():
@@ -156,7 +157,7 @@ def test_int8_per_token_one_scale_for_the_latent():
     assert np.all(np.abs(f["codes"][:, :512]).max(-1) == 127)
 
 
-@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4, 5, 6])
 def test_page_roundtrip(dtype):
     rng = np.random.default_rng(3 + dtype)
     c = _draw(rng, (50, 512))
@@ -176,7 +177,7 @@ def test_pool_dequant_matches_field_dequant():
     c = _draw(rng, (L, 512))
     r = _draw(rng, (L, 64))
     bt = np.array([5, 0, 3])
-    for dt in (0, 1, 2, 3, 4, 5):
+    for dt in (0, 1, 2, 3, 4, 5, 6):
         pool = quant.pack_pool(dt, 6, [(c, r, bt)])
         cc, rr = quant.dequant_pool_seq(dt, pool, bt, L)
         f = quant.encode_tokens(dt, c, r)
@@ -286,3 +287,20 @@ def test_planted_fp8_encoder_mistakes_fail_the_pins(mistake):
     assert _fp8_pins_hold(quant.fp8_e4m3_encode)
     assert _fp8_pins_hold(_broken_fp8_encode("none"))
     assert not _fp8_pins_hold(_broken_fp8_encode(mistake))
+
+
+def test_int4_sym_rope_key_groups_of_8():
+    """INT4 symmetric key variant: the RoPE key follows the latent's rule in
+    groups of 8 -- each group's absmax element maps to nibble 8 +- 7, the scale
+    is max|x| / 7, and every element is within half a step."""
+    rng = np.random.default_rng(21)
+    c, r = _draw(rng, (40, 512)), _draw(rng, (40, 64))
+    f = quant.encode_tokens(quant.CACHE_INT4_SYM_K4, c, r)
+    x = bf16_bits_to_f32(r).reshape(40, 8, 8)
+    s = f["r_scale"]
+    assert np.array_equal(s, (np.abs(x).max(-1) / np.float32(7)).astype(np.float32))
+    q = quant.unpack_nibbles(f["r_nib"]).reshape(40, 8, 8).astype(np.int32) - 8
+    assert np.all(np.abs(q).max(-1) == 7)
+    _, rr = quant.dequant_fields(quant.CACHE_INT4_SYM_K4, f)
+    err = np.abs(rr.reshape(40, 8, 8) - x)
+    assert np.all(err <= s[..., None] / 2 * (1 + 1e-6) + 1e-12)
