@@ -64,7 +64,8 @@ typedef enum {
   MLA_CACHE_INT4 = 2,     /* c_kv asymmetric INT4, fp32 scale + zero per 32; k_pe INT8    */
   MLA_CACHE_INT4_SYM = 3, /* c_kv symmetric INT4, fp32 scale per 32; k_pe INT8            */
   MLA_CACHE_INT8_TOK = 4, /* c_kv INT8, one fp32 scale per token; k_pe INT8 per 8         */
-  MLA_CACHE_FP8_TOK = 5   /* c_kv e4m3 FP8, one fp32 scale per token; k_pe e4m3 per 8     */
+  MLA_CACHE_FP8_TOK = 5,  /* c_kv e4m3 FP8, one fp32 scale per token; k_pe e4m3 per 8     */
+  MLA_CACHE_INT4_SYM_K4 = 6 /* c_kv symmetric INT4 per 32; k_pe symmetric INT4 per 8       */
 } mla_cache_dtype;
 
 /* Shape of one MLA layer.  Supported: num_heads in {16, 128}, qk_nope_dim = 128,
@@ -109,6 +110,8 @@ typedef struct {
  *   INT8_TOK: [64][576] int8 codes | [64] f32 latent scales
  *         | [64][8] f32 RoPE-key scales                               (39,168 B)
  *   FP8_TOK: as INT8_TOK with e4m3 codes                              (39,168 B)
+ *   INT4_SYM_K4: [64][256] latent nibbles | [64][32] RoPE-key nibbles
+ *         | [64][16] f32 scales | [64][8] f32 RoPE-key scales         (24,576 B)
  * A pool of N pages is N * mla_cache_page_bytes() contiguous bytes.          */
 mla_status mla_config_check(const mla_config* cfg);
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
@@ -138,7 +141,8 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
  *   max|x| = 0 gives scale 0 and codes 0.
  * INT4_SYM: per group of 32 latent channels, scale = max|x| / 7,
  *   q = clamp(rint(x/scale), -7, 7), stored as q + 8; max|x| = 0 gives scale 0
- *   and q = 0.  The RoPE key of both INT4 formats is INT8 as above.
+ *   and q = 0.  The RoPE key of INT4 and INT4_SYM is INT8 as above.
+ * INT4_SYM_K4: INT4_SYM, and the RoPE key by the same rule in 8-channel groups.
  * Codes and scales are bit-exact with that definition.
  * n_tokens == 0 is a no-op; n_tokens < 0 is MLA_ERR_VALUE.                  */
 mla_status mla_cache_append(const mla_config* cfg, void* pool, int64_t num_pages,

@@ -55,7 +55,7 @@ mla_status mla_config_check(const mla_config* cfg) {
   if (cfg->qk_nope_dim != 128 || cfg->kv_lora_rank != 512 || cfg->rope_dim != 64 || cfg->v_head_dim != 128 ||
       cfg->block_size != 64)
     return MLA_ERR_SHAPE;
-  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_FP8_TOK) return MLA_ERR_VALUE;
+  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_INT4_SYM_K4) return MLA_ERR_VALUE;
   if (!(cfg->softmax_scale > 0.f) || !std::isfinite(cfg->softmax_scale)) return MLA_ERR_VALUE;
   return MLA_OK;
 }
@@ -67,6 +67,7 @@ size_t mla_cache_bytes_per_token(const mla_config* cfg) {
     case MLA_CACHE_INT8: return 576 + 16 * 4 + 8 * 4;          // codes + latent scales + key scales
     case MLA_CACHE_INT4: return 256 + 64 + 16 * 4 + 16 * 4 + 8 * 4;   // nibbles + key codes + scales + zeros + key scales
     case MLA_CACHE_INT4_SYM: return 256 + 64 + 16 * 4 + 8 * 4;          // nibbles + key codes + scales + key scales
+    case MLA_CACHE_INT4_SYM_K4: return 256 + 32 + 16 * 4 + 8 * 4;       // nibbles + key nibbles + scales + key scales
     default: return 576 + 4 + 8 * 4;                           // codes + the token's latent scale + key scales
   }
 }

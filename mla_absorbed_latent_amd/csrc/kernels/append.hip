@@ -31,6 +31,7 @@ constexpr int kPageInt8 = kBlock * 672;                  // 43,008
 constexpr int kPageInt4 = kBlock * 480;                  // 30,720
 constexpr int kPageInt4Sym = kBlock * 416;               // 26,624
 constexpr int kPageInt8Tok = kBlock * 612;               // 39,168
+constexpr int kPageInt4SymK4 = kBlock * 384;             // 24,576
 
 __device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_pages) {
   return slot >= 0 && slot < num_pages * kBlock;
@@ -188,6 +189,8 @@ __global__ __launch_bounds__(256) void append_int4(uint8_t* pool, int64_t num_pa
 }
 
 // 24 groups a token: 16 symmetric INT4 latent groups of 32, then 8 INT8 RoPE-key groups.
+// kKey4: the RoPE key by the same symmetric INT4 rule in groups of 8.
+template <bool kKey4>
 __global__ __launch_bounds__(256) void append_int4s(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
                                                     const uint16_t* k_pe, const int64_t* slots, int n) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -196,12 +199,13 @@ __global__ __launch_bounds__(256) void append_int4s(uint8_t* pool, int64_t num_p
   if (tok >= n) return;
   const int64_t slot = slots[tok];
   if (!slot_ok(slot, num_pages)) return;
-  uint8_t* page = pool + (slot / kBlock) * kPageInt4Sym;
+  uint8_t* page = pool + (slot / kBlock) * (kKey4 ? kPageInt4SymK4 : kPageInt4Sym);
   const int off = (int)(slot % kBlock);
-  // page regions: nibbles [64][256] | rope codes [64][64] | scales [64][16] | rope scales [64][8]
+  // page regions: nibbles [64][256] | rope codes [64][64] (kKey4: rope nibbles
+  // [64][32]) | scales [64][16] | rope scales [64][8]
   uint8_t* nib = page;
   int8_t* rcodes = reinterpret_cast<int8_t*>(page + 64 * 256);
-  float* scales = reinterpret_cast<float*>(page + 64 * 256 + 64 * 64);
+  float* scales = reinterpret_cast<float*>(page + 64 * 256 + 64 * (kKey4 ? 32 : 64));
   float* rscales = scales + 64 * 16;
   if (grp < 16) {
     const uint16_t* x = c_kv + tok * kDc + grp * 32;
@@ -227,6 +231,28 @@ __global__ __launch_bounds__(256) void append_int4s(uint8_t* pool, int64_t num_p
 #pragma unroll
     for (int j = 0; j < 16; ++j) dst[j] = bytes[j];
     scales[off * 16 + grp] = scale;
+  } else if constexpr (kKey4) {
+    const int j = grp - 16;
+    const uint16_t* x = k_pe + tok * kDr + j * 8;
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = bf16_to_f32(x[i]);
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const float scale = __fdiv_rn(amax, 7.0f);
+    uint8_t* dst = page + 64 * 256 + off * 32 + j * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int q0 = 0, q1 = 0;
+      if (scale != 0.f) {
+        q0 = (int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * b], scale)), -7.f), 7.f);
+        q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v[2 * b + 1], scale)), -7.f), 7.f);
+      }
+      dst[b] = (uint8_t)((q0 + 8) | ((q1 + 8) << 4));
+    }
+    rscales[off * 8 + j] = scale;
   } else {
     const int j = grp - 16;
     int8_t codes[8];
@@ -337,8 +363,10 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
       hipLaunchKernelGGL(append_int8, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
     else if (cache_dtype == 2)
       hipLaunchKernelGGL(append_int4, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+    else if (cache_dtype == 3)
+      hipLaunchKernelGGL(append_int4s<false>, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
     else
-      hipLaunchKernelGGL(append_int4s, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+      hipLaunchKernelGGL(append_int4s<true>, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
   }
   return hipGetLastError();
 }

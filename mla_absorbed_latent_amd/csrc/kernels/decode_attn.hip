@@ -351,14 +351,17 @@ struct LoaderInt8Reg {
 //            | [64][16] f32 zeros | [64][8] f32 key scales.
 // Symmetric INT4 (kSym) drops the zeros: a nibble holds q + 8 and decodes to
 // (nibble - 8) * scale.
-template <int kTok, int kSwz, int kTid0 = 0, bool kSym = false>
+// kKey4 (with kSym): the RoPE key as symmetric INT4 too, 8 nibbles per lane
+// ([64][32] key nibbles in place of the [64][64] codes; 384 B/token).
+template <int kTok, int kSwz, int kTid0 = 0, bool kSym = false, bool kKey4 = false>
 struct LoaderInt4Reg {
   static constexpr int kPass = kTok / 32;
   static constexpr int kScorePrefetch = 2;    // its staging registers leave room for two
-  static constexpr int kPage = kBlock * (kSym ? 416 : 480);
+  static constexpr int kPage = kBlock * (kKey4 ? 384 : (kSym ? 416 : 480));
+  static constexpr int kMeta = 64 * 256 + 64 * (kKey4 ? 32 : 64);   // byte offset of the scales
   static constexpr int kKeyScales = kSym ? 64 * 16 : 2 * 64 * 16;   // float offset of the key scales after the scales
   uint32_t n[8 * kPass];     // 8 nibbles (latent chunk k) per dword
-  u32x2 kc[kPass];           // 8 key codes (chunk 8)
+  u32x2 kc[kPass];           // 8 key codes (chunk 8); kKey4: 8 key nibbles in kc[p][0]
   float s[9 * kPass];        // scale per chunk (k = 8: key scale)
   float z[kSym ? 1 : 8 * kPass];   // zero point per latent chunk (asymmetric only)
 
@@ -369,9 +372,9 @@ struct LoaderInt4Reg {
       const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
       const int row = (t0 % kBlock) + 32 * p + tok;
       const uint8_t* pg = page_base(a, page, ok, kPage);
-      const float* scales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + row * 16 + (c8 >> 2);
+      const float* scales = reinterpret_cast<const float*>(pg + kMeta) + row * 16 + (c8 >> 2);
       const float* zeros = scales + 64 * 16;
-      const float* kscales = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64) + kKeyScales + row * 8 + c8;
+      const float* kscales = reinterpret_cast<const float*>(pg + kMeta) + kKeyScales + row * 8 + c8;
       const uint8_t* nib = pg + row * 256 + 4 * c8;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -379,7 +382,8 @@ struct LoaderInt4Reg {
         s[9 * p + k] = scales[2 * k];
         if constexpr (!kSym) z[8 * p + k] = zeros[2 * k];
       }
-      kc[p] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
+      if constexpr (kKey4) kc[p][0] = *reinterpret_cast<const uint32_t*>(pg + 64 * 256 + row * 32 + 4 * c8);
+      else kc[p] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
       s[9 * p + 8] = kscales[0];
     }
     return page >= 0;
@@ -416,13 +420,14 @@ struct LoaderInt4Reg {
     if constexpr (I % 2 == 1) {
       constexpr int k = I / 2;
       const int c8 = ltid<kTid0>() & 7;
-      const float* meta = reinterpret_cast<const float*>(pg + 64 * 256 + 64 * 64);
+      const float* meta = reinterpret_cast<const float*>(pg + kMeta);
       if constexpr (k < 8) {
         n[k] = *reinterpret_cast<const uint32_t*>(pg + row * 256 + 4 * c8 + 32 * k);
         s[k] = meta[row * 16 + (c8 >> 2) + 2 * k];
         if constexpr (!kSym) z[k] = meta[64 * 16 + row * 16 + (c8 >> 2) + 2 * k];
       } else {
-        kc[0] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
+        if constexpr (kKey4) kc[0][0] = *reinterpret_cast<const uint32_t*>(pg + 64 * 256 + row * 32 + 4 * c8);
+        else kc[0] = *reinterpret_cast<const u32x2*>(pg + 64 * 256 + row * 64 + 8 * c8);
         s[8] = meta[kKeyScales + row * 8 + c8];
       }
     }
@@ -444,7 +449,14 @@ struct LoaderInt4Reg {
     } else {
       const _Float16 kh = (_Float16)s[9 * p + 8];
       const half2v k2 = {kh, kh};
-      cur = int8x4_to_f16(kc[p][I % 2], k2);
+      if constexpr (kKey4) {
+        const half2v z0 = {(_Float16)0.0f, (_Float16)0.0f};
+        const uint32_t w = kc[p][0];
+        constexpr int j0 = 2 * (I % 2);
+        cur = u32x2{nib2(w, j0, k2, z0), nib2(w, j0 + 1, k2, z0)};
+      } else {
+        cur = int8x4_to_f16(kc[p][I % 2], k2);
+      }
     }
     if constexpr (I % 2 == 0) {
       part = cur;
@@ -470,8 +482,15 @@ struct LoaderInt4Reg {
       }
       const _Float16 kh = (_Float16)s[9 * p + 8];
       const half2v k2 = {kh, kh};
-      const u32x2 lo = int8x4_to_f16(kc[p][0], k2), hi = int8x4_to_f16(kc[p][1], k2);
-      *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      if constexpr (kKey4) {
+        const half2v z0 = {(_Float16)0.0f, (_Float16)0.0f};
+        const uint32_t w = kc[p][0];
+        *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * 8) =
+            u32x4{nib2(w, 0, k2, z0), nib2(w, 1, k2, z0), nib2(w, 2, k2, z0), nib2(w, 3, k2, z0)};
+      } else {
+        const u32x2 lo = int8x4_to_f16(kc[p][0], k2), hi = int8x4_to_f16(kc[p][1], k2);
+        *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
     }
   }
 };
@@ -712,14 +731,17 @@ struct LoaderInt8Wide {
 // Threads c4 >= 2 write their chunks in the order j ^ 2, so that the four
 // threads of a token write four different LDS bank groups at every store.  The
 // key piece (16 codes at 16 c4) goes to chunks 2 c4, 2 c4 + 1 of group 8.
-template <int kSwz, int kTid0, bool kSym = false>
+// kKey4 (with kSym): the RoPE key as symmetric INT4, 16 nibbles (two 8-groups)
+// per thread in one 8-byte load.
+template <int kSwz, int kTid0, bool kSym = false, bool kKey4 = false>
 struct LoaderInt4Wide {
   static constexpr int kLoads = kSym ? 7 : 8;   // load instructions per tile
-  static constexpr int kPage = kBlock * (kSym ? 416 : 480);
+  static constexpr int kPage = kBlock * (kKey4 ? 384 : (kSym ? 416 : 480));
   static constexpr int kKeyScales = kSym ? 64 * 64 : 2 * 64 * 64;   // byte offset of the key scales after the scales
   u32x4 n[4] = {};
   floatx4 sq = {}, zq = {};  // scales / zeros 4 c4 .. 4 c4 + 3 of the token (transposed in commit)
   u32x4 kc = {};
+  u32x2 kn = {};             // kKey4: key nibbles 16 c4 .. 16 c4 + 15
   floatx2 ks = {};
 
   __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
@@ -732,8 +754,9 @@ struct LoaderInt4Wide {
     asm_ld16_nt<64>(n[1], nib);
     asm_ld16_nt<128>(n[2], nib);
     asm_ld16_nt<192>(n[3], nib);
-    asm_ld16_nt<0>(kc, pg + 64 * 256 + row * 64 + 16 * c4);
-    const uint8_t* meta = pg + 64 * 256 + 64 * 64;
+    if constexpr (kKey4) asm_ld8<0>(kn, pg + 64 * 256 + row * 32 + 8 * c4);
+    else asm_ld16_nt<0>(kc, pg + 64 * 256 + row * 64 + 16 * c4);
+    const uint8_t* meta = pg + 64 * 256 + 64 * (kKey4 ? 32 : 64);
     asm_ld16<0>(sq, meta + row * 64 + 16 * c4);
     if constexpr (!kSym) asm_ld16<0>(zq, meta + 64 * 64 + row * 64 + 16 * c4);
     asm_ld8<0>(ks, meta + kKeyScales + row * 32 + 8 * c4);
@@ -744,7 +767,8 @@ struct LoaderInt4Wide {
     for (int i = 0; i < 4; ++i) settle(n[i]);
     settle(sq);
     if constexpr (!kSym) settle(zq);
-    settle(kc);
+    if constexpr (kKey4) settle(kn);
+    else settle(kc);
     settle(ks);
   }
   __device__ __forceinline__ void commit(char* lds_buf) {
@@ -772,10 +796,17 @@ struct LoaderInt4Wide {
       }
     }
     const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
-    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
-    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
-    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4) + 128 * 8) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-    *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4 + 1) + 128 * 8) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+    if constexpr (kKey4) {
+      const half2v z0 = {(_Float16)0.0f, (_Float16)0.0f};
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4) + 128 * 8) = nib8_to_f16<true>(kn[0], half2v{k0, k0}, z0);
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4 + 1) + 128 * 8) =
+          nib8_to_f16<true>(kn[1], half2v{k1, k1}, z0);
+    } else {
+      const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+      const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4) + 128 * 8) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4 + 1) + 128 * 8) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+    }
   }
 };
 
@@ -1100,8 +1131,9 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
 
   using Loader = typename std::conditional<
       kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
-      typename std::conditional<kCache == 1 || kCache >= 4, LoaderInt8Reg<kTile128, kSwz128, 0, kCache >= 4, kCache == 5>,
-                                LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3>>::type>::type;
+      typename std::conditional<kCache == 1 || kCache == 4 || kCache == 5,
+                                LoaderInt8Reg<kTile128, kSwz128, 0, kCache >= 4, kCache == 5>,
+                                LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3 || kCache == 6, kCache == 6>>::type>::type;
   h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
                          overflow);
   if (__syncthreads_or(overflow)) {
@@ -1117,7 +1149,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   }
 
   // ---- per-head sums from the owning waves, then normalise and write ----
-  if constexpr (kCache == 2 || kCache == 3) {
+  if constexpr (kCache == 2 || kCache == 3 || kCache == 6) {
     // INT4: o_part is stored straight from the accumulator layout (16-byte row
     // pieces): with the transposed write below, this kernel spills in its tile loop.
     const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
@@ -1466,6 +1498,7 @@ using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
 using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
 using H16Int8Tok = LoaderInt8Wide<kSwz16, 256, true>;
 using H16Fp8Tok = LoaderInt8Wide<kSwz16, 256, true, true>;
+using H16Int4SymK4 = LoaderInt4Wide<kSwz16, 256, true, true>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
@@ -1477,6 +1510,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h128<3>, grid, block, 0, stream, a);
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h128<4>, grid, block, 0, stream, a);
     else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h128<5>, grid, block, 0, stream, a);
+    else if (cache_dtype == 6) hipLaunchKernelGGL(decode_h128<6>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
     const dim3 block16(512);                       // 4 compute + 4 staging waves
@@ -1486,6 +1520,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h16<H16Int4Sym>, grid, block16, 0, stream, a);
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h16<H16Int8Tok>, grid, block16, 0, stream, a);
     else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h16<H16Fp8Tok>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 6) hipLaunchKernelGGL(decode_h16<H16Int4SymK4>, grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

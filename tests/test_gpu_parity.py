@@ -22,7 +22,7 @@ def _note(msg):
 
 
 # ------------------------------------------------------------------ a-1 append
-@pytest.mark.parametrize("cache_dtype", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cache_dtype", [0, 1, 2, 3, 4, 5, 6])
 def test_append_bitexact(cache_dtype):
     case = mla_synth.small_decode(case_id=11, H=16, seq_lens=[1, 63, 64, 65, 130], paging="shuffled",
                                   normalise=cache_dtype == 0, outliers=cache_dtype != 0, extra_pages=3)
@@ -95,7 +95,7 @@ needs_quant = pytest.mark.skipif(not QUANT_DECODE_READY, reason="quantised decod
 
 
 @needs_quant
-@pytest.mark.parametrize("cache_dtype", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cache_dtype", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("H", [16, 128])
 def test_decode_quantised_small(cache_dtype, H):
     case = mla_synth.small_decode(case_id=14, H=H, seq_lens=[1, 70, 640, 2000], normalise=False, outliers=True)
@@ -277,12 +277,14 @@ FULL = [
     pytest.param("v2lite_quant_int4s", lambda: mla_synth.v2lite_quant(), 3, marks=needs_quant),
     pytest.param("v2lite_quant_int8t", lambda: mla_synth.v2lite_quant(), 4, marks=needs_quant),
     pytest.param("v2lite_quant_fp8t", lambda: mla_synth.v2lite_quant(), 5, marks=needs_quant),
+    pytest.param("v2lite_quant_int4k4", lambda: mla_synth.v2lite_quant(), 6, marks=needs_quant),
 ]
 
 
 @pytest.mark.parametrize("name,make,cache_dtype", FULL,
                          ids=["v2lite_decode", "v3_decode", "v3_ragged", "v2lite_quant_int8", "v2lite_quant_int4",
-                              "v2lite_quant_int4s", "v2lite_quant_int8t", "v2lite_quant_fp8t"])
+                              "v2lite_quant_int4s", "v2lite_quant_int8t", "v2lite_quant_fp8t",
+                              "v2lite_quant_int4k4"])
 def test_full_size_sampled(name, make, cache_dtype):
     case = make()
     _note("full %s B=%d H=%d tokens=%d" % (name, case.B, case.H, case.total_tokens))
