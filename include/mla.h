@@ -317,6 +317,17 @@ mla_status mla_out_residual(const mla_config* cfg, const uint16_t* attn_out, con
                             const uint16_t* x_in, uint16_t* x_out, float* workspace, size_t workspace_bytes,
                             int32_t n_tokens, hipStream_t stream);
 
+/* ------------------------------------------------------------------ a-1 + a-2
+ * mla_append_absorb_q: mla_cache_append followed by mla_absorb_q (same
+ * arguments, definitions and results, bit for bit), in one launch when the
+ * cache is bf16 (the append's copies run as extra work-groups of the absorb
+ * kernel; the two touch disjoint memory).  Other formats launch the two
+ * kernels in turn.  Either count may be 0.                                   */
+mla_status mla_append_absorb_q(const mla_config* cfg, void* pool, int64_t num_pages, const uint16_t* c_kv,
+                               const uint16_t* k_pe, const int64_t* slot_mapping, int32_t n_tokens,
+                               const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, uint16_t* q_abs,
+                               int32_t batch, hipStream_t stream);
+
 /* ------------------------------------------------------------------ prefill
  * mla_prefill_attn: causal attention of a chunk of T queries in the unabsorbed
  * form, the one engines use for prefill ([Tutorial] §四; the computation is

@@ -18,7 +18,7 @@ prefill_attn runs a prompt chunk's causal attention in the unabsorbed form.
 """
 from .api import (  # noqa: F401
     MlaError, Config, config, cache_bytes_per_token, cache_page_bytes, decode_workspace_bytes,
-    plan_splits, cache_append, absorb_q, decode_attn, decode_combine, out_proj, decode_combine_out_proj, status_string,
+    plan_splits, cache_append, absorb_q, append_absorb_q, decode_attn, decode_combine, out_proj, decode_combine_out_proj, status_string,
     layer_front, layer_front_workspace_bytes, prefill_attn, prefill_workspace_bytes,
     out_residual,
     CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4,

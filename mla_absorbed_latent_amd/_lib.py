@@ -50,6 +50,7 @@ SIGNATURES = {
                                    _P]),
     "mla_prefill_workspace_bytes": (C.c_size_t, [_CFG, C.c_int32]),
     "mla_out_residual": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]),
+    "mla_append_absorb_q": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P, C.c_int32, _P, _P, _P, _P, C.c_int32, _P]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
     "mla_last_hip_error": (C.c_int32, []),
 }

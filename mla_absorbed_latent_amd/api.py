@@ -119,6 +119,27 @@ def cache_append(cfg: Config, pool, c_kv, k_pe, slot_mapping) -> None:
            "mla_cache_append")
 
 
+def append_absorb_q(cfg: Config, pool, c_kv, k_pe, slot_mapping, q_nope, q_pe, w_uk, q_abs) -> None:
+    """cache_append then absorb_q, one launch for a bf16 cache (mla_append_absorb_q)."""
+    n = int(c_kv.shape[0])
+    _need(c_kv, "c_kv", (n, 512), 2)
+    _need(k_pe, "k_pe", (n, 64), 2)
+    _need(slot_mapping, "slot_mapping", (n,), 8)
+    page = cache_page_bytes(cfg)
+    nbytes = pool.numel() * pool.element_size()
+    if nbytes % page:
+        raise ValueError("pool size %d is not a whole number of %d-byte pages" % (nbytes, page))
+    B, H = int(q_nope.shape[0]), cfg.num_heads
+    _need(q_nope, "q_nope", (B, H, 128), 2)
+    _need(q_pe, "q_pe", (B, H, 64), 2)
+    _need(w_uk, "w_uk", (H, 128, 512), 2)
+    _need(q_abs, "q_abs", (B, H, 576), 2)
+    _check(L.load().mla_append_absorb_q(C.byref(cfg), _dev(pool, "pool"), nbytes // page, _dev(c_kv, "c_kv"),
+                                        _dev(k_pe, "k_pe"), _dev(slot_mapping, "slot_mapping"), n,
+                                        _dev(q_nope, "q_nope"), _dev(q_pe, "q_pe"), _dev(w_uk, "w_uk"),
+                                        _dev(q_abs, "q_abs"), B, _stream()), "mla_append_absorb_q")
+
+
 def absorb_q(cfg: Config, q_nope, q_pe, w_uk, q_abs) -> None:
     B, H = int(q_nope.shape[0]), cfg.num_heads
     _need(q_nope, "q_nope", (B, H, 128), 2)

@@ -104,6 +104,27 @@ mla_status mla_absorb_q(const mla_config* cfg, const uint16_t* q_nope, const uin
   return launched(mla::launch_absorb_q(cfg->num_heads, q_nope, q_pe, w_uk, q_abs, batch, stream));
 }
 
+mla_status mla_append_absorb_q(const mla_config* cfg, void* pool, int64_t num_pages, const uint16_t* c_kv,
+                               const uint16_t* k_pe, const int64_t* slot_mapping, int32_t n_tokens,
+                               const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, uint16_t* q_abs,
+                               int32_t batch, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (n_tokens < 0 || num_pages < 0 || batch < 0) return MLA_ERR_VALUE;
+  if (n_tokens > 0) {
+    if (!pool || !c_kv || !k_pe || !slot_mapping) return MLA_ERR_NULL;
+    if (!aligned16(pool) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(slot_mapping)) return MLA_ERR_ALIGN;
+  }
+  if (batch > 0) {
+    if (!q_nope || !q_pe || !w_uk || !q_abs) return MLA_ERR_NULL;
+    if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_ALIGN;
+  }
+  if (n_tokens == 0 && batch == 0) return MLA_OK;
+  if ((s = check_device()) != MLA_OK) return s;
+  return launched(mla::launch_append_absorb(cfg->cache_dtype, pool, num_pages, c_kv, k_pe, slot_mapping, n_tokens,
+                                            cfg->num_heads, q_nope, q_pe, w_uk, q_abs, batch, stream));
+}
+
 mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const void* pool, int64_t num_pages,
                            const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
                            const mla_work_item* items, int32_t n_items, uint16_t* o_part, float* lse_part,

@@ -24,7 +24,28 @@ constexpr int kWRow = kSlab * 2;                 // 256 B per LDS row (one d)
 __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
                                                        const uint16_t* __restrict__ q_pe,
                                                        const uint16_t* __restrict__ w_uk,
-                                                       uint16_t* __restrict__ q_abs, int H, int B) {
+                                                       uint16_t* __restrict__ q_abs, int H, int B,
+                                                       uint8_t* __restrict__ pool, int64_t num_pages,
+                                                       const uint16_t* __restrict__ c_kv,
+                                                       const uint16_t* __restrict__ k_pe,
+                                                       const int64_t* __restrict__ slots, int n_new) {
+  // Work-groups past the absorb grid append the step's new tokens to a bf16
+  // cache (16-byte chunk `chunk` of token `tok`'s 1,152-byte row), so that a
+  // decode step's append and absorb take one launch.  Out-of-range slots are
+  // skipped, as in mla_cache_append.
+  const int n_absorb = H * (kDc / kSlab);
+  if ((int)blockIdx.x >= n_absorb) {
+    const int64_t gid = (int64_t)(blockIdx.x - n_absorb) * 256 + threadIdx.x;
+    const int64_t tok = gid / 72;
+    const int chunk = (int)(gid % 72);
+    if (tok >= n_new) return;
+    const uint16_t* src = chunk < 64 ? c_kv + tok * kDc + chunk * 8 : k_pe + tok * kDr + (chunk - 64) * 8;
+    const u32x4 v = ld16(src);
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= num_pages * kBlock) return;
+    st16(pool + (slot / kBlock) * (kBlock * kRowBytesBf16) + (slot % kBlock) * kRowBytesBf16 + chunk * 16, v);
+    return;
+  }
   __shared__ __attribute__((aligned(16))) char lds[kDn * kWRow];     // 32 KB
   // Output tile of 32 sequences x 128 columns (fp16, rows of 256 B, 16-byte chunk c
   // at c ^ (row & 15)): written in the accumulator layout, read back as whole
@@ -123,7 +144,23 @@ hipError_t launch_absorb_q(int num_heads, const uint16_t* q_nope, const uint16_t
                            uint16_t* q_abs, int batch, hipStream_t stream) {
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(absorb_q_kernel, dim3(num_heads * (kDc / kSlab)), dim3(256), 0, stream, q_nope, q_pe, w_uk,
-                     q_abs, num_heads, batch);
+                     q_abs, num_heads, batch, nullptr, (int64_t)0, nullptr, nullptr, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_absorb(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
+                                const uint16_t* k_pe, const int64_t* slots, int n_new, int num_heads,
+                                const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, uint16_t* q_abs,
+                                int batch, hipStream_t stream) {
+  if (cache_dtype != 0 || batch <= 0 || n_new <= 0) {
+    hipError_t e = launch_append(cache_dtype, pool, num_pages, c_kv, k_pe, slots, n_new, stream);
+    if (e != hipSuccess) return e;
+    return launch_absorb_q(num_heads, q_nope, q_pe, w_uk, q_abs, batch, stream);
+  }
+  const int64_t append_blocks = ((int64_t)n_new * 72 + 255) / 256;
+  hipLaunchKernelGGL(absorb_q_kernel, dim3((unsigned)(num_heads * (kDc / kSlab) + append_blocks)), dim3(256), 0,
+                     stream, q_nope, q_pe, w_uk, q_abs, num_heads, batch, static_cast<uint8_t*>(pool), num_pages,
+                     c_kv, k_pe, slots, n_new);
   return hipGetLastError();
 }
 

@@ -13,6 +13,13 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
 hipError_t launch_absorb_q(int num_heads, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk,
                            uint16_t* q_abs, int batch, hipStream_t stream);
 
+// One launch for a bf16 cache (append work-groups after the absorb grid);
+// launch_append then launch_absorb_q for the other formats.
+hipError_t launch_append_absorb(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
+                                const uint16_t* k_pe, const int64_t* slots, int n_new, int num_heads,
+                                const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk, uint16_t* q_abs,
+                                int batch, hipStream_t stream);
+
 hipError_t launch_combine(int num_heads, const uint16_t* o_part, const float* lse_part, const int32_t* split_offsets,
                           float* o_lat, float* lse, int batch, hipStream_t stream);
 

@@ -79,11 +79,12 @@ class DecodeRunner:
 
     def step(self, q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c_kv=None, new_k_pe=None,
              new_slots=None, w_o=None, y=None, out_f32=None, fused=True, keep_latent=True):
-        """One decode step: append the new tokens, absorb, attend, merge, expand
-        (merge and expansion fused unless fused=False)."""
+        """One decode step: append the new tokens and absorb (one call), attend,
+        merge, expand (merge and expansion fused unless fused=False)."""
         if new_c_kv is not None:
-            self.append(new_c_kv, new_k_pe, new_slots)
-        self.absorb(q_nope, q_pe, w_uk)
+            api.append_absorb_q(self.cfg, self.pool, new_c_kv, new_k_pe, new_slots, q_nope, q_pe, w_uk, self.q_abs)
+        else:
+            self.absorb(q_nope, q_pe, w_uk)
         self.attend(block_table, seq_lens)
         if fused:
             self.combine_project(w_uv, w_o, y, out_f32, keep_latent)

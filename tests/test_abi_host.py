@@ -222,3 +222,19 @@ def test_out_residual_validation(lib):
     assert call(attn=odd) == L.MLA_ERR_ALIGN
     assert call(ws=64 * 2048 * 4 - 1) == L.MLA_ERR_WORKSPACE
     assert call(attn=None, x=None, n=0) == L.MLA_OK
+
+
+def test_append_absorb_validation(lib):
+    cfg = api.config(16)
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    f = lib.mla_append_absorb_q
+
+    def call(pool=fake, n=4, q=fake, b=2, np_=4):
+        return f(C.byref(cfg), pool, np_, fake, fake, fake, n, q, fake, fake, fake, b, None)
+
+    assert call(n=-1) == L.MLA_ERR_VALUE
+    assert call(b=-1) == L.MLA_ERR_VALUE
+    assert call(pool=None) == L.MLA_ERR_NULL
+    assert call(q=None) == L.MLA_ERR_NULL
+    assert call(pool=odd) == L.MLA_ERR_ALIGN
+    assert call(pool=None, n=0, q=None, b=0) == L.MLA_OK

@@ -298,3 +298,32 @@ def test_full_size_sampled(name, make, cache_dtype):
         _note("  seq %d L=%d max_rel %.2e mean_rel %.2e" % (b, lens[b], mx, mean))
         assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
     assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("cache_dtype", [0, 1])
+@pytest.mark.parametrize("H,B", [(128, 64), (16, 5)])
+def test_append_absorb_fused_matches_the_two_calls(cache_dtype, H, B):
+    """mla_append_absorb_q (one launch for a bf16 cache) writes the same pool
+    bytes and q_abs, bit for bit, as mla_cache_append then mla_absorb_q; one
+    slot is out of range and skipped by both."""
+    case = mla_synth.small_decode(case_id=23, H=H, seq_lens=[1] * B)
+    cfg = api.config(H, cache_dtype)
+    pages = 4
+    page = api.cache_page_bytes(cfg)
+    c = to_dev_bits(mla_synth.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((B, 512)).astype(np.float32)))
+    r = to_dev_bits(mla_synth.f32_to_bf16_bits(np.random.default_rng(4).standard_normal((B, 64)).astype(np.float32)))
+    slots = np.random.default_rng(5).permutation(pages * 64)[:B].astype(np.int64)
+    slots[B // 2] = pages * 64 + 7                          # out of range: skipped
+    slots = torch.from_numpy(slots).to(DEV)
+    qn, qp, wk = to_dev_bits(case.q_nope), to_dev_bits(case.q_pe), to_dev_bits(case.w_uk)
+    pool_a = torch.zeros(pages * page, dtype=torch.uint8, device=DEV)
+    pool_b = torch.zeros_like(pool_a)
+    qa = torch.empty(B, H, 576, dtype=torch.float16, device=DEV)
+    qb = torch.empty_like(qa)
+    api.cache_append(cfg, pool_a, c, r, slots)
+    api.absorb_q(cfg, qn, qp, wk, qa)
+    api.append_absorb_q(cfg, pool_b, c, r, slots, qn, qp, wk, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a, pool_b)
+    assert torch.equal(qa.view(torch.int16), qb.view(torch.int16))
+    assert pool_a.any()
