@@ -85,7 +85,11 @@ typedef struct {
 
 /* One unit of split-KV work: pages [first_page, first_page + n_pages) of
  * sequence `seq` (logical page numbers, i.e. indices into its block-table row);
- * the partial result is written to row `out_row` of o_part / lse_part. */
+ * the partial result is written to row `out_row` of o_part / lse_part.  The
+ * range is clipped to the block-table row and to the sequence's length; an
+ * item whose range is then empty (first_page past either) writes o = 0 and
+ * lse = -inf.  An item with seq or out_row out of range, or a negative
+ * first_page or n_pages, is skipped (its row is not written). */
 typedef struct {
   int32_t seq;
   int32_t first_page;
@@ -194,7 +198,8 @@ mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, 
  *   q_abs        device [batch][H][576] fp16 (from mla_absorb_q)
  *   pool         device, num_pages pages in the config's format
  *   block_table  device [batch][max_pages_per_seq] int32 physical page ids;
- *                ids outside [0, num_pages) make their tokens contribute nothing
+ *                ids outside [0, num_pages) make their tokens contribute nothing;
+ *                max_pages_per_seq <= 2^24 (MLA_ERR_VALUE otherwise)
  *   seq_lens     device [batch] int32
  *   items        device [n_items] (from mla_plan_splits, uploaded by the caller)
  *   o_part       device [n_items][H][512] fp16 (IEEE binary16 bits),
@@ -204,7 +209,14 @@ mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, 
  * Numerics: scores and probabilities use fp16 operands on the matrix cores
  * with fp32 accumulation; the bf16 latent is widened to fp16 exactly (values
  * beyond +-65504 are not supported); softmax state is fp32; the normalised
- * partial o_j is rounded to fp16 (round to nearest even), lse_j stays fp32.  */
+ * partial o_j is rounded to fp16 (round to nearest even), lse_j stays fp32.
+ * Quantised caches are dequantised to fp16 with each fp32 scale (and INT4
+ * zero point) rounded to fp16 first: the result stays within the output
+ * tolerance while every group's scale is at least 2^-17 (INT8: max|x| of a
+ * 32-channel group >= 127 * 2^-17, about 1e-3; INT4: max - min >= 15 * 2^-17),
+ * including groups much smaller than the rest of their token; smaller scales
+ * become fp16 subnormals and lose relative precision.  Zero points far above
+ * their scale are fine: a dequantised value keeps fp16's relative precision.  */
 mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const void* pool,
                            int64_t num_pages, const int32_t* block_table,
                            int32_t max_pages_per_seq, const int32_t* seq_lens,

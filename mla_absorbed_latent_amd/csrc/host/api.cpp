@@ -45,6 +45,11 @@ mla_status check_device() {
 
 mla_status launched(hipError_t e) { return e == hipSuccess ? MLA_OK : hip_fail(e); }
 
+// Widest block-table row mla_decode_attn accepts: 2^24 pages (2^30 tokens), so
+// that every token index a kernel forms, look-ahead tiles included, stays below
+// 2^31.
+constexpr int32_t kMaxPagesPerSeq = 1 << 24;
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +137,7 @@ mla_status mla_decode_attn(const mla_config* cfg, const uint16_t* q_abs, const v
   mla_status s = mla_config_check(cfg);
   if (s != MLA_OK) return s;
   if (n_items < 0 || batch < 0 || num_pages < 0 || max_pages_per_seq < 0) return MLA_ERR_VALUE;
+  if (max_pages_per_seq > kMaxPagesPerSeq) return MLA_ERR_VALUE;
   if (n_items == 0) return MLA_OK;
   if (!q_abs || !pool || !block_table || !seq_lens || !items || !o_part || !lse_part) return MLA_ERR_NULL;
   if (!aligned16(q_abs) || !aligned16(pool) || !aligned16(block_table) || !aligned16(seq_lens) ||

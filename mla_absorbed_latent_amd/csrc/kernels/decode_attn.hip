@@ -39,6 +39,7 @@
 
 #include "common.h"
 #include "decode_attn.h"
+#include "item_range.h"
 
 namespace mla {
 
@@ -80,18 +81,16 @@ __device__ __forceinline__ ItemRange item_range(const DecodeArgs& a) {
   r.ok = it.seq >= 0 && it.seq < a.batch && it.out_row >= 0 && it.out_row < a.n_items && it.first_page >= 0 &&
          it.n_pages >= 0;
   if (!r.ok) { r.t_begin = r.t_end = 0; return r; }
-  const int L = max(a.seq_lens[it.seq], 0);
-  const int pmax = min(it.first_page + it.n_pages, a.max_pages);
-  r.t_begin = it.first_page * kBlock;
-  r.t_end = min(pmax * kBlock, L);
-  if (r.t_end < r.t_begin) r.t_end = r.t_begin;
+  const TokenRange tr = item_token_range(it.first_page, it.n_pages, a.max_pages, a.seq_lens[it.seq], kBlock);
+  r.t_begin = tr.t_begin;
+  r.t_end = tr.t_end;
   return r;
 }
 
 // Physical page of logical token t of sequence b, or -1 when out of range.
 __device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int t) {
   const int lp = t / kBlock;
-  if (lp >= a.max_pages) return -1;
+  if (lp < 0 || lp >= a.max_pages) return -1;
   const int64_t p = a.block_table[(int64_t)b * a.max_pages + lp];
   return (p >= 0 && p < a.num_pages) ? p : -1;
 }

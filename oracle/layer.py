@@ -17,10 +17,13 @@ layer_decode then decodes the last position over all positions (the decoded
 token attends to itself: the cache holds prefill + 1 token, as in [Audit] §4.1)
 and applies the output projection.
 
-Parity: the front (projection, RMSNorm, RoPE) has no printed values for
-synthetic weights -- "parity unpinned" beyond the properties tested
-(RoPE preserves pair norms and is the identity at position 0; RMSNorm output
-has unit RMS).  The decode part is pinned through mla_ref.
+Pins (tests/test_layer_oracle.py): RoPE is the identity at position 0,
+preserves pair norms, gives scores that depend only on relative position, and
+turns pairs 0, 8, 16 and 24 by exactly 1, 0.1, 0.01 and 0.001 rad per position
+(the four decades of a 64-wide key with base 10000); RMSNorm of a constant row
+is c / sqrt(c^2 + eps); a one-hot hidden state reads back one column of every
+projection, which fixes their orientation and the head-major query split.  The
+decode part is pinned through mla_ref.
 """
 from __future__ import annotations
 

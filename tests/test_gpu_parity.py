@@ -227,14 +227,20 @@ def test_merge_with_no_split_rows(H):
     assert torch.all(o_lat == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("hidden", [2048, 520])
 @pytest.mark.parametrize("fused", [True, False])
-def test_output_projection_with_wo(fused):
-    """V2-Lite layer shapes: one sequence of 26 tokens, H=16, W_O to hidden 2048."""
+def test_output_projection_with_wo(fused, hidden):
+    """V2-Lite layer shapes: one sequence of 26 tokens, H=16, W_O to hidden 2048,
+    and a non-square W_O (hidden 520 != 16 * 128) that a transposed operand on
+    either side would not survive."""
     layer = mla_synth.v2lite_layer()
+    if hidden != 2048:
+        w = np.random.default_rng(71).standard_normal((hidden, 16 * 128)).astype(np.float32) * np.float32(0.02)
+        layer.w_o = mla_synth.f32_to_bf16_bits(w)
     case = mla_synth.small_decode(case_id=19, H=16, seq_lens=[26])
     run, dev = upload(case)
     run.plan([26], chunk_pages=0)
-    y = torch.empty(1, 2048, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(1, hidden, dtype=torch.bfloat16, device=DEV)
     of = torch.empty(1, 16, 128, dtype=torch.float32, device=DEV)
     run.step(dev["q_nope"], dev["q_pe"], dev["w_uk"], dev["w_uv"], dev["block_table"], dev["seq_lens"],
              w_o=to_dev_bits(layer.w_o), y=y, out_f32=of, fused=fused)

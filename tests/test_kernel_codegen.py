@@ -89,3 +89,92 @@ def test_prompt_path_kernels_use_no_scratch(src, tmp_path):
     assert sizes, src
     for name, size in sizes:
         assert int(size) == 0, (name, size)
+
+
+_VMEM = re.compile(r"^\s*(global_load|global_store|buffer_load|buffer_store|global_atomic)\w*\s+(v\[(\d+):(\d+)\]|v(\d+))")
+_WAIT_VM = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
+_VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _regs(line):
+    out = set()
+    for m in _VREG.finditer(line.split(";")[0]):
+        if m.group(1) is not None:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+        else:
+            out.add(int(m.group(3)))
+    return out
+
+
+def _loop_bodies(body):
+    """Lines of every loop, keyed by its header block, from the compiler's block
+    annotations: a block belongs to the innermost loop named in its comment
+    ("in Loop: Header=BBx_y") or heads one ("Loop Header" / "Parent Loop").
+    Blocks are returned in layout order; the compiler lays a loop out so that
+    this order, taken cyclically, is the order of execution."""
+    blocks = []   # (header or None, [lines])
+    for l in body:
+        m = re.match(r"^(?:\.L(BB\d+_\d+)|; %bb\.\d+):(.*)$", l)
+        if m:
+            own, note = m.group(1), m.group(2)
+            h = re.search(r"in Loop: Header=(BB\d+_\d+)", note)
+            if h:
+                hdr = h.group(1)
+            elif own and ("Loop Header" in note or "Parent Loop" in note):
+                hdr = own
+            else:
+                hdr = None
+            blocks.append((hdr, [l]))
+        elif blocks:
+            blocks[-1][1].append(l)
+    loops = {}
+    for hdr, lines in blocks:
+        if hdr is not None:
+            loops.setdefault(hdr, []).extend(lines)
+    return loops
+
+
+def _staging_loops(body):
+    """Innermost loops that issue non-temporal tile loads, write LDS, hold no
+    matrix instruction and wait with vmcnt(N > 0): the 16-head kernels'
+    staging waves."""
+    out = []
+    for hdr, seg in _loop_bodies(body).items():
+        if any(" nt" in x and "global_load" in x for x in seg) and any("ds_write" in x for x in seg) \
+                and not any("v_mfma" in x for x in seg) \
+                and any(int(m.group(1)) > 0 for x in seg for m in [_WAIT_VM.search(x)] if m):
+            out.append((hdr, seg))
+    return out
+
+
+def test_staging_waits_match_the_loads_left_in_flight(asm):
+    """The 16-head staging waves load tiles with inline assembly the compiler
+    does not count, and wait for them with hand-written vmcnt(N) values.  In
+    each staging loop, taken cyclically, every vmcnt(N) wait must leave in flight
+    exactly the vector-memory instructions issued since the previous wait (the
+    other tile), so N must equal their count; and no instruction between the
+    wait and the next load may touch a destination register of those loads,
+    which are still in flight there."""
+    checked = 0
+    for name, body in _kernels(asm):
+        if "decode_h16" not in name:
+            continue
+        loops = _staging_loops(body)
+        assert loops, name
+        for hdr, seg in loops:
+            waits = [i for i, l in enumerate(seg) if _WAIT_VM.search(l)]
+            for k, w in enumerate(waits):
+                n = int(_WAIT_VM.search(seg[w]).group(1))
+                prev = waits[k - 1]
+                idx = list(range(prev + 1, w)) if prev < w else list(range(prev + 1, len(seg))) + list(range(0, w))
+                issued = [i for i in idx if _VMEM.match(seg[i])]
+                assert n == len(issued), (name, hdr, w, n, len(issued))
+                inflight = set()
+                for i in issued:
+                    inflight |= _regs(seg[i].split(",")[0])
+                j = w + 1
+                while j < len(seg) and not _VMEM.match(seg[j]):
+                    assert not (_regs(seg[j]) & inflight), (name, hdr, j, seg[j].strip())
+                    j += 1
+                checked += 1
+    assert checked >= 14, checked

@@ -12,9 +12,19 @@ output rounded to bf16.
 
 With q_abs and P in fp16 the output meets the tolerance; with both in bf16 (the
 other 16-bit matrix-core type) it exceeds the mean-relative bound.
+
+FP8 (e4m3) operands, for an FP8 latent cache on the FP8 matrix instructions:
+rounded once to e4m3 with an fp32 scale (per head and 32-column block for q_abs,
+per head for P), either operand misses the mean-relative bound by about ten
+times; split into two e4m3 terms (the value and the e4m3 rounding of its
+remainder, both products accumulated in fp32) both operands meet it.  Two FP8
+products take the matrix cores as long as one fp16 product of the same shape
+(twice the rate, twice the work), so FP8 matrix instructions can only save
+operand conversion and LDS traffic, not matrix time.
 """
 import numpy as np
 import pytest
+import torch
 
 import mla_synth
 from oracle import mla_ref
@@ -77,3 +87,40 @@ def test_fp16_operands_meet_the_tolerance(v3_sequence):
 def test_bf16_operands_exceed_the_mean_relative_bound(v3_sequence):
     mx, mean = _emulate(v3_sequence, _bf16, _bf16)
     assert mean > MEAN_REL, (mx, mean)
+
+
+def _e4m3(x):
+    """float32 -> nearest e4m3 value (torch's float8_e4m3fn conversion)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _fp8(group=None):
+    """Round to e4m3 with an fp32 scale (max|x| -> 448) per `group` consecutive
+    values of the last axis (the whole row when None)."""
+    def r(x):
+        x = np.asarray(x, np.float32)
+        shp = x.shape
+        g = shp[-1] if group is None else group
+        xg = x.reshape(shp[:-1] + (shp[-1] // g, g))
+        s = (np.abs(xg).max(axis=-1, keepdims=True) / np.float32(448.0)).astype(np.float32)
+        s = np.where(s == 0, np.float32(1.0), s)
+        return (_e4m3(xg / s) * s).reshape(shp)
+    return r
+
+
+def _two_term(r1):
+    def r(x):
+        hi = r1(x)
+        return hi + r1(np.asarray(x, np.float32) - hi)
+    return r
+
+
+def test_e4m3_operands_exceed_the_mean_relative_bound(v3_sequence):
+    _, mean_q = _emulate(v3_sequence, _fp8(32), _f16)
+    _, mean_p = _emulate(v3_sequence, _f16, _fp8())
+    assert mean_q > 5 * MEAN_REL and mean_p > 5 * MEAN_REL, (mean_q, mean_p)
+
+
+def test_two_term_e4m3_operands_meet_the_tolerance(v3_sequence):
+    mx, mean = _emulate(v3_sequence, _two_term(_fp8(32)), _two_term(_fp8()))
+    assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
