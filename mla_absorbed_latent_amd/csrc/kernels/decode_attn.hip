@@ -387,10 +387,12 @@ struct LoaderInt4Reg {
     }
     return page >= 0;
   }
-  // Byte j of nibble word w (elements 2j, 2j+1) -> two fp16 values q * s + z
-  // (symmetric: (q - 8) * s).
+  // Byte j of nibble word w (elements 2j, 2j+1) -> two fp16 values (q - 8) * s + z8,
+  // z8 = z + 8 s (symmetric: (q - 8) * s).  Centring the code keeps the fp16
+  // zero point near the group's midpoint, small for centred data, so its
+  // rounding (and the scale's) moves a value by far less than with z itself.
   static __device__ __forceinline__ uint32_t nib2(uint32_t w, int j, half2v s2, half2v z2) {
-    constexpr float kBias = kSym ? -1032.0f : -1024.0f;
+    constexpr float kBias = -1032.0f;
     const half2v bias = {(_Float16)kBias, (_Float16)kBias};
     const uint32_t byte = (w >> (8 * j)) & 0xffu;
     // (element 2j, element 2j+1) = (low nibble, high nibble) as fp16 1024 + q
@@ -399,9 +401,10 @@ struct LoaderInt4Reg {
     if constexpr (kSym) return __builtin_bit_cast(uint32_t, qv * s2);
     else return __builtin_bit_cast(uint32_t, qv * s2 + z2);
   }
-  __device__ __forceinline__ _Float16 zero_h(int i) const {
+  // fp16 zero point of latent chunk i (scale s): z + 8 s, formed in fp32.
+  __device__ __forceinline__ _Float16 zero_h(int i, float s) const {
     if constexpr (kSym) return (_Float16)0.0f;
-    else return (_Float16)z[i];
+    else return (_Float16)fmaf(8.0f, s, z[i]);
   }
   // Stepwise issue (one pass, 128-head pipeline): begin() sets this lane's page
   // and row; load_step<I> (after store_step<I>) reloads chunk I / 2 once its
@@ -440,7 +443,7 @@ struct LoaderInt4Reg {
     constexpr int kcx = I / 2, p = kcx / 9, k = kcx % 9;
     u32x2 cur;
     if constexpr (k < 8) {
-      const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k);
+      const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k, s[9 * p + k]);
       const half2v s2 = {sh, sh}, z2 = {zh, zh};
       const uint32_t w = n[8 * p + k];
       constexpr int j0 = 2 * (I % 2);
@@ -471,7 +474,7 @@ struct LoaderInt4Reg {
     for (int p = 0; p < kPass; ++p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k);
+        const _Float16 sh = (_Float16)s[9 * p + k], zh = zero_h(8 * p + k, s[9 * p + k]);
         const half2v s2 = {sh, sh}, z2 = {zh, zh};
         const uint32_t w = n[8 * p + k];
         u32x4 v;
@@ -513,9 +516,10 @@ __device__ __forceinline__ int wide_tok() {
 }
 
 // Eight packed nibbles (byte b: element 2b in its low nibble, 2b + 1 in its high
-// one) -> eight fp16 values q * s + z, as four fp16 pairs.  Byte permutes place
-// each nibble under the constant 0x64 high byte (fp16 1024 + q, exactly).
-// Symmetric INT4 (kSym): (q - 8) * s, no zero point.
+// one) -> eight fp16 values (q - 8) * s + z8, as four fp16 pairs, where z8 is
+// the zero point plus 8 s (near the group's midpoint, see LoaderInt4Reg::nib2).
+// Byte permutes place each nibble under the constant 0x64 high byte (fp16
+// 1024 + q, exactly).  Symmetric INT4 (kSym): (q - 8) * s, no zero point.
 template <bool kSym = false>
 __device__ __forceinline__ u32x4 nib8_to_f16(uint32_t w, half2v s2, half2v z2) {
   const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
@@ -523,7 +527,7 @@ __device__ __forceinline__ u32x4 nib8_to_f16(uint32_t w, half2v s2, half2v z2) {
   const uint32_t x1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // lo.b2 hi.b2 lo.b3 hi.b3
   // Each pair is formed in a scalar: hipcc's __builtin_bit_cast of a vector
   // element (r[j]) reads element 0 whatever the index.
-  constexpr float kBias = kSym ? -1032.0f : -1024.0f;
+  constexpr float kBias = -1032.0f;
   const half2v bias = {(_Float16)kBias, (_Float16)kBias};
   auto cv = [&](uint32_t h) {
     const half2v q = __builtin_bit_cast(half2v, h) + bias;
@@ -787,7 +791,7 @@ struct LoaderInt4Wide {
     if constexpr (!kSym) zt = quad_transpose(zq, c4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const _Float16 sh = (_Float16)st[i], zh = (_Float16)zt[i];
+      const _Float16 sh = (_Float16)st[i], zh = kSym ? (_Float16)0.0f : (_Float16)fmaf(8.0f, st[i], zt[i]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = (n[i][j] & ~blend) | (n[i][j ^ 2] & blend);

@@ -4,12 +4,13 @@ edges of its documented input range, through the C ABI, against the fp64 oracle.
 * Softmax: the 128-head kernel fixes each head's reference maximum at the first
   tile of a work item and redoes the item against exact maxima when a later
   tile exceeds it by more than 2^15; the 16-head kernel rescales its running
-  sums only when a wave's maximum grows by more than 2^8.  Queries scaled by 16
-  spread the scores over tens of log2 units, so the maximum arrives late and
-  both branches run; a sequence whose first tile holds rows scaled by 4 puts
-  the maximum first and lets later scores fall by far more than 24 log2 units
-  (their fp16 probabilities underflow to zero).  Each case checks, on the CPU
-  from the oracle's own scores, that it really exercises the branch.
+  sums only when a wave's maximum grows by more than 2^8.  Queries scaled by 6
+  spread the scores over about 50 log2 units (35 nats), so the maximum arrives
+  late and both branches run; a sequence whose first tile holds rows scaled by
+  4 puts the maximum first and lets later scores fall by more than 24 log2
+  units for some heads (their fp16 probabilities underflow to zero), the shape
+  of an attention sink.  Each case checks, on the CPU from the oracle's own
+  scores, that it really exercises the branch.
 * Dequantisation range: caches shrunk by 2^-8, latent groups shrunk to
   max|x| < 2^-7 inside normal tokens, and INT4 groups whose zero point is about
   150 times their scale.
@@ -103,16 +104,17 @@ def _check(case, cache_dtype, chunk):
 
 # ------------------------------------------------------------------ softmax branches
 def _spread_case(H, case_id=60):
-    """Queries scaled by 16: scores span tens of log2 units; the maximum arrives late."""
+    """Queries scaled by 6: scores span about 50 log2 units; the maximum arrives late."""
     case = mla_synth.small_decode(case_id=case_id, H=H, seq_lens=[1500, 900])
-    case.q_nope = _scaled_bits(case.q_nope, 16.0)
-    case.q_pe = _scaled_bits(case.q_pe, 16.0)
+    case.q_nope = _scaled_bits(case.q_nope, 6.0)
+    case.q_pe = _scaled_bits(case.q_pe, 6.0)
     return case
 
 
 def _early_max_case(H, case_id=61):
-    """As above, and the first 32 rows of every sequence scaled by 4: the maximum
-    sits in the first tile and later scores fall by far more than 24 log2 units."""
+    """As above, and the first 32 rows of every sequence scaled by 4: for most
+    heads the maximum sits in the first tile, and for some later scores fall by
+    more than 24 log2 units."""
     case = _spread_case(H, case_id)
 
     def fn(b, c, r):
@@ -128,12 +130,10 @@ def _early_max_case(H, case_id=61):
 @pytest.mark.parametrize("H", [16, 128])
 def test_late_maximum(H, cache_dtype):
     case = _spread_case(H)
-    s = _log2_scores(case, 0, cache_dtype)
-    if H == 128:
-        assert _h128_redo_taken(s), "case does not reach the redo branch"
-    else:
-        assert _h16_rescale_taken(s), "case does not reach the rescale branch"
-    _note("late max H=%d dtype=%d spread %.1f log2" % (H, cache_dtype, float(np.ptp(s))))
+    scores = [_log2_scores(case, b, cache_dtype) for b in range(case.B)]
+    taken = _h128_redo_taken if H == 128 else _h16_rescale_taken
+    assert any(taken(s) for s in scores), "case does not reach the branch"
+    _note("late max H=%d dtype=%d spread %.1f log2" % (H, cache_dtype, float(np.ptp(scores[0]))))
     _check(case, cache_dtype, chunk=1000)      # one work item per sequence
 
 
@@ -143,8 +143,8 @@ def test_early_maximum_then_falling_scores(H, cache_dtype):
     case = _early_max_case(H)
     s = _log2_scores(case, 0, cache_dtype)
     fall = s[:, :32].max(axis=1) - s[:, 32:].max(axis=1)
-    assert np.all(fall > 24.0), float(fall.min())
-    _note("early max H=%d dtype=%d min fall %.1f log2" % (H, cache_dtype, float(fall.min())))
+    assert np.any(fall > 24.0) and np.mean(fall > 0) > 0.5, (float(fall.max()), float(np.mean(fall > 0)))
+    _note("early max H=%d dtype=%d largest fall %.1f log2" % (H, cache_dtype, float(fall.max())))
     _check(case, cache_dtype, chunk=1000)
 
 
@@ -220,7 +220,7 @@ def test_item_range_past_the_table_is_empty(H):
     items = torch.tensor([[0, 1 << 25, 4, 0],
                           [1, mp + 1, 2, 1],
                           [0, 3, 1, 2],                 # page 3 of a 4-page sequence: tokens 192..199
-                          [1, 2, 2, 3],                 # starts past sequence 1's 130 tokens
+                          [1, 3, 1, 3],                 # page 3: past sequence 1's 130 tokens (pages 0-2)
                           [1, 0, (1 << 31) - 1, 4]],    # whole sequence 1, n_pages clipped
                          dtype=torch.int32, device=DEV)
     o_part = torch.full((5, H, 512), float("nan"), dtype=torch.float16, device=DEV)
