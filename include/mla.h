@@ -309,6 +309,24 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
 /* n_tokens * (576 + H * 192) * 4 bytes: the fp32 projection results.        */
 size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
 
+/* ------------------------------------------------------------------ layer front, no allocation
+ * mla_layer_front_noalloc: mla_layer_front (same arguments, definitions and
+ * results, bit for bit) for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The fp32 projections live in a 16 MiB scratch array that the
+ * library holds on every GPU it runs on until the process ends, instead of a
+ * caller workspace; the call itself allocates nothing.
+ *   n_tokens * (576 + H * 192) * 4 <= 16 MiB, i.e. n_tokens <= 1,149 (H = 16)
+ *   or <= 166 (H = 128); larger n_tokens gives MLA_ERR_WORKSPACE.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU
+ * (different streams, or host threads without ordering) race and must not be
+ * issued.  The first call on a device looks up the scratch's device address
+ * (no allocation); make it before capturing a graph.                        */
+mla_status mla_layer_front_noalloc(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
+                                   const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                   uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe,
+                                   int32_t n_tokens, hipStream_t stream);
+
 /* ------------------------------------------------------------------ residual
  * mla_out_residual: close a layer whose attention output is per head (as
  * mla_prefill_attn writes it): the output projection and the residual sum,

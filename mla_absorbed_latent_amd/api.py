@@ -245,6 +245,25 @@ def layer_front(cfg: Config, x, w_q, w_dkv, positions, workspace, q_nope, q_pe, 
            "mla_layer_front")
 
 
+def layer_front_noalloc(cfg: Config, x, w_q, w_dkv, positions, q_nope, q_pe, c_kv, k_pe,
+                        rms_eps: float = 1e-6, rope_base: float = 10000.0) -> None:
+    """layer_front with the projections in the library's own scratch (mla_layer_front_noalloc)."""
+    T, hidden, H = int(x.shape[0]), int(x.shape[1]), cfg.num_heads
+    _need(x, "x", (T, hidden), 2)
+    _need(w_q, "w_q", (H * 192, hidden), 2)
+    _need(w_dkv, "w_dkv", (576, hidden), 2)
+    _need(positions, "positions", (T,), 4)
+    _need(q_nope, "q_nope", (T, H, 128), 2)
+    _need(q_pe, "q_pe", (T, H, 64), 2)
+    _need(c_kv, "c_kv", (T, 512), 2)
+    _need(k_pe, "k_pe", (T, 64), 2)
+    _check(L.load().mla_layer_front_noalloc(C.byref(cfg), _dev(x, "x"), hidden, _dev(w_q, "w_q"),
+                                            _dev(w_dkv, "w_dkv"), _dev(positions, "positions"), float(rms_eps),
+                                            float(rope_base), _dev(q_nope, "q_nope"), _dev(q_pe, "q_pe"),
+                                            _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"), T, _stream()),
+           "mla_layer_front_noalloc")
+
+
 def prefill_workspace_bytes(cfg: Config, seq_len: int) -> int:
     return int(L.load().mla_prefill_workspace_bytes(C.byref(cfg), int(seq_len)))
 

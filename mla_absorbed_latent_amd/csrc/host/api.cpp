@@ -244,6 +244,26 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
                                           workspace, q_nope, q_pe, c_kv, k_pe, n_tokens, stream));
 }
 
+mla_status mla_layer_front_noalloc(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
+                                   const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                   uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe,
+                                   int32_t n_tokens, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (n_tokens < 0 || hidden <= 0 || hidden % 8 != 0) return MLA_ERR_VALUE;
+  if (!(rms_eps > 0.f) || !std::isfinite(rms_eps) || !(rope_base > 1.f) || !std::isfinite(rope_base))
+    return MLA_ERR_VALUE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!x || !w_q || !w_dkv || !positions || !q_nope || !q_pe || !c_kv || !k_pe) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_dkv) || !aligned16(positions) || !aligned16(q_nope) ||
+      !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe))
+    return MLA_ERR_ALIGN;
+  if (mla_layer_front_workspace_bytes(cfg, n_tokens) > mla::kFrontScratchBytes) return MLA_ERR_WORKSPACE;
+  if ((s = check_device()) != MLA_OK) return s;
+  return launched(mla::launch_layer_front_noalloc(cfg->num_heads, x, hidden, w_q, w_dkv, positions, rms_eps,
+                                                  rope_base, q_nope, q_pe, c_kv, k_pe, n_tokens, stream));
+}
+
 mla_status mla_out_residual(const mla_config* cfg, const uint16_t* attn_out, const uint16_t* w_o, int32_t hidden,
                             const uint16_t* x_in, uint16_t* x_out, float* workspace, size_t workspace_bytes,
                             int32_t n_tokens, hipStream_t stream) {

@@ -20,10 +20,21 @@
 // 64 tokens or more (a prompt: compute-bound, on the matrix cores); then
 // front_finish applies the norm, the rotation and the bf16 rounding (the norm
 // and the angles in double precision).
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
+
+// Device scratch of launch_layer_front_noalloc: the fp32 projections that
+// launch_layer_front otherwise keeps in the caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; every call on a
+// GPU shares it.  The projections write every element they later read, so it
+// needs no clearing between calls.
+__device__ __attribute__((aligned(256))) static float scratch[kFrontScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int kTokChunk = 16;      // tokens accumulated together per pass over a weight row
@@ -245,6 +256,47 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
   hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens), dim3(256), 0, stream, kv, q, positions,
                      num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the name is a host-side stand-in; only this address is valid on the GPU).
+static hipError_t front_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (q == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(q);
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_layer_front_noalloc(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q,
+                                      const uint16_t* w_dkv, const int32_t* positions, float rms_eps,
+                                      float rope_base, uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv,
+                                      uint16_t* k_pe, int n_tokens, hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  if ((size_t)n_tokens * (size_t)(kDc + kDr + num_heads * (kDn + kDr)) * sizeof(float) > kFrontScratchBytes)
+    return hipErrorInvalidValue;     // the host entry point rejects this first
+  float* ws = nullptr;
+  const hipError_t e = front_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_layer_front(num_heads, x, hidden, w_q, w_dkv, positions, rms_eps, rope_base, ws, q_nope, q_pe,
+                            c_kv, k_pe, n_tokens, stream);
 }
 
 }  // namespace mla

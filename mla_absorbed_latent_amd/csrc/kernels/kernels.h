@@ -37,6 +37,14 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
                               uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
                               hipStream_t stream);
 
+// launch_layer_front with the fp32 projections in the library's per-device
+// scratch (kFrontScratchBytes) instead of a caller workspace; allocates nothing.
+constexpr size_t kFrontScratchBytes = size_t(16) << 20;
+hipError_t launch_layer_front_noalloc(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q,
+                                      const uint16_t* w_dkv, const int32_t* positions, float rms_eps,
+                                      float rope_base, uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv,
+                                      uint16_t* k_pe, int n_tokens, hipStream_t stream);
+
 hipError_t launch_out_residual(int num_heads, const uint16_t* attn_out, const uint16_t* w_o, int hidden,
                                const uint16_t* x_in, uint16_t* x_out, float* workspace, int n_tokens,
                                hipStream_t stream);

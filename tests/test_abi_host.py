@@ -238,3 +238,24 @@ def test_append_absorb_validation(lib):
     assert call(q=None) == L.MLA_ERR_NULL
     assert call(pool=odd) == L.MLA_ERR_ALIGN
     assert call(pool=None, n=0, q=None, b=0) == L.MLA_OK
+
+
+def test_layer_front_noalloc_validation(lib):
+    """Host-side checks of the allocation-free front: the token count is bounded by
+    the library's 16 MiB scratch (MLA_ERR_WORKSPACE beyond it), before any HIP call."""
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    f = lib.mla_layer_front_noalloc
+    for H, t_max in ((16, 1149), (128, 166)):
+        cfg = api.config(H)
+        assert api.layer_front_workspace_bytes(cfg, t_max) <= 16 << 20 < api.layer_front_workspace_bytes(cfg, t_max + 1)
+
+        def call(x=fake, hidden=2048, eps=1e-6, base=1e4, n=4):
+            return f(C.byref(cfg), x, hidden, fake, fake, fake, eps, base, fake, fake, fake, fake, n, None)
+
+        assert call(n=t_max + 1) == L.MLA_ERR_WORKSPACE
+        assert call(hidden=2044) == L.MLA_ERR_VALUE
+        assert call(n=-1) == L.MLA_ERR_VALUE
+        assert call(eps=0.0) == L.MLA_ERR_VALUE
+        assert call(x=None) == L.MLA_ERR_NULL
+        assert call(x=odd) == L.MLA_ERR_ALIGN
+        assert call(x=None, n=0) == L.MLA_OK        # no-op
