@@ -15,7 +15,9 @@ data with the workload's shapes (no checkpoint or dataset is read).
 Prints ONE JSON line.  `value` is the latent-cache bytes the step attends over
 divided by the step time (GB/s).  `roofline` is for the dominant kernel,
 mla_decode_attn, timed alone with HIP events on the stream it runs on;
-`cpu_baseline` times the CPU oracle (fp64, as it stands) on a bounded sample.
+`cpu_baseline` times the CPU oracle's float32 form on a bounded sample (median
+of three runs).  Before --warmup, untimed steps run until the card's clock has
+settled under the load (at least --settle-s seconds; recorded in the line).
 """
 from __future__ import annotations
 
@@ -56,36 +58,83 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(case, cache_dtype, budget_s=15.0):
-    """Time the oracle's absorbed decode (fp64 numpy) on whole sequences of the
-    workload until ~budget_s of CPU work; report GB/s of latent cache read."""
+def _host_info():
+    """CPU model, the threads numpy's BLAS uses, and which BLAS it is."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            blas = "%s %s" % (info[0].get("internal_api"), info[0].get("version"))
+            threads = int(info[0].get("num_threads", threads))
+    except Exception:       # threadpoolctl missing: keep the affinity count
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(case, cache_dtype, budget_s=20.0):
+    """Time the oracle's float32 absorbed decode (numpy with its BLAS, all host
+    cores) on whole sequences of the workload; quantised caches include
+    dequantising the sample.  The sample is sized so that three runs take about
+    budget_s; the median of the three is reported as GB/s of latent cache."""
     from oracle import mla_ref, quant
-    wk = mla_ref.bf16_to_f64(case.w_uk)
-    wv = mla_ref.bf16_to_f64(case.w_uv)
+    f32 = np.float32
+    wk = mla_ref.bf16_to_f64(case.w_uk).astype(f32)
+    wv = mla_ref.bf16_to_f64(case.w_uv).astype(f32)
     bpt = quant.token_bytes(cache_dtype)
-    done_tokens, t_total, seqs = 0, 0.0, 0
-    for b in range(case.B):
+
+    def prepare(b):
         c_bits, r_bits = case.seq_cache(b)
+        qn = mla_ref.bf16_to_f64(case.q_nope[b]).astype(f32)
+        qp = mla_ref.bf16_to_f64(case.q_pe[b]).astype(f32)
         if cache_dtype == 0:
-            c, r = mla_ref.bf16_to_f64(c_bits), mla_ref.bf16_to_f64(r_bits)
-            t0 = time.perf_counter()
+            return (qn, qp, mla_ref.bf16_to_f64(c_bits).astype(f32), mla_ref.bf16_to_f64(r_bits).astype(f32))
+        return (qn, qp, quant.encode_tokens(cache_dtype, c_bits, r_bits))
+
+    def one(item):
+        if cache_dtype == 0:
+            qn, qp, c, r = item
         else:
-            t0 = time.perf_counter()
-            f = quant.encode_tokens(cache_dtype, c_bits, r_bits)
-            c32, r32 = quant.dequant_fields(cache_dtype, f)
-            c, r = c32.astype(np.float64), r32.astype(np.float64)
-        mla_ref.absorbed_decode(mla_ref.bf16_to_f64(case.q_nope[b]), mla_ref.bf16_to_f64(case.q_pe[b]),
-                                c, r, wk, wv, case.softmax_scale)
-        t_total += time.perf_counter() - t0
-        done_tokens += int(case.seq_lens[b])
-        seqs += 1
-        if t_total >= budget_s:
+            qn, qp, fields = item
+            c, r = quant.dequant_fields(cache_dtype, fields)
+        mla_ref.absorbed_decode_f32(qn, qp, c, r, wk, wv, case.softmax_scale)
+
+    order = sorted(range(case.B), key=lambda b: -int(case.seq_lens[b]))[: max(1, case.B // 2)][::-1]
+    sample, t_one = [], 0.0
+    for b in order:                       # grow the sample until one run costs budget_s / 3
+        item = prepare(b)
+        t0 = time.perf_counter()
+        one(item)
+        t_one += time.perf_counter() - t0
+        sample.append((b, item))
+        if t_one >= budget_s / 3:
             break
-    cores = len(os.sched_getaffinity(0))
-    return {"value": round(done_tokens * bpt / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _, item in sample:
+            one(item)
+        runs.append(time.perf_counter() - t0)
+    t_med = float(np.median(runs))
+    tokens = int(sum(int(case.seq_lens[b]) for b, _ in sample))
+    model, blas, threads = _host_info()
+    return {"value": round(tokens * bpt / t_med / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d sequences (%d tokens), fp64 numpy absorbed decode incl. W_UK/W_UV, %.1f s"
-                      % (seqs, case.B, done_tokens, t_total)}
+            "sample": "%d of %d sequences (%d tokens), float32 numpy absorbed decode incl. W_UK/W_UV%s; "
+                      "median of 3 runs (%s s)" % (len(sample), case.B, tokens,
+                                                    "" if cache_dtype == 0 else " and dequantisation",
+                                                    ", ".join("%.2f" % r for r in runs)),
+            "cpu_model": model, "blas": blas,
+            "tflops": round(2176.0 * case.H * tokens / t_med / 1e12, 5)}
 
 
 def prefill_flops(case):
@@ -156,6 +205,7 @@ def bench_prefill(args):
         def step():
             api.prefill_attn(cfg, q_nope, q_pe, c, r, w_uk, w_uv, ws, out, lse)
 
+    settled = settle(torch, step, min_s=args.settle_s, chunk=5) if args.settle_s > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -196,6 +246,7 @@ def bench_prefill(args):
                      "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS_16, "unit": "TFLOP/s",
                      "frac": round(tf / MFMA_PEAK_TFLOPS_16, 4), "traffic": None, "launch_ms": round(call_ms, 5),
                      "flops_per_launch": flops},
+        "settle": settled,
     }
     if not args.no_cpu_baseline and not proj:
         log("timing the CPU oracle on a sample ...")
@@ -203,34 +254,101 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def _bench_lib():
+    from mla_absorbed_latent_amd import _lib
+    return _lib.load()
+
+
+def clock_probe_ghz(torch, dev):
+    """The shader clock now: a one-wave spin timed by the shader-clock counter
+    against the constant 100 MHz counter (mla_bench_clock_probe)."""
+    import ctypes as C
+    out = torch.zeros(3, dtype=torch.int64, device=dev)
+    err = _bench_lib().mla_bench_clock_probe(200000, C.c_void_p(out.data_ptr()),
+                                             C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if err:
+        raise RuntimeError("mla_bench_clock_probe: hipError %d" % err)
+    torch.cuda.synchronize()
+    cyc, ticks, _ = (int(v) for v in out.cpu())
+    return round(cyc / ticks * 0.1, 3) if ticks > 0 else None
+
+
 def measured_peaks(torch, dev):
-    """Achievable rates on this card in this run (context for the vendor peaks):
-    a 1 GiB device-to-device copy (bytes read + written) and a 8192^3 fp16 GEMM
-    (hipBLASLt through torch.mm)."""
-    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)        # 1 GiB
-    dst = torch.empty_like(src)
-    a = torch.randn(8192, 8192, device=dev).half()
-    b = torch.randn(8192, 8192, device=dev).half()
+    """Achievable rates on this card in this run (context for the vendor peaks),
+    from the library's own microbenchmarks: a 4 GiB streaming read with 16-byte
+    loads, and independent chains of 32x32x16 fp16 / bf16 MFMAs on registers over
+    the whole chip (each: best of 5 after a warm-up)."""
+    import ctypes as C
+    lib = _bench_lib()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    blocks = 8192
+    red = torch.empty(blocks, dtype=torch.int32, device=dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
-        dst.copy_(src)
-        torch.mm(a, b)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(20):
-        dst.copy_(src)
-    ev1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 4 * 20 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
-    ev0.record()
-    for _ in range(20):
-        torch.mm(a, b)
-    ev1.record()
-    torch.cuda.synchronize()
-    tflops = 2.0 * 8192 ** 3 * 20 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
-    del src, dst, a, b
-    return {"hbm_copy_gbs": round(copy_gbs, 1), "mfma_f16_tflops": round(tflops, 1),
-            "how": "1 GiB fp32 device copy (read + write bytes); torch.mm fp16 8192^3; 20 reps each after warm-up"}
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = []
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            best.append(ev0.elapsed_time(ev1) * 1e-3)
+        return min(best), float(np.median(best))
+
+    def read():
+        err = lib.mla_bench_stream_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(red.data_ptr()), blocks, stream)
+        if err:
+            raise RuntimeError("mla_bench_stream_read: hipError %d" % err)
+
+    t_read, t_read_med = timed(read)
+    read_clock = clock_probe_ghz(torch, dev)
+    del buf, red
+    wgs, iters = 512, 4000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    flop = 2.0 * 32 * 32 * 16 * 8 * iters * 4 * wgs
+    res = {}
+    for name, bf in (("f16", 0), ("bf16", 1)):
+        def mm(bf=bf):
+            err = lib.mla_bench_mfma_loop(bf, iters, wgs, C.c_void_p(out.data_ptr()), stream)
+            if err:
+                raise RuntimeError("mla_bench_mfma_loop: hipError %d" % err)
+        t, _ = timed(mm)
+        res[name] = flop / t / 1e12
+        res[name + "_clock"] = clock_probe_ghz(torch, dev)
+    return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "hbm_read_gbs_median": round(nbytes / t_read_med / 1e9, 1),
+            "mfma_f16_tflops": round(res["f16"], 1), "mfma_bf16_tflops": round(res["bf16"], 1),
+            "clock_ghz_after": {"read": read_clock, "mfma_f16": res["f16_clock"], "mfma_bf16": res["bf16_clock"]},
+            "how": "mla_bench_stream_read over 4 GiB (16-byte non-temporal loads, 8192 work-groups); "
+                   "mla_bench_mfma_loop: 512 work-groups x 4 waves x 8 independent 32x32x16 chains x 4000; "
+                   "best of 5 after one warm-up"}
+
+
+def settle(torch, step, min_s=1.0, max_s=6.0, chunk=20):
+    """Run untimed steps until the card's clock has settled under this load:
+    at least min_s of wall time and two consecutive chunks of `chunk` steps
+    within 1.5 % of each other (at most max_s).  From idle the clock takes some
+    tens of milliseconds to ramp up, so runs with a short warm-up read slow."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    ms, n = [], 0
+    while True:
+        ev0.record()
+        for _ in range(chunk):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        n += chunk
+        ms.append(ev0.elapsed_time(ev1) / chunk)
+        el = time.time() - t0
+        if el >= max_s or (el >= min_s and len(ms) >= 2 and abs(ms[-1] - ms[-2]) <= 0.015 * ms[-1]):
+            break
+    return {"seconds": round(time.time() - t0, 3), "steps": n,
+            "first_chunks_ms_per_step": [round(v, 5) for v in ms[:3]],
+            "last_chunks_ms_per_step": [round(v, 5) for v in ms[-2:]]}
 
 
 def recorded_traffic(workload, cache_dtype):
@@ -257,10 +375,12 @@ def recorded_traffic(workload, cache_dtype):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The card runs this workload at its power limit, and its clock settles only
-    # after some tens of milliseconds of sustained load: warm up for ~0.3 s.
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    # From idle the card's clock takes some tens of milliseconds of sustained
+    # load to ramp up: untimed steps run first until it has settled (recorded
+    # in the JSON line), whatever --warmup is.
+    ap.add_argument("--settle-s", type=float, default=1.0)
     ap.add_argument("--workload", default="v3_decode", choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--cache-dtype", default="bf16", choices=sorted(DTYPES))
     ap.add_argument("--chunk-pages", type=int, default=0)
@@ -346,6 +466,8 @@ def main():
         next_pool()
         run.step(q_nope, q_pe, w_uk, w_uv, block_table, seq_lens, new_c, new_r, new_s, keep_latent=False)
 
+    clock_idle = clock_probe_ghz(torch, dev)
+    settled = settle(torch, step, min_s=args.settle_s) if args.settle_s > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -357,6 +479,7 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    clock_after = clock_probe_ghz(torch, dev)
 
     # ---- the dominant kernel alone: mla_decode_attn, events on its own stream
     stream = torch.cuda.current_stream()
@@ -379,6 +502,9 @@ def main():
     comb_ms = ev0.elapsed_time(ev1) / args.steps
 
     achievable = measured_peaks(torch, dev)
+    traffic = recorded_traffic(args.workload, args.cache_dtype)
+    traffic_src = ("recorded: profiles/decode_attn_%s_%s.md (rocprofv3 FETCH_SIZE + WRITE_SIZE at this kernel "
+                   "source hash)" % (args.workload, args.cache_dtype)) if traffic is not None else None
     bpt = api.cache_bytes_per_token(cfg)
     latent_bytes = case.total_tokens * bpt
     flops = 2176.0 * case.H * case.total_tokens
@@ -411,13 +537,16 @@ def main():
         "pct_roofline_attn": round(100.0 * roof_t / (t_attn_ms * 1e-3), 2),
         "roofline": {"bound": "hbm", "kernel": "mla_decode_attn", "achieved": round(attn_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload, args.cache_dtype), "launch_ms": round(attn_ms, 5),
+                     "traffic": traffic, "traffic_source": traffic_src, "launch_ms": round(attn_ms, 5),
                      "bytes_per_launch": latent_bytes,
                      "mfma_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16, 4),
-                     "frac_of_measured_hbm": round(attn_gbs / achievable["hbm_copy_gbs"], 4)},
+                     "frac_of_measured_hbm": round(attn_gbs / achievable["hbm_read_gbs"], 4),
+                     "mfma_frac_of_measured": round(flops / (attn_ms * 1e-3) / 1e12 / achievable["mfma_f16_tflops"], 4)},
         "measured_peaks": achievable,
         "pool_copies": len(pools),
+        "settle": settled,
+        "shader_clock_ghz": {"idle_before": clock_idle, "right_after_timed_steps": clock_after},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")

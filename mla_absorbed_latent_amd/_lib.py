@@ -1,4 +1,5 @@
-"""ctypes view of the C ABI in include/mla.h.  Argument marshalling only.
+"""ctypes view of the C ABI in include/mla.h (and the measurement helpers of
+include/mla_bench.h).  Argument marshalling only.
 
 Loading never falls back to anything: if the shared library is missing the
 import fails with an error that says how to build it.
@@ -25,7 +26,7 @@ class WorkItem(C.Structure):
     _fields_ = [("seq", C.c_int32), ("first_page", C.c_int32), ("n_pages", C.c_int32), ("out_row", C.c_int32)]
 
 
-# Every symbol include/mla.h declares, with its C signature.
+# Every symbol include/*.h declares, with its C signature.
 _P = C.c_void_p
 _CFG = C.POINTER(MlaConfig)
 SIGNATURES = {
@@ -54,6 +55,10 @@ SIGNATURES = {
     "mla_out_residual": (C.c_int, [_CFG, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]),
     "mla_append_absorb_q": (C.c_int, [_CFG, _P, C.c_int64, _P, _P, _P, C.c_int32, _P, _P, _P, _P, C.c_int32, _P]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
+    # include/mla_bench.h (measurement helpers)
+    "mla_bench_stream_read": (C.c_int32, [_P, C.c_int64, _P, C.c_int32, _P]),
+    "mla_bench_mfma_loop": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, _P, _P]),
+    "mla_bench_clock_probe": (C.c_int32, [C.c_int32, _P, _P]),
     "mla_last_hip_error": (C.c_int32, []),
 }
 

@@ -131,6 +131,19 @@ def absorbed_decode(q_nope, q_pe, c, r, w_uk, w_uv, scale=None):
     return out_proj(o_lat, w_uv), lse, o_lat
 
 
+def absorbed_decode_f32(q_nope, q_pe, c, r, w_uk, w_uv, scale=None):
+    """absorbed_decode with every array in float32 (numpy's BLAS), the form the
+    CPU baseline times; the float64 absorbed_decode above is the parity
+    reference.  Returns out [H,128] float32."""
+    f = np.float32
+    scale = f(softmax_scale() if scale is None else scale)
+    q_lat = np.einsum("hd,hdc->hc", q_nope.astype(f), w_uk.astype(f))
+    s = scale * (q_lat @ c.astype(f, copy=False).T + q_pe.astype(f) @ r.astype(f, copy=False).T)
+    p = _softmax(s)
+    o_lat = p @ c.astype(f, copy=False)
+    return np.einsum("hc,hdc->hd", o_lat, w_uv.astype(f))
+
+
 # --------------------------------------------------------------------------
 # Split-KV partials and their exact merge.  The pages stream history through a
 # running max / running sum (the TileLang accumulators of [Budget] part C); the

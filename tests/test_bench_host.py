@@ -34,3 +34,14 @@ def test_prefill_cpu_baseline_fields():
     b = bench.cpu_baseline_prefill(case, budget_s=0.01)
     assert b["kind"] == "oracle" and b["unit"] == "TFLOP/s" and b["value"] > 0 and b["cores"] >= 1
     assert "64" in b["sample"]
+
+
+def test_decode_cpu_baseline_fields():
+    """The decode CPU baseline: float32 oracle, median of three runs, with the
+    host's CPU model and BLAS recorded (bf16 and a quantised cache)."""
+    for dt in (0, 1):
+        case = mla_synth.small_decode(case_id=33, H=16, seq_lens=[300, 200, 100, 50], normalise=dt == 0)
+        b = bench.cpu_baseline(case, dt, budget_s=0.01)
+        assert b["kind"] == "oracle" and b["unit"] == "GB/s" and b["value"] > 0 and b["cores"] >= 1
+        assert "median of 3" in b["sample"] and "float32" in b["sample"]
+        assert b["cpu_model"] and b["blas"]

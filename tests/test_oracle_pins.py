@@ -17,6 +17,7 @@ import torch
 
 import oracle
 from oracle import mla_ref
+import mla_synth
 
 
 def _rand_case(rng, H=2, dn=4, dc=8, dr=4, dv=4, L=5):
@@ -275,3 +276,16 @@ class _Broken:
 def test_planted_mistakes_fail_the_pins(mistake):
     assert _pins_hold(mla_ref)
     assert not _pins_hold(_Broken(mistake))
+
+
+def test_float32_twin_matches_the_float64_oracle():
+    """The CPU baseline's float32 form of the absorbed decode agrees with the
+    float64 oracle to float32 round-off (it is timed, never used as a reference)."""
+    case = mla_synth.small_decode(case_id=31, H=16, seq_lens=[700])
+    c_bits, r_bits = case.seq_cache(0)
+    f = mla_ref.bf16_to_f64
+    args = (f(case.q_nope[0]), f(case.q_pe[0]), f(c_bits), f(r_bits), f(case.w_uk), f(case.w_uv), case.softmax_scale)
+    ref, _, _ = mla_ref.absorbed_decode(*args)
+    got = mla_ref.absorbed_decode_f32(*args)
+    assert got.dtype == np.float32
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
