@@ -1494,6 +1494,410 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   }
 }
 
+// ===========================================================================
+// H = 128, bf16 cache: eight waves per work-group, two per SIMD
+// ===========================================================================
+// A single wave per SIMD (decode_h128 above) leaves the matrix cores idle
+// while it runs its softmax, its staging and its barriers.  Here each SIMD
+// holds one score wave (waves 0-3) and one value wave (waves 4-7), and every
+// 32-token tile takes two phases separated by barriers:
+//   phase 1  score wave w: S^T for heads 32w..32w+31 over all 576 columns (36 x
+//            mfma 32x32x16; K from the LDS tile; Q^T of the first kQReg2
+//            k-steps in VGPRs, the rest from LDS), softmax against the fixed
+//            reference maximum, P^T (fp16) to the exchange buffer;
+//            value wave w: widens and stores its share of the next tile (four of
+//            the nine 16-byte chunks per row), then issues the loads of the tile
+//            after it;
+//   phase 2  O^T += V^T . P^T: score wave w for features 128w..128w+31 (8
+//            MFMAs, with its share of the staging (five chunks per row) woven
+//            between them), value wave w for features 128w+32..128w+127 (24
+//            MFMAs).
+// The registers of one SIMD hold O^T for 128 features of all heads (256 per
+// lane), 20 k-steps of Q^T for 32 heads (80) and one tile in flight (36): one
+// wave alone could not hold more, two waves can split it so that each stays
+// within 256.  With eight waves the LDS also serves about twice the bytes per
+// clock that four waves draw from it.
+// Q^T k-steps from kQReg2 on live in LDS as the register image of the score
+// waves: the B-operand fragment of score wave w for tail k-step j is 64 lanes x
+// 16 B, lane l at 16 l (so every fragment read is one contiguous, conflict-free
+// 1 KB).
+constexpr int kQReg2 = 18, kQTail2 = kDk / 16 - kQReg2;
+constexpr int kQTail2Bytes = 4 * kQTail2 * 1024;          // 73,728 B
+__device__ __forceinline__ uint32_t qtail2_off(int w, int j, int lane) { return ((w * kQTail2 + j) * 64 + lane) * 16; }
+
+// Staging of a bf16 tile: work-group threads (tid & 255) own token (tid & 255) >> 3
+// of the 32 and 16-byte chunks c8 + 8k of its row, c8 = tid & 7; this part holds
+// chunks K0 <= k < K1.
+template <int K0, int K1>
+struct StageBf16 {
+  static constexpr int kN = K1 - K0;
+  u32x4 r[kN];
+  const uint8_t* src;
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int lt = threadIdx.x & 255, tok = lt >> 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    src = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + tok) * kRowBytesBf16 + 16 * (lt & 7);
+  }
+  template <int I>
+  __device__ __forceinline__ void load() { r[I] = ld16_stream(src + 128 * (K0 + I)); }
+  __device__ __forceinline__ void load_all() {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) r[i] = ld16_stream(src + 128 * (K0 + i));
+  }
+  template <int I>
+  __device__ __forceinline__ void store(char* buf) {
+    const int lt = threadIdx.x & 255;
+    *reinterpret_cast<u32x4*>(buf + swz<kSwz128>(lt >> 3, lt & 7) + 128 * (K0 + I)) = bf16x8_to_f16x8(r[I]);
+  }
+  __device__ __forceinline__ void store_all(char* buf) {
+    const int lt = threadIdx.x & 255;
+    char* dst = buf + swz<kSwz128>(lt >> 3, lt & 7);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) *reinterpret_cast<u32x4*>(dst + 128 * (K0 + i)) = bf16x8_to_f16x8(r[i]);
+  }
+};
+constexpr int kStageSplit = 6;              // score waves stage chunks 0..5, value waves 6..8
+using StageA = StageBf16<0, kStageSplit>;
+using StageB = StageBf16<kStageSplit, 9>;
+
+// Score chain of one tile for a score wave, as fenced steps (see H128Scores).
+template <int kPf>
+struct ScoresV2 {
+  const char* buf;
+  const char* qtail;
+  const H128Lane& L;
+  const half8 (&q)[kQReg2];
+  floatx16 sacc;
+  half8 kb[kPf], qb[kPf];
+  static constexpr int kSteps = kDk / 16;
+
+  __device__ __forceinline__ half8 kread(int ks) const {
+    return *reinterpret_cast<const half8*>(buf + L.qk_off[ks & 3] + 128 * (ks >> 2));
+  }
+  template <int KS>
+  __device__ __forceinline__ void step() {
+    if constexpr (KS < kQReg2) sacc = mfma32x32x16(kb[KS % kPf], q[KS], sacc);
+    else sacc = mfma32x32x16(kb[KS % kPf], qb[KS % kPf], sacc);
+    constexpr int kn = KS + kPf;
+    if constexpr (kn < kSteps) {
+      kb[KS % kPf] = kread(kn);
+      if constexpr (kn >= kQReg2) qb[KS % kPf] = *reinterpret_cast<const half8*>(qtail + 1024 * (kn - kQReg2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KS + 1 < kSteps) step<KS + 1>();
+  }
+  __device__ __forceinline__ floatx16 run() {
+    __builtin_amdgcn_sched_barrier(0);
+    sacc = floatx16{};
+#pragma unroll
+    for (int d = 0; d < kPf; ++d) kb[d] = kread(d);
+    static_assert(kQReg2 >= kPf, "the first Q^T fragments come from VGPRs");
+    __builtin_amdgcn_sched_barrier(0);
+    step<0>();
+    return sacc;
+  }
+};
+
+// Scores and softmax of one tile for a score wave (modes as h128_scores).
+template <int kMode>
+__device__ __forceinline__ void v2_scores(const char* buf, const char* qtail, const H128Lane& L,
+                                          const half8 (&q)[kQReg2], float& m_ref, float& l_sum,
+                                          bool& overflow, int t0, int t_end, bool page_ok, float scale_log2,
+                                          half8 (&p)[2]) {
+  floatx16 sacc = ScoresV2<3>{buf, qtail, L, q}.run();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sacc[r] *= scale_log2;
+  if (!page_ok || t0 + kTile128 > t_end) {          // partial tile: mask the missing rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = t0 + 8 * (r >> 2) + 4 * L.g + (r & 3);
+      if (!page_ok || tt >= t_end) sacc[r] = -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+  mx = wave_max_xor(mx, 32);               // lanes l and l^32 hold the same head
+  if (kMode == 1) {
+    m_ref = fmaxf(m_ref, mx);
+    return;
+  }
+  if (kMode == 0) {
+    if (m_ref == -INFINITY) m_ref = mx;    // first non-empty tile: nothing accumulated yet
+    overflow |= mx > m_ref + kTauFixed;
+  }
+  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
+    psum += e;
+    p[r >> 3][r & 7] = (_Float16)e;
+  }
+  l_sum += psum;
+}
+
+// Value product of one tile for kNF feature blocks F0.. of SIMD slot w (block
+// 4w + f covers features 128w + 32f .. +31) and all 128 heads: MFMA
+// I = 4 kNF j + kNF hg + f over token half j and head group hg.  V^T fragments
+// of one token half are held at a time (refilled right after their last use),
+// P^T fragments two at a time.  With kStage, the score wave's share of the
+// next tile is stored (and its registers reloaded from the tile after it)
+// between the MFMAs, one chunk per step.
+template <int kNF, int F0, bool kStage>
+struct ValuesV2 {
+  const char* buf;
+  const char* pbuf;
+  const H128Lane& L;
+  int w;
+  floatx16 (&o)[4 * kNF];
+  StageA* st;
+  char* nxt;
+  half8 vb[kNF];
+  half8 pt[2];
+  static constexpr int kMfma = 8 * kNF;
+
+  __device__ __forceinline__ half8 vread(int j, int f) const {
+    const int blk = 4 * w + F0 + f;
+    const uint32_t off = 16 * j * kRowLds + 128 * (blk >> 1);
+    const half4 lo = lds_read_tr(buf, L.pv_off[blk & 1] + off);
+    const half4 hi = lds_read_tr(buf, L.pv_off[2 + (blk & 1)] + off);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ half8 pread(int j, int hg) const {
+    return *reinterpret_cast<const half8*>(pbuf + hg * 32 * kPRow + L.p_off(j));
+  }
+  template <int I>
+  __device__ __forceinline__ void step() {
+    constexpr int j = I / (4 * kNF), hg = (I / kNF) % 4, f = I % kNF;
+    o[4 * f + hg] = mfma32x32x16(vb[f], pt[hg & 1], o[4 * f + hg]);
+    if constexpr (j == 0 && hg == 3) vb[f] = vread(1, f);          // last use of this token half's V^T
+    if constexpr (f == kNF - 1 && I + 1 + kNF < kMfma) {           // P^T two head groups on, same slot
+      constexpr int n2 = I + 1 + kNF, j2 = n2 / (4 * kNF), hg2 = (n2 / kNF) % 4;
+      pt[hg2 & 1] = pread(j2, hg2);
+    }
+    if constexpr (kStage && I < StageA::kN) {
+      st->template store<I>(nxt);
+      __builtin_amdgcn_sched_barrier(0);     // the reload may not overtake the store of the same registers
+      st->template load<I>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (I + 1 < kMfma) step<I + 1>();
+  }
+  __device__ __forceinline__ void run() {
+    static_assert(!kStage || StageA::kN <= kMfma, "staging must fit in the value product");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) vb[f] = vread(0, f);
+    pt[0] = pread(0, 0);
+    pt[1] = pread(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    step<0>();
+  }
+};
+
+// Both kinds of wave walk the same segments and tiles and pass the same
+// barriers: per segment two (table refill), per tile two (X1: tile s complete,
+// the other buffer and the P buffer free; X2: P of all heads written).
+struct SegV2 {
+  int seg0, seg1, n_tiles;
+};
+__device__ __forceinline__ SegV2 v2_segment(const DecodeArgs& a, const ItemRange& it, int seg0, int32_t* ptab) {
+  SegV2 sg;
+  sg.seg0 = seg0;
+  sg.seg1 = seg0 + min(it.t_end - seg0, kSegPages * kBlock);
+  __syncthreads();                         // earlier users of the buffers and the table are done
+  fill_ptab(a, it.b, sg.seg0, sg.seg1, ptab);
+  __syncthreads();
+  sg.n_tiles = (sg.seg1 - sg.seg0 + kTile128 - 1) / kTile128;
+  return sg;
+}
+__device__ __forceinline__ int64_t v2_page(const SegV2& sg, const int32_t* ptab, int t) {
+  const int pg = ptab[(min(t, sg.n_tiles - 1) * kTile128) / kBlock];   // read clamped, then select
+  return t < sg.n_tiles ? pg : -1;
+}
+
+// Score waves: scores, softmax and P in phase 1; feature block 4w of the value
+// product with their share of the staging in phase 2.
+template <int kMode>
+__device__ __forceinline__ void v2_score_pass(const DecodeArgs& a, const ItemRange& it, char* lds0, char* lds1,
+                                              char* pbuf, const char* qtail, int32_t* ptab, const H128Lane& L,
+                                              int w, const half8 (&q)[kQReg2], floatx16 (&oa)[4], float& m_ref,
+                                              float& l_sum, bool& overflow) {
+  const char* qimg = qtail + qtail2_off(w, 0, 32 * L.g + L.hl);
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
+    const SegV2 sg = v2_segment(a, it, seg0, ptab);
+    StageA sa;
+    sa.begin(a, v2_page(sg, ptab, 0), sg.seg0, sg.seg1);
+    sa.load_all();
+    sa.store_all(lds0);
+    sa.begin(a, v2_page(sg, ptab, 1), sg.seg0 + kTile128, sg.seg1);
+    sa.load_all();
+    auto tile = [&](int s, const char* cur, char* nxt) {
+      __syncthreads();                     // X1
+      int pg0 = __builtin_amdgcn_readfirstlane((int)v2_page(sg, ptab, s));
+      int pg2 = __builtin_amdgcn_readfirstlane((int)v2_page(sg, ptab, s + 2));
+      asm volatile("" : "+s"(pg0), "+s"(pg2));
+      half8 p[2];
+      v2_scores<kMode>(cur, qimg, L, q, m_ref, l_sum, overflow, sg.seg0 + s * kTile128, sg.seg1, pg0 >= 0,
+                       a.scale_log2, p);
+      if (kMode != 1) {
+        char* pw = pbuf + w * 32 * kPRow;
+        *reinterpret_cast<half8*>(pw + L.p_off(0)) = p[0];
+        *reinterpret_cast<half8*>(pw + L.p_off(1)) = p[1];
+      }
+      __syncthreads();                     // X2
+      sa.begin(a, pg2, sg.seg0 + (s + 2) * kTile128, sg.seg1);   // the reloads read the tile after next
+      if (kMode != 1) {
+        ValuesV2<1, 0, true>{cur, pbuf, L, w, oa, &sa, nxt}.run();
+      } else {
+        sa.store_all(nxt);
+        sa.load_all();
+      }
+    };
+    for (int s = 0; s < sg.n_tiles; s += 2) {
+      tile(s, lds0, lds1);
+      if (s + 1 < sg.n_tiles) tile(s + 1, lds1, lds0);
+    }
+  }
+}
+
+// Value waves: their share of the staging in phase 1; feature blocks 4w + 1..3
+// of the value product in phase 2.
+template <int kMode>
+__device__ __forceinline__ void v2_value_pass(const DecodeArgs& a, const ItemRange& it, char* lds0, char* lds1,
+                                              const char* pbuf, int32_t* ptab, const H128Lane& L, int w,
+                                              floatx16 (&ob)[12]) {
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
+    const SegV2 sg = v2_segment(a, it, seg0, ptab);
+    StageB sb;
+    sb.begin(a, v2_page(sg, ptab, 0), sg.seg0, sg.seg1);
+    sb.load_all();
+    sb.store_all(lds0);
+    sb.begin(a, v2_page(sg, ptab, 1), sg.seg0 + kTile128, sg.seg1);
+    sb.load_all();
+    auto tile = [&](int s, const char* cur, char* nxt) {
+      __syncthreads();                     // X1
+      int pg2 = __builtin_amdgcn_readfirstlane((int)v2_page(sg, ptab, s + 2));
+      asm volatile("" : "+s"(pg2));
+      sb.store_all(nxt);
+      sb.begin(a, pg2, sg.seg0 + (s + 2) * kTile128, sg.seg1);
+      sb.load_all();
+      __syncthreads();                     // X2
+      if (kMode != 1) ValuesV2<3, 1, false>{cur, pbuf, L, w, ob, nullptr, nullptr}.run();
+    };
+    for (int s = 0; s < sg.n_tiles; s += 2) {
+      tile(s, lds0, lds1);
+      if (s + 1 < sg.n_tiles) tile(s + 1, lds1, lds0);
+    }
+  }
+}
+
+// O^T accumulators (feature block base fb0 + f, head group hg) normalised by
+// 1 / l of each head and stored as fp16 rows of o_part, straight from the
+// accumulator layout (lane: head 32 hg + hl, features 8 (r / 4) + 4 g + r % 4).
+template <int kN>
+__device__ __forceinline__ void v2_store(const DecodeArgs& a, const ItemRange& it, const floatx16 (&o)[kN],
+                                         int feat0, const float (&inv)[4], int hl, int g) {
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int f = i / 4, hg = i % 4;
+    uint16_t* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + feat0 + 32 * f + 4 * g;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const floatx4 x = floatx4{o[i][4 * rr], o[i][4 * rr + 1], o[i][4 * rr + 2], o[i][4 * rr + 3]} * inv[hg];
+      *reinterpret_cast<half4*>(op + 8 * rr) = __builtin_convertvector(x, half4);   // round to nearest even
+    }
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds0[kBuf128];
+  __shared__ __attribute__((aligned(16))) char lds1[kBuf128];
+  __shared__ __attribute__((aligned(16))) char pbuf[kPBuf];
+  __shared__ __attribute__((aligned(16))) char qtail[kQTail2Bytes];
+  __shared__ int32_t ptab[kSegPages];
+  ItemRange it = item_range(a);
+  if (!it.ok) return;
+  if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scorer = wave < 4;                    // uniform per wave
+  const int w = wave & 3;
+  const int lane = threadIdx.x & 63, hl = lane & 31, g = lane >> 5;
+  const H128Lane L = h128_lane();
+
+  // Q^T k-steps from kQReg2 on, all heads, to LDS: thread -> head tid / 4 and the
+  // 16-byte chunks c = tid % 4 + 4 i of its row's tail (chunk c is k-step
+  // kQReg2 + c / 2, lane group c % 2).
+  {
+    const int hr = threadIdx.x >> 2;
+    const uint16_t* qr = a.q_abs + ((int64_t)it.b * 128 + hr) * kDk + 16 * kQReg2;
+#pragma unroll
+    for (int i = 0; i < 2 * kQTail2 / 4; ++i) {
+      const int c = (threadIdx.x & 3) + 4 * i;
+      *reinterpret_cast<u32x4*>(qtail + qtail2_off(hr >> 5, c >> 1, (hr & 31) + 32 * (c & 1))) = ld16(qr + 8 * c);
+    }
+  }
+  float m_ref = -INFINITY, l_sum = 0.f;
+  bool overflow = false;
+  float* red = reinterpret_cast<float*>(pbuf);
+  if (scorer) {
+    // Q^T as the B operand: lane holds q_abs[b][32w + hl][16 ks + 8 g .. +7] for the first kQReg2 k-steps.
+    half8 q[kQReg2];
+    const uint16_t* qp = a.q_abs + ((int64_t)it.b * 128 + 32 * w + hl) * kDk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kQReg2; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 16 * ks));
+    wait_vm<0>();                          // the Q loads retire before the tile loop's loads are issued
+    floatx16 oa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oa[i] = floatx16{};
+    v2_score_pass<0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, w, q, oa, m_ref, l_sum, overflow);
+    if (__syncthreads_or(overflow)) {
+      // Rare: some head's scores grew by more than 2^15 after its first tile.
+      m_ref = -INFINITY;
+      v2_score_pass<1>(a, it, lds0, lds1, pbuf, qtail, ptab, L, w, q, oa, m_ref, l_sum, overflow);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oa[i] = floatx16{};
+      l_sum = 0.f;
+      v2_score_pass<2>(a, it, lds0, lds1, pbuf, qtail, ptab, L, w, q, oa, m_ref, l_sum, overflow);
+    }
+    const float l_tot = l_sum + __shfl_xor(l_sum, 32, 64);
+    __syncthreads();                       // every wave is done with the P buffer
+    if (g == 0) red[32 * w + hl] = l_tot;
+    __syncthreads();
+    float inv[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const float l = red[32 * hg + hl];
+      inv[hg] = l > 0.f ? 1.f / l : 0.f;
+    }
+    v2_store(a, it, oa, 128 * w, inv, hl, g);
+    if (g == 0)
+      a.lse_part[(int64_t)it.out_row * 128 + 32 * w + hl] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    wait_vm<0>();
+    floatx16 ob[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) ob[i] = floatx16{};
+    v2_value_pass<0>(a, it, lds0, lds1, pbuf, ptab, L, w, ob);
+    if (__syncthreads_or(false)) {
+      v2_value_pass<1>(a, it, lds0, lds1, pbuf, ptab, L, w, ob);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) ob[i] = floatx16{};
+      v2_value_pass<2>(a, it, lds0, lds1, pbuf, ptab, L, w, ob);
+    }
+    __syncthreads();
+    __syncthreads();
+    float inv[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const float l = red[32 * hg + hl];
+      inv[hg] = l > 0.f ? 1.f / l : 0.f;
+    }
+    v2_store(a, it, ob, 128 * w + 32, inv, hl, g);
+  }
+}
+
 // ---------------------------------------------------------------------------
 using H16Bf16 = LoaderBf16Wide<kSwz16, 256>;   // the staging waves are threads 256..511
 using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
@@ -1507,7 +1911,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid(a.n_items), block(256);
   if (num_heads == 128) {
-    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h128<0>, grid, block, 0, stream, a);
+    if (cache_dtype == 0) hipLaunchKernelGGL(decode_h128v2, grid, dim3(512), 0, stream, a);
     else if (cache_dtype == 1) hipLaunchKernelGGL(decode_h128<1>, grid, block, 0, stream, a);
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h128<2>, grid, block, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h128<3>, grid, block, 0, stream, a);
