@@ -264,7 +264,7 @@ def clock_probe_ghz(torch, dev):
     against the constant 100 MHz counter (mla_bench_clock_probe)."""
     import ctypes as C
     out = torch.zeros(3, dtype=torch.int64, device=dev)
-    err = _bench_lib().mla_bench_clock_probe(200000, C.c_void_p(out.data_ptr()),
+    err = _bench_lib().mla_bench_clock_probe(40000, C.c_void_p(out.data_ptr()),
                                              C.c_void_p(torch.cuda.current_stream().cuda_stream))
     if err:
         raise RuntimeError("mla_bench_clock_probe: hipError %d" % err)
