@@ -30,6 +30,16 @@ by itself, so append can be done token by token) are:
   INT4 symmetric with an INT4 RoPE key (a variant the report does not
   measure): the latent as INT4 symmetric; the RoPE key by the same rule in
   groups of 8 (scale = max|x| / 7, nibble q + 8, same byte order).
+  INT8 per channel over 32-token blocks (the report's "per-channel INT8 (32
+  blocks)", which §4.1 keeps as its production setting): the 32 consecutive
+  tokens of a block (positions 32j .. 32j + 31 of a sequence) share, for each
+  latent channel c, one scale over the block:
+      amax_c = max_t |x[t][c]|, scale_c = amax_c / 127 (float32),
+      code = clamp(rint(x / scale_c), -127, 127); amax_c == 0 -> scale 0, codes 0
+  (the INT8 reading applied down a channel instead of along a token).  A block
+  is quantised when its 32nd token is appended; until then its tokens' latent
+  rows are kept in bf16 (the "open" block, at most one per sequence).  The
+  RoPE key is INT8 per token in 8-element groups, as for the other INT8 formats.
   FP8 per token (e4m3; a cache format the pages name but do not specify):
       amax = max |x| over the token's 512 latent channels (8 for each RoPE-key
       group), scale = amax / 448 (float32; 448 is the largest e4m3 value)
@@ -55,6 +65,13 @@ Page layouts (64 tokens a page, bytes):
   fp8t : as int8t with e4m3 codes                                     39,168
   int4k4: [64][256] latent nibbles | [64][32] RoPE-key nibbles
          | [64][16] f32 scales | [64][8] f32 RoPE-key scales           24,576
+  int8c: [64][512] int8 latent codes | [64][64] int8 RoPE-key codes
+         | [2][512] f32 channel scales of blocks 0 and 1
+         | [64][8] f32 RoPE-key scales | [32][512 B] overflow          59,392
+         An open block b keeps its bf16 latent rows in place of its codes:
+         channels 0..255 of row r in code row 32 b + r (512 B), channels
+         256..511 in overflow row r.  Bytes the decode reads per closed token:
+         512 + 64 + 64 (block scales, 2,048 B per 32 tokens) + 32 = 672.
 
 Parity pins (tests/test_oracle_quant.py): the absmax element maps to +-127; an
 INT4 group's min maps to 0 and its max to 15; the reconstruction error of every
@@ -77,7 +94,8 @@ D_R = 64
 G_C = 32      # latent channels per group
 G_R = 8       # RoPE-key channels per group
 
-CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4 = range(7)
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4, CACHE_INT8_CHAN = range(8)
+T_BLK = 32    # tokens per channel-scale block of the int8c format
 _F448 = np.float32(448.0)
 _F127 = np.float32(127.0)
 _F15 = np.float32(15.0)
@@ -217,17 +235,44 @@ def token_bytes(dtype: int) -> int:
             CACHE_INT4_SYM: D_C // 2 + D_R + (D_C // G_C) * 4 + (D_R // G_R) * 4,
             CACHE_INT8_TOK: 576 + 4 + (D_R // G_R) * 4,
             CACHE_FP8_TOK: 576 + 4 + (D_R // G_R) * 4,
-            CACHE_INT4_SYM_K4: D_C // 2 + D_R // 2 + (D_C // G_C) * 4 + (D_R // G_R) * 4}[dtype]
+            CACHE_INT4_SYM_K4: D_C // 2 + D_R // 2 + (D_C // G_C) * 4 + (D_R // G_R) * 4,
+            CACHE_INT8_CHAN: D_C + D_R + D_C * 4 // T_BLK + (D_R // G_R) * 4}[dtype]
 
 
 def page_bytes(dtype: int) -> int:
+    if dtype == CACHE_INT8_CHAN:
+        return BLOCK * (D_C + D_R + (D_R // G_R) * 4) + 2 * D_C * 4 + T_BLK * D_C
     return BLOCK * token_bytes(dtype)
+
+
+def quant_int8_channel_block(x_bits: np.ndarray):
+    """One closed block: x_bits [32, C] bf16 bits -> codes int8 [32, C] and one
+    float32 scale per channel [C], by the INT8 rule applied down each channel."""
+    assert x_bits.shape[0] == T_BLK
+    q, s = quant_int8_sym(np.ascontiguousarray(x_bits.T), T_BLK)
+    return np.ascontiguousarray(q.T), s[:, 0]
+
+
+def _encode_int8_chan(c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
+    """Rows 0..n-1 of a sequence from a block boundary on: full 32-row blocks are
+    closed (codes + channel scales), a trailing partial block stays open (bf16)."""
+    n = c_bits.shape[0]
+    n_closed = (n // T_BLK) * T_BLK
+    codes = np.zeros((n, D_C), np.int8)
+    scales = np.zeros((n_closed // T_BLK, D_C), np.float32)
+    for j in range(n_closed // T_BLK):
+        codes[j * T_BLK:(j + 1) * T_BLK], scales[j] = quant_int8_channel_block(c_bits[j * T_BLK:(j + 1) * T_BLK])
+    rc, rs = quant_int8_sym(r_bits, G_R)
+    return {"codes": codes, "blk_scale": scales, "r_codes": rc, "r_scale": rs,
+            "open": np.asarray(c_bits[n_closed:], np.uint16).copy(), "n_closed": n_closed}
 
 
 def encode_tokens(dtype: int, c_bits: np.ndarray, r_bits: np.ndarray) -> dict:
     """Quantise (or copy) n token rows into their per-field arrays."""
     if dtype == CACHE_BF16:
         return {"rows": np.concatenate([c_bits, r_bits], axis=-1).astype(np.uint16)}
+    if dtype == CACHE_INT8_CHAN:
+        return _encode_int8_chan(c_bits, r_bits)
     if dtype == CACHE_INT4_SYM_K4:
         q, s = quant_int4_sym(c_bits, G_C)
         rq, rs = quant_int4_sym(r_bits, G_R)
@@ -261,6 +306,22 @@ def pack_page(dtype: int, fields: dict) -> np.ndarray:
 
     if dtype == CACHE_BF16:
         put(0, fields["rows"], 1152)
+    elif dtype == CACHE_INT8_CHAN:
+        nc = fields["n_closed"]
+        off = put(0, fields["codes"][:nc], 512)
+        op = fields["open"]
+        if len(op):                                    # open block b = nc // 32 of this page
+            row0 = nc
+            halves = np.ascontiguousarray(op[:, :D_C // 2]).view(np.uint8).reshape(-1)
+            out[row0 * 512: row0 * 512 + halves.size] = halves
+            tail = np.ascontiguousarray(op[:, D_C // 2:]).view(np.uint8).reshape(-1)
+            base = BLOCK * (D_C + D_R + (D_R // G_R) * 4) + 2 * D_C * 4
+            out[base: base + tail.size] = tail
+        off = put(off, fields["r_codes"], 64)
+        sc = np.ascontiguousarray(fields["blk_scale"]).view(np.uint8).reshape(-1)
+        out[off: off + sc.size] = sc
+        off += 2 * D_C * 4
+        put(off, fields["r_scale"], 32)
     elif dtype in (CACHE_INT8, CACHE_INT8_TOK, CACHE_FP8_TOK):
         off = put(0, fields["codes"], 576)
         off = put(off, fields["c_scale"], 64 if dtype == CACHE_INT8 else 4)
@@ -291,6 +352,14 @@ def unpack_page(dtype: int, page: np.ndarray) -> dict:
     if dtype == CACHE_BF16:
         rows, _ = get(0, 1152, np.uint16, 576)
         return {"rows": rows}
+    if dtype == CACHE_INT8_CHAN:
+        codes, off = get(0, 512, np.int8, 512)
+        rc, off = get(off, 64, np.int8, 64)
+        sc = page[off: off + 2 * D_C * 4].copy().view(np.float32).reshape(2, D_C)
+        off += 2 * D_C * 4
+        rs, off = get(off, 32, np.float32, 8)
+        ov = page[off: off + T_BLK * D_C].copy().view(np.uint16).reshape(T_BLK, D_C // 2)
+        return {"codes": codes, "r_codes": rc, "blk_scale": sc, "r_scale": rs, "overflow": ov}
     if dtype in (CACHE_INT8, CACHE_INT8_TOK, CACHE_FP8_TOK):
         codes, off = get(0, 576, np.uint8 if dtype == CACHE_FP8_TOK else np.int8, 576)
         cs, off = get(off, 64, np.float32, 16) if dtype == CACHE_INT8 else get(off, 4, np.float32, 1)
@@ -317,6 +386,14 @@ def dequant_fields(dtype: int, f: dict):
     if dtype == CACHE_BF16:
         rows = _bf16_to_f32(f["rows"])
         return rows[..., :D_C], rows[..., D_C:]
+    if dtype == CACHE_INT8_CHAN:
+        nc = f["n_closed"]
+        c = np.zeros((nc + len(f["open"]), D_C), np.float32)
+        for j in range(nc // T_BLK):
+            c[j * T_BLK:(j + 1) * T_BLK] = (f["codes"][j * T_BLK:(j + 1) * T_BLK].astype(np.float32)
+                                            * f["blk_scale"][j][None, :]).astype(np.float32)
+        c[nc:] = _bf16_to_f32(f["open"])
+        return c, dequant_int8(f["r_codes"], f["r_scale"], G_R)
     if dtype == CACHE_FP8_TOK:
         return dequant_fp8(f["codes"][..., :D_C], f["c_scale"], D_C), dequant_fp8(f["codes"][..., D_C:], f["r_scale"], G_R)
     if dtype in (CACHE_INT8, CACHE_INT8_TOK):
@@ -344,6 +421,21 @@ def pack_pool(dtype: int, num_pages: int, seqs) -> np.ndarray:
             f = encode_tokens(dtype, c_bits[p0:p0 + n], r_bits[p0:p0 + n])
             pool[int(bt_row[p0 // BLOCK])] = pack_page(dtype, f)
     return pool
+
+
+def page_fields_int8_chan(page: np.ndarray, n: int) -> dict:
+    """The fields an int8c page holds for its first n tokens (the layout read back
+    the way encode_tokens returns it: closed codes and scales, open rows)."""
+    u = unpack_page(CACHE_INT8_CHAN, page)
+    nc = (n // T_BLK) * T_BLK
+    codes = np.zeros((n, D_C), np.int8)
+    codes[:nc] = u["codes"][:nc]
+    op = np.zeros((n - nc, D_C), np.uint16)
+    if n > nc:
+        op[:, :D_C // 2] = u["codes"][nc:n].view(np.uint16)
+        op[:, D_C // 2:] = u["overflow"][: n - nc]
+    return {"codes": codes, "blk_scale": u["blk_scale"][: nc // T_BLK].copy(), "r_codes": u["r_codes"][:n].copy(),
+            "r_scale": u["r_scale"][:n].copy(), "open": op, "n_closed": nc}
 
 
 def dequant_pool_seq(dtype: int, pool: np.ndarray, bt_row: np.ndarray, L: int):

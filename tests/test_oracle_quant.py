@@ -304,3 +304,77 @@ def test_int4_sym_rope_key_groups_of_8():
     _, rr = quant.dequant_fields(quant.CACHE_INT4_SYM_K4, f)
     err = np.abs(rr.reshape(40, 8, 8) - x)
     assert np.all(err <= s[..., None] / 2 * (1 + 1e-6) + 1e-12)
+
+
+# ------------------------------------------------------------------ per-channel INT8 over 32-token blocks
+# ([Report] §3.2, the "per-channel INT8 (32 blocks)" row; §4.1 keeps it as the production setting)
+def test_int8_chan_each_channels_extreme_hits_127_and_error_within_half_step():
+    rng = np.random.default_rng(11)
+    xb = _draw(rng, (32, 512))
+    codes, scales = quant.quant_int8_channel_block(xb)
+    x = bf16_bits_to_f32(xb)
+    assert codes.shape == (32, 512) and scales.shape == (512,)
+    am = np.argmax(np.abs(x), axis=0)                     # the extreme token of every channel
+    ext = codes[am, np.arange(512)].astype(np.int32)
+    assert np.array_equal(np.abs(ext), np.full(512, 127))
+    assert np.array_equal(np.sign(ext), np.sign(x[am, np.arange(512)]).astype(np.int32))
+    xh = (codes.astype(np.float32) * scales[None, :]).astype(np.float64)
+    err = np.abs(xh - x)
+    # half a step, plus the float32 roundings of the scale and of code * scale
+    bound = scales[None, :].astype(np.float64) * 0.5 * (1 + 2 ** -20) + 2 * np.spacing(np.abs(x))
+    assert np.all(err <= bound)
+
+
+def test_int8_chan_scales_run_down_channels_not_along_tokens():
+    """x[t][c] = 2^(c mod 16) u_t with u_0 = 1 and |u_t| < 1 after: every
+    channel's extreme is token 0, so every code of token 0 is 127 and channel
+    c's scale is 2^(c mod 16) / 127.  A reading along tokens (one scale per 32
+    channels of a token) would give token 0 the code 127 only where c mod 16 = 15."""
+    u = np.concatenate([[1.0], np.round(np.linspace(0.9, -0.9, 31) * 8) / 8]).astype(np.float32)
+    s = (2.0 ** (np.arange(512) % 16)).astype(np.float32)
+    x = (s[None, :] * u[:, None]).astype(np.float32)
+    xb = _bf16(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x)            # exact in bf16
+    codes, scales = quant.quant_int8_channel_block(xb)
+    assert np.all(codes[0] == 127)
+    assert np.allclose(scales, s / 127.0, rtol=1e-6)
+
+
+def test_int8_chan_zero_channel_and_split_of_closed_and_open_rows():
+    rng = np.random.default_rng(12)
+    for L in (1, 31, 32, 33, 64, 95, 130):
+        c = _draw(rng, (L, 512))
+        c[:, 7] = 0                                       # an all-zero channel
+        r = _draw(rng, (L, 64))
+        f = quant.encode_tokens(quant.CACHE_INT8_CHAN, c, r)
+        nc = (L // 32) * 32
+        assert f["n_closed"] == nc and f["blk_scale"].shape == (nc // 32, 512) and f["open"].shape == (L - nc, 512)
+        assert np.all(f["blk_scale"][:, 7] == 0) and np.all(f["codes"][:, 7] == 0)
+        cd, rd = quant.dequant_fields(quant.CACHE_INT8_CHAN, f)
+        assert np.array_equal(cd[nc:], bf16_bits_to_f32(c[nc:]))        # open rows exact
+        assert np.all(cd[:nc, 7] == 0)
+        # the RoPE key: INT8 per token in 8-groups, as the other INT8 formats
+        rc, rs = quant.quant_int8_sym(r, 8)
+        assert np.array_equal(f["r_codes"], rc) and np.array_equal(f["r_scale"], rs)
+
+
+def test_int8_chan_page_layout_and_roundtrip():
+    """Block 1 open with 5 rows: channels 0..255 of open row r sit in code row
+    32 + r, channels 256..511 in overflow row r; block 0's scales at offset
+    36,864, block 1's slot empty; the page reads back to the same fields."""
+    rng = np.random.default_rng(13)
+    c = _draw(rng, (37, 512))
+    r = _draw(rng, (37, 64))
+    f = quant.encode_tokens(quant.CACHE_INT8_CHAN, c, r)
+    pg = quant.pack_page(quant.CACHE_INT8_CHAN, f)
+    assert pg.size == quant.page_bytes(quant.CACHE_INT8_CHAN) == 59392
+    assert quant.token_bytes(quant.CACHE_INT8_CHAN) == 672
+    for rr in range(5):
+        lo = pg[(32 + rr) * 512:(33 + rr) * 512].view(np.uint16)
+        hi = pg[43008 + rr * 512:43008 + (rr + 1) * 512].view(np.uint16)
+        assert np.array_equal(lo, c[32 + rr, :256]) and np.array_equal(hi, c[32 + rr, 256:])
+    assert np.array_equal(pg[36864:36864 + 2048].view(np.float32), f["blk_scale"][0])
+    assert not pg[36864 + 2048:36864 + 4096].any()
+    g = quant.page_fields_int8_chan(pg, 37)
+    for k in ("codes", "blk_scale", "r_codes", "r_scale", "open"):
+        assert np.array_equal(g[k], f[k]), k
