@@ -51,7 +51,7 @@ PREFILL_WORKLOADS = {
     "v2lite_prompt_layer": ("v2lite_layer", "one V2-Lite layer over a 4096-token prompt: front (projections, "
                                             "RMSNorm, RoPE), causal unabsorbed attention, W_O + residual"),
 }
-DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3, "int8t": 4, "fp8t": 5, "int4k4": 6}
+DTYPES = {"bf16": 0, "int8": 1, "int4": 2, "int4s": 3, "int8t": 4, "fp8t": 5, "int4k4": 6, "int8c": 7}
 
 
 def log(msg):
@@ -524,7 +524,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f16", 1: "i8/f16", 2: "i4/f16", 3: "i4s/f16", 4: "i8t/f16", 5: "e4m3t/f16", 6: "i4s+k4/f16"}[cache_dtype],
+        "dtype": {0: "f16", 1: "i8/f16", 2: "i4/f16", 3: "i4s/f16", 4: "i8t/f16", 5: "e4m3t/f16", 6: "i4s+k4/f16",
+                  7: "i8c/f16"}[cache_dtype],
         "data": "synthetic (seeded; shapes and distributions of the workload, no checkpoint)",
         "config": {"workload": args.workload, "description": desc, "batch": case.B, "heads": case.H,
                    "cached_tokens": case.total_tokens, "cache_dtype": args.cache_dtype,

@@ -65,7 +65,9 @@ typedef enum {
   MLA_CACHE_INT4_SYM = 3, /* c_kv symmetric INT4, fp32 scale per 32; k_pe INT8            */
   MLA_CACHE_INT8_TOK = 4, /* c_kv INT8, one fp32 scale per token; k_pe INT8 per 8         */
   MLA_CACHE_FP8_TOK = 5,  /* c_kv e4m3 FP8, one fp32 scale per token; k_pe e4m3 per 8     */
-  MLA_CACHE_INT4_SYM_K4 = 6 /* c_kv symmetric INT4 per 32; k_pe symmetric INT4 per 8       */
+  MLA_CACHE_INT4_SYM_K4 = 6, /* c_kv symmetric INT4 per 32; k_pe symmetric INT4 per 8      */
+  MLA_CACHE_INT8_CHAN = 7   /* c_kv INT8, one fp32 scale per channel per 32-token block;
+                               k_pe INT8 per 8 ([Report] §3.2 "per-channel INT8 (32 blocks)") */
 } mla_cache_dtype;
 
 /* Shape of one MLA layer.  Supported: num_heads in {16, 128}, qk_nope_dim = 128,
@@ -116,6 +118,13 @@ typedef struct {
  *   FP8_TOK: as INT8_TOK with e4m3 codes                              (39,168 B)
  *   INT4_SYM_K4: [64][256] latent nibbles | [64][32] RoPE-key nibbles
  *         | [64][16] f32 scales | [64][8] f32 RoPE-key scales         (24,576 B)
+ *   INT8_CHAN: [64][512] int8 latent codes | [64][64] int8 RoPE-key codes
+ *         | [2][512] f32 channel scales (blocks 0, 1: tokens 0..31, 32..63)
+ *         | [64][8] f32 RoPE-key scales | [32][512 B] overflow        (59,392 B)
+ *         A block that has not yet received its 32nd token is "open": its
+ *         latent rows are bf16, channels 0..255 of row r in code row
+ *         32 b + r, channels 256..511 in overflow row r.  Bytes per token
+ *         (672) count what the decode reads for a closed token.
  * A pool of N pages is N * mla_cache_page_bytes() contiguous bytes.          */
 mla_status mla_config_check(const mla_config* cfg);
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
@@ -147,6 +156,14 @@ size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items);
  *   q = clamp(rint(x/scale), -7, 7), stored as q + 8; max|x| = 0 gives scale 0
  *   and q = 0.  The RoPE key of INT4 and INT4_SYM is INT8 as above.
  * INT4_SYM_K4: INT4_SYM, and the RoPE key by the same rule in 8-channel groups.
+ * INT8_CHAN: positions 32j..32j+31 of a sequence form a block; when the
+ *   block's last position is appended, each latent channel c of the block gets
+ *   scale = max_t |x[t][c]| / 127 and the INT8 codes above; earlier positions
+ *   are stored as bf16 until then.  The RoPE key is INT8 per token as above.
+ *   A call may hold several positions of a block only at consecutive indices
+ *   in increasing slot order (as a prompt chunk or decode steps append them);
+ *   a block whose rows were not all appended gets unspecified codes.  Two
+ *   kernels run in order (block closing, then per-token work).
  * Codes and scales are bit-exact with that definition.
  * n_tokens == 0 is a no-op; n_tokens < 0 is MLA_ERR_VALUE.                  */
 mla_status mla_cache_append(const mla_config* cfg, void* pool, int64_t num_pages,

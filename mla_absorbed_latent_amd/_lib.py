@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libm
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_VALUE, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, \
     MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = range(8)
-CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4 = range(7)
+CACHE_BF16, CACHE_INT8, CACHE_INT4, CACHE_INT4_SYM, CACHE_INT8_TOK, CACHE_FP8_TOK, CACHE_INT4_SYM_K4, \
+    CACHE_INT8_CHAN = range(8)
 
 
 class MlaConfig(C.Structure):

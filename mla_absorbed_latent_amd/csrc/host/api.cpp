@@ -60,7 +60,7 @@ mla_status mla_config_check(const mla_config* cfg) {
   if (cfg->qk_nope_dim != 128 || cfg->kv_lora_rank != 512 || cfg->rope_dim != 64 || cfg->v_head_dim != 128 ||
       cfg->block_size != 64)
     return MLA_ERR_SHAPE;
-  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_INT4_SYM_K4) return MLA_ERR_VALUE;
+  if (cfg->cache_dtype < MLA_CACHE_BF16 || cfg->cache_dtype > MLA_CACHE_INT8_CHAN) return MLA_ERR_VALUE;
   if (!(cfg->softmax_scale > 0.f) || !std::isfinite(cfg->softmax_scale)) return MLA_ERR_VALUE;
   return MLA_OK;
 }
@@ -73,11 +73,17 @@ size_t mla_cache_bytes_per_token(const mla_config* cfg) {
     case MLA_CACHE_INT4: return 256 + 64 + 16 * 4 + 16 * 4 + 8 * 4;   // nibbles + key codes + scales + zeros + key scales
     case MLA_CACHE_INT4_SYM: return 256 + 64 + 16 * 4 + 8 * 4;          // nibbles + key codes + scales + key scales
     case MLA_CACHE_INT4_SYM_K4: return 256 + 32 + 16 * 4 + 8 * 4;       // nibbles + key nibbles + scales + key scales
+    case MLA_CACHE_INT8_CHAN: return 512 + 64 + 512 * 4 / 32 + 8 * 4;   // codes + key codes + block scales / 32 + key scales
     default: return 576 + 4 + 8 * 4;                           // codes + the token's latent scale + key scales
   }
 }
 
-size_t mla_cache_page_bytes(const mla_config* cfg) { return 64 * mla_cache_bytes_per_token(cfg); }
+size_t mla_cache_page_bytes(const mla_config* cfg) {
+  if (mla_config_check(cfg) != MLA_OK) return 0;
+  // the per-channel block format also holds the open block's bf16 rows (overflow [32][512 B])
+  if (cfg->cache_dtype == MLA_CACHE_INT8_CHAN) return 64 * (512 + 64 + 8 * 4) + 2 * 512 * 4 + 32 * 512;
+  return 64 * mla_cache_bytes_per_token(cfg);
+}
 
 size_t mla_decode_workspace_bytes(const mla_config* cfg, int32_t n_items) {
   if (mla_config_check(cfg) != MLA_OK || n_items < 0) return 0;

@@ -16,6 +16,8 @@
 //         group of all 512 latent channels; RoPE key as INT8.
 //   INT4 symmetric (a variant the report does not measure): scale = amax / 7,
 //         q = clamp(rint(x / scale), -7, 7), stored as the nibble q + 8; amax 0 -> 8.
+//   INT8 per channel over 32-token blocks: see append_int8c_close below (a block
+//         is quantised when its 32nd token arrives).
 //
 // One thread per 16-byte chunk (bf16) or per quantisation group; slots outside
 // [0, num_pages * 64) are skipped.
@@ -342,6 +344,109 @@ __global__ __launch_bounds__(256) void append_fp8t(uint8_t* pool, int64_t num_pa
   }
 }
 
+// ---------------------------------------------------------------------------
+// INT8 per channel over 32-token blocks (the report's "per-channel INT8 (32
+// blocks)"): the 32 positions 32j..32j+31 of a sequence share, per latent
+// channel, scale = max_t |x| / 127; a block is quantised when its 32nd token is
+// appended, and until then its rows are kept in bf16.  Page (59,392 B):
+//   [64][512] int8 latent codes | [64][64] int8 RoPE-key codes
+//   | [2][512] f32 channel scales of blocks 0, 1 | [64][8] f32 RoPE-key scales
+//   | [32][512 B] overflow
+// An open block b keeps latent channels 0..255 of its row r (bf16, 512 B) in
+// code row 32 b + r and channels 256..511 in overflow row r.
+// Within one call, the tokens of a block that the call holds must sit at
+// consecutive indices in increasing slot order (as a prompt or a decode step
+// appends them); a row found neither there nor in the block's open storage
+// gives that block unspecified codes, never a fault.
+constexpr int kPageInt8c = 59392;
+constexpr int kI8cKeyCodes = 64 * 512, kI8cScales = kI8cKeyCodes + 64 * 64, kI8cKeyScales = kI8cScales + 2 * 512 * 4,
+              kI8cOverflow = kI8cKeyScales + 64 * 8 * 4;
+constexpr int kTBlk = 32;
+
+// bf16 row pieces of a block's row rr: from the call's input when the call holds
+// that position at index j, else from the block's open storage.
+__device__ __forceinline__ u32x4 i8c_row_piece(const uint16_t* c_kv, const int64_t* slots, int n, int64_t i_close,
+                                               int64_t slot_close, int rr, const uint8_t* page, int blk, int lane) {
+  const int64_t j = i_close - (kTBlk - 1) + rr;
+  const bool in_call = j >= 0 && j < n && slots[j] == slot_close - (kTBlk - 1) + rr;
+  if (in_call) return ld16(c_kv + j * kDc + 8 * lane);
+  const uint8_t* src = lane < 32 ? page + (kTBlk * blk + rr) * 512 + 16 * lane : page + kI8cOverflow + rr * 512 + 16 * (lane - 32);
+  return ld16(src);
+}
+
+// Launch 1: one wave per input token; the wave of a token that closes its block
+// (position 31 within it) quantises the block, lane l owning latent channels
+// 8 l .. 8 l + 7: the maximum down each channel over the 32 rows, then each
+// row's codes (a row's codes overwrite its open storage only after the whole
+// wave has read that row).
+__global__ __launch_bounds__(256) void append_int8c_close(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                          const int64_t* slots, int n) {
+  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // uniform per wave
+  const int lane = threadIdx.x & 63;
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages) || slot % kTBlk != kTBlk - 1) return;
+  uint8_t* page = pool + (slot / kBlock) * (int64_t)kPageInt8c;
+  const int blk = (int)((slot % kBlock) / kTBlk);
+  float amax[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) amax[c] = 0.f;
+  for (int rr = 0; rr < kTBlk; ++rr) {
+    const u32x4 v = i8c_row_piece(c_kv, slots, n, tok, slot, rr, page, blk, lane);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      amax[2 * d] = fmaxf(amax[2 * d], fabsf(__uint_as_float(v[d] << 16)));
+      amax[2 * d + 1] = fmaxf(amax[2 * d + 1], fabsf(__uint_as_float(v[d] & 0xffff0000u)));
+    }
+  }
+  float scale[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) scale[c] = __fdiv_rn(amax[c], 127.0f);
+  for (int rr = 0; rr < kTBlk; ++rr) {
+    const u32x4 v = i8c_row_piece(c_kv, slots, n, tok, slot, rr, page, blk, lane);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float x = __uint_as_float(c & 1 ? (v[c >> 1] & 0xffff0000u) : (v[c >> 1] << 16));
+      float q = 0.f;
+      if (scale[c] != 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(x, scale[c])), -127.f), 127.f);
+      packed[c >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (c & 3));
+    }
+    *reinterpret_cast<u32x2*>(page + (kTBlk * blk + rr) * 512 + 8 * lane) = u32x2{packed[0], packed[1]};
+  }
+  float* sc = reinterpret_cast<float*>(page + kI8cScales) + blk * kDc + 8 * lane;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sc[c] = scale[c];
+}
+
+// Launch 2 (after launch 1 on the stream): one wave per input token; lanes 0-7
+// quantise the RoPE key's 8-groups; the whole wave writes the latent row to its
+// block's open storage unless this call also closes the block.
+__global__ __launch_bounds__(256) void append_int8c_tok(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
+                                                        const uint16_t* k_pe, const int64_t* slots, int n) {
+  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // uniform per wave
+  const int lane = threadIdx.x & 63;
+  if (tok >= n) return;
+  const int64_t slot = slots[tok];
+  if (!slot_ok(slot, num_pages)) return;
+  uint8_t* page = pool + (slot / kBlock) * (int64_t)kPageInt8c;
+  const int off = (int)(slot % kBlock), blk = off / kTBlk, rr = off % kTBlk;
+  if (lane < 8) {
+    int8_t rc[8];
+    const float s = quant_sym8<8>(k_pe + tok * kDr + lane * 8, rc);
+    int8_t* rdst = reinterpret_cast<int8_t*>(page + kI8cKeyCodes + off * 64 + lane * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rdst[i] = rc[i];
+    reinterpret_cast<float*>(page + kI8cKeyScales)[off * 8 + lane] = s;
+  }
+  const int64_t jc = tok + (kTBlk - 1 - rr);                 // where this call would hold the block's last row
+  const bool closes_here = jc < n && slots[jc] == slot + (kTBlk - 1 - rr);
+  if (closes_here) return;
+  const u32x4 v = ld16(c_kv + tok * kDc + 8 * lane);
+  uint8_t* dst = lane < 32 ? page + (kTBlk * blk + rr) * 512 + 16 * lane : page + kI8cOverflow + rr * 512 + 16 * (lane - 32);
+  st16(dst, v);
+}
+
 }  // namespace
 
 hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const uint16_t* c_kv,
@@ -352,6 +457,11 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
     const int64_t work = (int64_t)n * 72;
     hipLaunchKernelGGL(append_bf16, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
                        c_kv, k_pe, slots, n);
+  } else if (cache_dtype == 7) {
+    const int64_t work = (int64_t)n * 64;                  // one wave a token
+    const dim3 grid((unsigned)((work + 255) / 256));
+    hipLaunchKernelGGL(append_int8c_close, grid, dim3(256), 0, stream, p, num_pages, c_kv, slots, n);
+    hipLaunchKernelGGL(append_int8c_tok, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
   } else if (cache_dtype == 4 || cache_dtype == 5) {
     const int64_t work = (int64_t)n * 64;                  // one wave a token
     hipLaunchKernelGGL(cache_dtype == 4 ? append_int8t : append_fp8t, dim3((unsigned)((work + 255) / 256)),

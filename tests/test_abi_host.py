@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_sizes(lib):
-    for dt, tok, page in ((0, 1152, 73728), (1, 672, 43008), (2, 480, 30720), (3, 416, 26624), (4, 612, 39168), (5, 612, 39168), (6, 384, 24576)):
+    for dt, tok, page in ((0, 1152, 73728), (1, 672, 43008), (2, 480, 30720), (3, 416, 26624), (4, 612, 39168), (5, 612, 39168), (6, 384, 24576), (7, 672, 59392)):
         cfg = api.config(128, dt)
         assert api.cache_bytes_per_token(cfg) == tok
         assert api.cache_page_bytes(cfg) == page
@@ -57,7 +57,7 @@ def test_config_check(lib):
     assert lib.mla_config_check(C.byref(ok)) == L.MLA_OK
     assert lib.mla_config_check(None) == L.MLA_ERR_NULL
     for field, val, st in (("num_heads", 64, L.MLA_ERR_SHAPE), ("kv_lora_rank", 256, L.MLA_ERR_SHAPE),
-                           ("block_size", 16, L.MLA_ERR_SHAPE), ("cache_dtype", 7, L.MLA_ERR_VALUE),
+                           ("block_size", 16, L.MLA_ERR_SHAPE), ("cache_dtype", 8, L.MLA_ERR_VALUE),
                            ("softmax_scale", 0.0, L.MLA_ERR_VALUE), ("softmax_scale", float("inf"), L.MLA_ERR_VALUE)):
         c = api.config(16)
         setattr(c, field, val)
