@@ -211,7 +211,10 @@ mla_status mla_plan_splits(const mla_config* cfg, const int32_t* seq_lens_host, 
  *   lse_j = m + ln sum_t exp(s_t - m)             (natural log)
  * over the item's tokens t (a range of the sequence's first seq_lens[b] tokens).
  * An empty item gives lse_j = -inf and o_j = 0.  Quantised caches are
- * dequantised in registers (code * scale; q * scale + zero).
+ * dequantised in registers (code * scale; q * scale + zero).  INT8_CHAN: the
+ * closed blocks of the first floor(seq_lens[b] / 32) * 32 positions are read
+ * as codes times their channel scales, the open block's rows as bf16; a
+ * position that was never appended reads whatever the pool holds.
  *   q_abs        device [batch][H][576] fp16 (from mla_absorb_q)
  *   pool         device, num_pages pages in the config's format
  *   block_table  device [batch][max_pages_per_seq] int32 physical page ids;

@@ -346,6 +346,200 @@ struct LoaderInt8Reg {
   }
 };
 
+// INT8 per channel over 32-token blocks: page [64][512] latent codes | [64][64]
+// key codes | [2][512] f32 channel scales (one row per block) | [64][8] f32 key
+// scales | [32][256] bf16 overflow.  A block is closed once its 32nd token is
+// written (codes and channel scales); the one open block of a sequence keeps its
+// rows in bf16, channels 0..255 in the row's own code row and 256..511 in
+// overflow row (row % 32).  The RoPE key is INT8 per 8-group in every row.
+constexpr int kPageInt8c = 59392;
+constexpr int kI8cKeyCodes = 64 * 512, kI8cScales = kI8cKeyCodes + 64 * 64, kI8cKeyScales = kI8cScales + 2 * 512 * 4,
+              kI8cOverflow = kI8cKeyScales + 64 * 8 * 4;
+static_assert(kI8cOverflow + 32 * 512 == kPageInt8c, "page layout");
+
+// Byte offset of 16-byte LDS chunk q (0..71) of tile row `row`.
+template <int kSwz>
+__device__ __forceinline__ uint32_t swz_chunk(int row, int q) { return swz<kSwz>(row, q & 7) + 128 * (q >> 3); }
+
+// Closed blocks, 32-token tiles (a tile is one block: tiles start at multiples
+// of 32 and a closed range ends at one).  Threads are laid out down the
+// channels, so that each needs 8 of the block's channel scales: thread t owns
+// the 8-channel chunk q = t % 64 of tile rows 8 (t / 64) + m, m = 0..7; and the
+// 8 key codes of group t % 8 of row t / 8.  A whole tile is in range or not.
+template <int kSwz>
+struct LoaderInt8cReg {
+  static constexpr int kScorePrefetch = 3;
+  u32x2 c[8];                 // codes of chunk q, rows 8 w + m
+  floatx4 sv[2];              // f32 scales of channels 8 q .. 8 q + 7
+  uint32_t h2[4];             // the same as fp16 pairs, formed at the first store step
+  u32x2 kc;                   // key codes of group t % 8 of row t / 8
+  float ks;
+  const uint8_t* pg;          // the tile's page (uniform: the whole tile is in range or not)
+  uint32_t row0;              // first tile row within the page (0 or 32)
+
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    pg = page_base(a, page, page >= 0 && t0 < t_end, kPageInt8c);
+    row0 = (uint32_t)(t0 % kBlock);
+  }
+  __device__ __forceinline__ void load_codes(int m) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t off = (row0 + 8 * (t >> 6)) * 512 + 8 * (t & 63);
+    c[m] = *reinterpret_cast<const u32x2*>(pg + off + 512 * m);
+  }
+  __device__ __forceinline__ void load_scales() {
+    const uint32_t off = kI8cScales + (row0 >> 5) * 2048 + 32 * (threadIdx.x & 63);
+    sv[0] = *reinterpret_cast<const floatx4*>(pg + off);
+    sv[1] = *reinterpret_cast<const floatx4*>(pg + off + 16);
+  }
+  __device__ __forceinline__ void load_key() {
+    const uint32_t row = row0 + (threadIdx.x >> 3), g8 = threadIdx.x & 7;
+    kc = *reinterpret_cast<const u32x2*>(pg + (kI8cKeyCodes + row * 64 + 8 * g8));
+    ks = *reinterpret_cast<const float*>(pg + (kI8cKeyScales + row * 32 + 4 * g8));
+  }
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    begin(a, page, t0, t_end);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) load_codes(m);
+    load_scales();
+    load_key();
+    return page >= 0;
+  }
+  __device__ __forceinline__ void make_h2() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      h2[j] = __builtin_bit_cast(uint32_t, half2v{(_Float16)sv[j >> 1][2 * (j & 1)], (_Float16)sv[j >> 1][2 * (j & 1) + 1]});
+  }
+  // Four codes (channels 4 d .. 4 d + 3 of the chunk) -> two fp16 pairs.
+  __device__ __forceinline__ u32x2 deq4(uint32_t w, int d) const {
+    const uint32_t u = w ^ 0x80808080u;
+    const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t lo = 0x64006400u | (u & 0xffu) | ((u & 0xff00u) << 8);
+    const uint32_t hi = 0x64006400u | ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u);
+    return u32x2{__builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, lo) + bias) * __builtin_bit_cast(half2v, h2[2 * d])),
+                 __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, hi) + bias) * __builtin_bit_cast(half2v, h2[2 * d + 1]))};
+  }
+  __device__ __forceinline__ void store_key(char* lds_buf) const {
+    const _Float16 k = (_Float16)ks;
+    const u32x2 lo = int8x4_to_f16(kc[0], half2v{k, k}), hi = int8x4_to_f16(kc[1], half2v{k, k});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(threadIdx.x >> 3, 64 + (threadIdx.x & 7))) =
+        u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  // Stepwise commit (steps 2 m, 2 m + 1: row m's chunk; 16, 17: the key) and
+  // reload, as for the other formats.  The scales are turned into fp16 pairs at
+  // step 0 and reloaded at step 1.
+  static constexpr int kStoreSteps = 18;
+  u32x2 part;
+  template <int I>
+  __device__ __forceinline__ void store_step(char* lds_buf) {
+    constexpr int m = I / 2;
+    if constexpr (m < 8) {
+      if constexpr (I == 0) make_h2();
+      if constexpr (I % 2 == 0) {
+        part = deq4(c[m][0], 0);
+      } else {
+        const u32x2 hi = deq4(c[m][1], 1);
+        *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(8 * (threadIdx.x >> 6) + m, threadIdx.x & 63)) =
+            u32x4{part[0], part[1], hi[0], hi[1]};
+      }
+    } else if constexpr (I % 2 == 1) {
+      store_key(lds_buf);
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void load_step() {
+    if constexpr (I % 2 == 1) {
+      constexpr int m = I / 2;
+      if constexpr (m < 8) load_codes(m);
+      else load_key();
+      if constexpr (I == 1) load_scales();
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    make_h2();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const u32x2 lo = deq4(c[m][0], 0), hi = deq4(c[m][1], 1);
+      *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(8 * (threadIdx.x >> 6) + m, threadIdx.x & 63)) =
+          u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    store_key(lds_buf);
+  }
+};
+
+// The open block, 32-token tiles: rows in bf16 as in LoaderBf16Reg (thread t:
+// row t / 8, latent chunks t % 8 + 8 k), chunks 0..31 from the code row and
+// 32..63 from the overflow row; the key as in LoaderInt8cReg.  Rows past t_end
+// read the zero page.
+template <int kSwz>
+struct LoaderInt8cOpenReg {
+  static constexpr int kScorePrefetch = 3;
+  u32x4 r[8];
+  u32x2 kc;
+  float ks;
+  const uint8_t* pg;
+  int row;
+
+  __device__ __forceinline__ void begin(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = threadIdx.x >> 3;
+    pg = page_base(a, page, page >= 0 && t0 + tok < t_end, kPageInt8c);
+    row = t0 % kBlock + tok;
+  }
+  template <int K>
+  __device__ __forceinline__ void load_chunk() {
+    const int q = (threadIdx.x & 7) + 8 * K;
+    if constexpr (K < 4) r[K] = ld16_stream(pg + row * 512 + 16 * q);
+    else r[K] = ld16_stream(pg + kI8cOverflow + (row % 32) * 512 + 16 * (q - 32));
+  }
+  __device__ __forceinline__ void load_key() {
+    const int g8 = threadIdx.x & 7;
+    kc = *reinterpret_cast<const u32x2*>(pg + kI8cKeyCodes + row * 64 + 8 * g8);
+    ks = reinterpret_cast<const float*>(pg + kI8cKeyScales)[row * 8 + g8];
+  }
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    begin(a, page, t0, t_end);
+    load_chunk<0>();
+    load_chunk<1>();
+    load_chunk<2>();
+    load_chunk<3>();
+    load_chunk<4>();
+    load_chunk<5>();
+    load_chunk<6>();
+    load_chunk<7>();
+    load_key();
+    return page >= 0;
+  }
+  __device__ __forceinline__ void store_key(char* lds_buf) const {
+    const _Float16 k = (_Float16)ks;
+    const u32x2 lo = int8x4_to_f16(kc[0], half2v{k, k}), hi = int8x4_to_f16(kc[1], half2v{k, k});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(threadIdx.x >> 3, 64 + (threadIdx.x & 7))) =
+        u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  static constexpr int kStoreSteps = 18;
+  template <int I>
+  __device__ __forceinline__ void store_step(char* lds_buf) {
+    constexpr int k = I / 2;
+    if constexpr (I % 2 == 1) {
+      if constexpr (k < 8)
+        *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * k) = bf16x8_to_f16x8(r[k]);
+      else
+        store_key(lds_buf);
+    }
+  }
+  template <int I>
+  __device__ __forceinline__ void load_step() {
+    if constexpr (I % 2 == 1) {
+      if constexpr (I / 2 < 8) load_chunk<I / 2>();
+      else load_key();
+    }
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(threadIdx.x >> 3, threadIdx.x & 7) + 128 * k) = bf16x8_to_f16x8(r[k]);
+    store_key(lds_buf);
+  }
+};
+
 // INT4 page: [64][256] latent nibbles | [64][64] int8 key codes | [64][16] f32 scales
 //            | [64][16] f32 zeros | [64][8] f32 key scales.
 // Symmetric INT4 (kSym) drops the zeros: a nibble holds q + 8 and decodes to
@@ -604,6 +798,7 @@ __device__ __forceinline__ floatx4 quad_transpose(floatx4 a, int r) {
 // (eight threads per token, two 32-token passes), with tied assembly loads.
 template <int kSwz, int kTid0>
 struct LoaderBf16Wide {
+  __device__ __forceinline__ void set_lo(int) {}   // rows below a bound are masked by the scores instead
   static constexpr int kLoads = 18;      // load instructions per tile
   u32x4 r[18] = {};
 
@@ -653,6 +848,7 @@ struct LoaderBf16Wide {
 // kTok1): the same page with e4m3 codes.
 template <int kSwz, int kTid0, bool kTok1 = false, bool kFp8 = false>
 struct LoaderInt8Wide {
+  __device__ __forceinline__ void set_lo(int) {}   // rows below a bound are masked by the scores instead
   static constexpr int kPage = kBlock * (kTok1 ? 612 : 672);
   static constexpr int kLoads = 11;      // load instructions per tile
   static constexpr int kKeyScales = 64 * 576 + (kTok1 ? 64 * 4 : 64 * 64);   // byte offset of the key scales
@@ -738,6 +934,7 @@ struct LoaderInt8Wide {
 // per thread in one 8-byte load.
 template <int kSwz, int kTid0, bool kSym = false, bool kKey4 = false>
 struct LoaderInt4Wide {
+  __device__ __forceinline__ void set_lo(int) {}   // rows below a bound are masked by the scores instead
   static constexpr int kLoads = kSym ? 7 : 8;   // load instructions per tile
   static constexpr int kPage = kBlock * (kKey4 ? 384 : (kSym ? 416 : 480));
   static constexpr int kKeyScales = kSym ? 64 * 64 : 2 * 64 * 64;   // byte offset of the key scales after the scales
@@ -810,6 +1007,147 @@ struct LoaderInt4Wide {
       *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4) + 128 * 8) = u32x4{a0[0], a0[1], a1[0], a1[1]};
       *reinterpret_cast<u32x4*>(lds_buf + swz<kSwz>(tok, 2 * c4 + 1) + 128 * 8) = u32x4{b0[0], b0[1], b1[0], b1[1]};
     }
+  }
+};
+
+// INT8 per channel over 32-token blocks, closed blocks (page: [64][512] latent
+// codes | [64][64] key codes | [2][512] f32 channel scales | [64][8] f32 key
+// scales | overflow).  Threads are laid out down the channels so that each one
+// needs only 16 of the block's channel scales: thread t owns the 16-channel
+// piece p = t % 32 (LDS chunks 2p, 2p + 1) of the 8 tokens 8 (t / 32) + m of
+// one block (tile rows 0..31 are block 0, 32..63 block 1), and the key piece
+// t % 4 (16 key codes, groups 2 (t % 4) and 2 (t % 4) + 1) of token t / 4.
+template <int kSwz, int kTid0>
+struct LoaderInt8cWide {
+  static constexpr int kLoads = 14;      // load instructions per tile
+  u32x4 c[8] = {};
+  floatx4 sv[4] = {};
+  u32x4 kc = {};
+  floatx2 ks = {};
+  __device__ __forceinline__ void set_lo(int) {}
+
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int lt = ltid<kTid0>(), p = lt & 31, tg = lt >> 5;
+    const int tok0 = 8 * tg;
+#define MLA_I8C_ROW(m)                                                                                     \
+    asm_ld16_nt<0>(c[m], page_base(a, page, page >= 0 && t0 + tok0 + (m) < t_end, kPageInt8c) +              \
+                             (tok0 + (m)) * 512 + 16 * p)
+    MLA_I8C_ROW(0);
+    MLA_I8C_ROW(1);
+    MLA_I8C_ROW(2);
+    MLA_I8C_ROW(3);
+    MLA_I8C_ROW(4);
+    MLA_I8C_ROW(5);
+    MLA_I8C_ROW(6);
+    MLA_I8C_ROW(7);
+#undef MLA_I8C_ROW
+    // a block past t_end may hold no scales yet: read the zero page's (the codes are zero too)
+    const uint8_t* sc = page_base(a, page, page >= 0 && t0 + 32 * (tg >> 2) < t_end, kPageInt8c) + kI8cScales +
+                        (tg >> 2) * 2048 + 64 * p;
+    asm_ld16<0>(sv[0], sc);
+    asm_ld16<16>(sv[1], sc);
+    asm_ld16<32>(sv[2], sc);
+    asm_ld16<48>(sv[3], sc);
+    const int ktok = lt >> 2, kq = lt & 3;
+    const uint8_t* kp = page_base(a, page, page >= 0 && t0 + ktok < t_end, kPageInt8c);
+    asm_ld16_nt<0>(kc, kp + kI8cKeyCodes + ktok * 64 + 16 * kq);
+    asm_ld8<0>(ks, kp + kI8cKeyScales + ktok * 32 + 8 * kq);
+    return page >= 0;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) settle(c[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) settle(sv[i]);
+    settle(kc);
+    settle(ks);
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    const int lt = ltid<kTid0>(), p = lt & 31, tok0 = 8 * (lt >> 5);
+    // fp16 scale pairs of channels (2j, 2j + 1) of the piece
+    half2v s2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s2[j] = half2v{(_Float16)sv[j >> 1][2 * (j & 1)], (_Float16)sv[j >> 1][2 * (j & 1) + 1]};
+    const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint32_t h[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t u = c[m][d] ^ 0x80808080u;
+        const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);   // codes 4d, 4d + 1
+        const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);   // codes 4d + 2, 4d + 3
+        h[2 * d] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, lo) + bias) * s2[2 * d]);
+        h[2 * d + 1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, hi) + bias) * s2[2 * d + 1]);
+      }
+      *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok0 + m, 2 * p)) = u32x4{h[0], h[1], h[2], h[3]};
+      *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok0 + m, 2 * p + 1)) = u32x4{h[4], h[5], h[6], h[7]};
+    }
+    const int ktok = lt >> 2, kq = lt & 3;
+    const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
+    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+  }
+};
+
+// The open block of the per-channel INT8 format: latent rows in bf16, channels
+// 0..255 in the row's own code row and 256..511 in overflow row (row % 32); the
+// RoPE key INT8 as for closed rows.  Thread t takes token t / 4: latent
+// channels 128 (t % 4) .. +127 (16 chunks of 8) and key piece t % 4.  Rows
+// below t_lo (closed rows of the same page) and past t_end read the zero page.
+template <int kSwz, int kTid0>
+struct LoaderInt8cOpenWide {
+  static constexpr int kLoads = 18;      // load instructions per tile
+  u32x4 v[16] = {};
+  u32x4 kc = {};
+  floatx2 ks = {};
+  int t_lo = 0;
+  __device__ __forceinline__ void set_lo(int lo) { t_lo = lo; }
+
+  __device__ __forceinline__ bool issue(const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int lt = ltid<kTid0>(), tok = lt >> 2, c4 = lt & 3;
+    const bool ok = page >= 0 && t0 + tok < t_end && t0 + tok >= t_lo;
+    const uint8_t* pg = page_base(a, page, ok, kPageInt8c);
+    // c4 = 0, 1: channels < 256 in the token's code row; c4 = 2, 3: its overflow row
+    const uint8_t* src = pg + (c4 < 2 ? tok * 512 + 256 * c4 : kI8cOverflow + (tok % 32) * 512 + 256 * (c4 - 2));
+    asm_ld16_nt<0>(v[0], src);
+    asm_ld16_nt<16>(v[1], src);
+    asm_ld16_nt<32>(v[2], src);
+    asm_ld16_nt<48>(v[3], src);
+    asm_ld16_nt<64>(v[4], src);
+    asm_ld16_nt<80>(v[5], src);
+    asm_ld16_nt<96>(v[6], src);
+    asm_ld16_nt<112>(v[7], src);
+    asm_ld16_nt<128>(v[8], src);
+    asm_ld16_nt<144>(v[9], src);
+    asm_ld16_nt<160>(v[10], src);
+    asm_ld16_nt<176>(v[11], src);
+    asm_ld16_nt<192>(v[12], src);
+    asm_ld16_nt<208>(v[13], src);
+    asm_ld16_nt<224>(v[14], src);
+    asm_ld16_nt<240>(v[15], src);
+    asm_ld16_nt<0>(kc, pg + kI8cKeyCodes + tok * 64 + 16 * c4);
+    asm_ld8<0>(ks, pg + kI8cKeyScales + tok * 32 + 8 * c4);
+    return page >= 0;
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) settle(v[i]);
+    settle(kc);
+    settle(ks);
+  }
+  __device__ __forceinline__ void commit(char* lds_buf) {
+    const int lt = ltid<kTid0>(), tok = lt >> 2, c4 = lt & 3;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 16 * c4 + i)) = bf16x8_to_f16x8(v[i]);
+    const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
+    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4 + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
   }
 };
 
@@ -1020,6 +1358,25 @@ struct H128Values {
   }
 };
 
+// The per-channel INT8 format splits a work item in two passes that share the
+// softmax state: tokens of closed blocks [t_begin, closed_end), then the tile
+// holding the open block, from open_begin (a multiple of the tile size kTile),
+// tokens below open_lo masked (they were in the first pass).  closed_end is a
+// multiple of 32 (or the item's end), so every 32 tokens of the first pass are
+// all in range or all out.
+struct Int8cSplit {
+  int closed_end, open_begin, open_lo;
+};
+template <int kTile>
+__device__ __forceinline__ Int8cSplit int8c_split(const DecodeArgs& a, const ItemRange& it) {
+  const int ce = (a.seq_lens[it.b] / 32) * 32;   // end of the closed blocks
+  Int8cSplit sp;
+  sp.closed_end = min(it.t_end, max(it.t_begin, ce));
+  sp.open_lo = max(it.t_begin, ce);
+  sp.open_begin = sp.open_lo < it.t_end ? max(it.t_begin, ce & ~(kTile - 1)) : it.t_end;
+  return sp;
+}
+
 // All store steps of a loader at once (when there is no value product to hide them in).
 template <int I = 0, class Loader>
 __device__ __forceinline__ void store_all(Loader& ld, char* buf) {
@@ -1064,16 +1421,19 @@ __device__ __forceinline__ void h128_step(const DecodeArgs& a, int s, int seg0, 
   }
 }
 
+// Tokens [t_begin, t_end) of sequence b.  t_begin is a multiple of the page
+// size, or the range fits one tile (the page table is sampled per 64 tokens
+// from t_begin).
 template <class Loader, int kMode>
-__device__ __forceinline__ void h128_pass(const DecodeArgs& a, const ItemRange& it, char* lds0, char* lds1,
+__device__ __forceinline__ void h128_pass(const DecodeArgs& a, int b, int t_begin, int t_end, char* lds0, char* lds1,
                                           char* pbuf, const char* qtail, int32_t* ptab,
                                           const H128Lane& L,
                                           int wave, const half8 (&q)[kQReg], floatx16 (&o)[16], float& m_ref,
                                           float& l_sum, bool& overflow) {
-  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
-    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+  for (int seg0 = t_begin; seg0 < t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(t_end, seg0 + kSegPages * kBlock);
     __syncthreads();                       // earlier users of the buffers and the table are done
-    fill_ptab(a, it.b, seg0, seg1, ptab);
+    fill_ptab(a, b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile128 - 1) / kTile128;
     auto page_at = [&](int t) -> int64_t {       // -1 past the segment; branch free (read clamped, then select)
@@ -1091,6 +1451,30 @@ __device__ __forceinline__ void h128_pass(const DecodeArgs& a, const ItemRange& 
         h128_step<Loader, kMode>(a, s + 1, seg0, seg1, lds1, lds0, pbuf, qtail, L, wave, q, o, m_ref,
                                  l_sum, overflow, ld, page_at);
     }
+  }
+}
+
+// One pass of the item in mode kMode: the format's loader over the whole range,
+// or for the per-channel INT8 format its closed blocks and then its open block.
+template <int kCache, int kMode>
+__device__ __forceinline__ void h128_passes(const DecodeArgs& a, const ItemRange& it, char* lds0, char* lds1,
+                                            char* pbuf, const char* qtail, int32_t* ptab, const H128Lane& L,
+                                            int wave, const half8 (&q)[kQReg], floatx16 (&o)[16], float& m_ref,
+                                            float& l_sum, bool& overflow) {
+  if constexpr (kCache == 7) {
+    const Int8cSplit sp = int8c_split<kTile128>(a, it);
+    h128_pass<LoaderInt8cReg<kSwz128>, kMode>(a, it.b, it.t_begin, sp.closed_end, lds0, lds1, pbuf, qtail, ptab, L,
+                                              wave, q, o, m_ref, l_sum, overflow);
+    h128_pass<LoaderInt8cOpenReg<kSwz128>, kMode>(a, it.b, sp.open_begin, it.t_end, lds0, lds1, pbuf, qtail, ptab,
+                                                  L, wave, q, o, m_ref, l_sum, overflow);
+  } else {
+    using Loader = typename std::conditional<
+        kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
+        typename std::conditional<kCache == 1 || kCache == 4 || kCache == 5,
+                                  LoaderInt8Reg<kTile128, kSwz128, 0, kCache >= 4, kCache == 5>,
+                                  LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3 || kCache == 6, kCache == 6>>::type>::type;
+    h128_pass<Loader, kMode>(a, it.b, it.t_begin, it.t_end, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref,
+                             l_sum, overflow);
   }
 }
 
@@ -1132,23 +1516,15 @@ __global__ __launch_bounds__(256, 1) void decode_h128(DecodeArgs a) {
   float m_ref = -INFINITY, l_sum = 0.f;
   bool overflow = false;
 
-  using Loader = typename std::conditional<
-      kCache == 0, LoaderBf16Reg<kTile128, kSwz128>,
-      typename std::conditional<kCache == 1 || kCache == 4 || kCache == 5,
-                                LoaderInt8Reg<kTile128, kSwz128, 0, kCache >= 4, kCache == 5>,
-                                LoaderInt4Reg<kTile128, kSwz128, 0, kCache == 3 || kCache == 6, kCache == 6>>::type>::type;
-  h128_pass<Loader, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
-                         overflow);
+  h128_passes<kCache, 0>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum, overflow);
   if (__syncthreads_or(overflow)) {
     // Rare: some head's scores grew by more than 2^15 after its first tile.
     m_ref = -INFINITY;
-    h128_pass<Loader, 1>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
-                         overflow);
+    h128_passes<kCache, 1>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum, overflow);
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = floatx16{};
     l_sum = 0.f;
-    h128_pass<Loader, 2>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum,
-                         overflow);
+    h128_passes<kCache, 2>(a, it, lds0, lds1, pbuf, qtail, ptab, L, wave, q, o, m_ref, l_sum, overflow);
   }
 
   // ---- per-head sums from the owning waves, then normalise and write ----
@@ -1270,11 +1646,12 @@ constexpr int kQ16Reg = 10, kQ16Lds = kDk / 32 - kQ16Reg;
 // waves.  Stage (s + 1) % 2 holds tile s + 1 (written at step s, then reloaded
 // with tile s + 3); the other holds tile s + 2.
 template <class Loader>
-__device__ __forceinline__ void h16_stage(const DecodeArgs& a, const ItemRange& it, char* lds, int32_t* ptab) {
-  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
-    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+__device__ __forceinline__ void h16_stage(const DecodeArgs& a, int b, int t_begin, int t_end, int t_lo, char* lds,
+                                          int32_t* ptab) {
+  for (int seg0 = t_begin; seg0 < t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(t_end, seg0 + kSegPages * kBlock);
     __syncthreads();                       // earlier users of the buffers and the table are done
-    fill_ptab(a, it.b, seg0, seg1, ptab);
+    fill_ptab(a, b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
     // Every step commits and issues unconditionally (tiles past the end load
@@ -1282,6 +1659,8 @@ __device__ __forceinline__ void h16_stage(const DecodeArgs& a, const ItemRange& 
     // tied assembly loads, so the waits are explicit: a commit waits until only
     // the other loader's tile is in flight.
     Loader ld0, ld1;
+    ld0.set_lo(t_lo);
+    ld1.set_lo(t_lo);
     ld0.issue(a, ptab[0], seg0, seg1);
     wait_vm<0>();
     ld0.settle_all();
@@ -1308,8 +1687,10 @@ __device__ __forceinline__ void h16_stage(const DecodeArgs& a, const ItemRange& 
   }
 }
 
-template <class Loader>
+// OpenLoader (not void): the two-pass form above, Loader taking the closed blocks.
+template <class Loader, class OpenLoader = void>
 __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
+  constexpr bool kSplit = !std::is_same<OpenLoader, void>::value;
   __shared__ __attribute__((aligned(16))) char lds[2 * kBuf16];
   __shared__ __attribute__((aligned(16))) char qt16[kQ16Lds * 1024];
   __shared__ int32_t ptab[kSegPages];
@@ -1331,7 +1712,13 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   }
   if (stager) {
     wait_vm<0>();
-    h16_stage<Loader>(a, it, lds, ptab);
+    if constexpr (kSplit) {
+      const Int8cSplit sp = int8c_split<kTile16>(a, it);
+      h16_stage<Loader>(a, it.b, it.t_begin, sp.closed_end, it.t_begin, lds, ptab);
+      h16_stage<OpenLoader>(a, it.b, sp.open_begin, it.t_end, sp.open_lo, lds, ptab);
+    } else {
+      h16_stage<Loader>(a, it.b, it.t_begin, it.t_end, it.t_begin, lds, ptab);
+    }
     __syncthreads();                       // the two barriers of the compute waves' merge
     __syncthreads();
     return;
@@ -1363,8 +1750,10 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) pv_off[t4] = swz<kSwz16>(pv_row, 2 * t4 + ((hl & 3) >> 1)) + 8 * (hl & 1);
 
-  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
-    const int seg1 = min(it.t_end, seg0 + kSegPages * kBlock);
+  // Tokens [t_begin, t_end) of the item; rows below t_lo are masked.
+  auto pass = [&](int t_begin, int t_end, int t_lo) {
+  for (int seg0 = t_begin; seg0 < t_end; seg0 += kSegPages * kBlock) {
+    const int seg1 = min(t_end, seg0 + kSegPages * kBlock);
     __syncthreads();                       // earlier users of the buffers and the table are done
     fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
@@ -1407,7 +1796,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int tt = t0 + tw + 4 * grp + r;
         float v = sacc[r] * a.scale_log2;
-        if (!page_ok || tt >= seg1) v = -INFINITY;
+        if (!page_ok || tt >= seg1 || (kSplit && tt < t_lo)) v = -INFINITY;
         sacc[r] = v;
         mx = fmaxf(mx, v);
       }
@@ -1439,6 +1828,14 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
       }
     }
     if (n_tiles & 1) __syncthreads();      // the staging waves' idle step
+  }
+  };
+  if constexpr (kSplit) {
+    const Int8cSplit sp = int8c_split<kTile16>(a, it);
+    pass(it.t_begin, sp.closed_end, it.t_begin);
+    pass(sp.open_begin, it.t_end, sp.open_lo);
+  } else {
+    pass(it.t_begin, it.t_end, it.t_begin);
   }
 
   // ---- merge the four waves (each saw a quarter of every page) ----
@@ -1906,6 +2303,8 @@ using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
 using H16Int8Tok = LoaderInt8Wide<kSwz16, 256, true>;
 using H16Fp8Tok = LoaderInt8Wide<kSwz16, 256, true, true>;
 using H16Int4SymK4 = LoaderInt4Wide<kSwz16, 256, true, true>;
+using H16Int8c = LoaderInt8cWide<kSwz16, 256>;
+using H16Int8cOpen = LoaderInt8cOpenWide<kSwz16, 256>;
 
 hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtype, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
@@ -1918,6 +2317,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h128<4>, grid, block, 0, stream, a);
     else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h128<5>, grid, block, 0, stream, a);
     else if (cache_dtype == 6) hipLaunchKernelGGL(decode_h128<6>, grid, block, 0, stream, a);
+    else if (cache_dtype == 7) hipLaunchKernelGGL(decode_h128<7>, grid, block, 0, stream, a);
     else return hipErrorInvalidValue;
   } else if (num_heads == 16) {
     const dim3 block16(512);                       // 4 compute + 4 staging waves
@@ -1928,6 +2328,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h16<H16Int8Tok>, grid, block16, 0, stream, a);
     else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h16<H16Fp8Tok>, grid, block16, 0, stream, a);
     else if (cache_dtype == 6) hipLaunchKernelGGL(decode_h16<H16Int4SymK4>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 7) hipLaunchKernelGGL((decode_h16<H16Int8c, H16Int8cOpen>), grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;

@@ -74,3 +74,56 @@ def test_int8c_append_bitexact(mode):
             ref = quant.encode_tokens(DT, c[p0: p0 + n], r[p0: p0 + n])
             for k in ("codes", "blk_scale", "r_codes", "r_scale", "open"):
                 assert np.array_equal(got[k], ref[k]), (mode, b, p0, k)
+
+
+DEC_LENS = [1, 31, 32, 33, 64, 95, 96, 130, 200, 2000]
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 3])
+@pytest.mark.parametrize("H", [16, 128])
+def test_int8c_decode_small(H, chunk):
+    """Closed blocks only, open block only, a closed and an open block on one
+    page (33, 95, 130, 200), and work items of one page (chunk 1) that hold only
+    a closed or only an open block."""
+    case = mla_synth.small_decode(case_id=71, H=H, seq_lens=DEC_LENS, paging="shuffled", normalise=False,
+                                  outliers=True)
+    print("int8c decode H=%d chunk=%d" % (H, chunk), flush=True)
+    run, dev = upload(case, DT)
+    out = run_step(run, dev, case.seq_lens, chunk_pages=chunk).float().cpu().numpy()
+    for b in range(case.B):
+        ref_out, _, _ = oracle_seq(case, b, DT)
+        mx, mean = errors(out[b], ref_out)
+        assert mx <= MAX_REL and mean <= MEAN_REL, (b, int(case.seq_lens[b]), mx, mean)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_int8c_decode_after_token_steps(H):
+    """The cache filled one position per call, as decode steps write it, gives
+    the same output, bit for bit, as the cache written by one prompt call."""
+    case = mla_synth.small_decode(case_id=72, H=H, seq_lens=[33, 64, 100], paging="shuffled")
+    run, dev = upload(case, DT)
+    ref = run_step(run, dev, case.seq_lens, chunk_pages=1).clone()
+    run.pool.zero_()
+    for t in range(int(case.seq_lens.max())):
+        bs = [b for b in range(case.B) if t < case.seq_lens[b]]
+        c = np.stack([case.seq_cache(b)[0][t] for b in bs])
+        r = np.stack([case.seq_cache(b)[1][t] for b in bs])
+        s = np.array([case.slots_of(b)[t] for b in bs], np.int64)
+        run.append(to_dev_bits(c), to_dev_bits(r), torch.from_numpy(s).to(DEV))
+    out = run_step(run, dev, case.seq_lens, chunk_pages=1)
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_int8c_full_size_sampled(H):
+    case = mla_synth.v2lite_quant() if H == 16 else mla_synth.v3_decode()
+    print("int8c full H=%d B=%d tokens=%d" % (H, case.B, case.total_tokens), flush=True)
+    run, dev = upload(case, DT)
+    out = run_step(run, dev, case.seq_lens).float().cpu().numpy()
+    lens = case.seq_lens
+    for b in sorted({0, case.B // 2, case.B - 1, int(np.argmax(lens)), int(np.argmin(lens))}):
+        ref_out, _, _ = oracle_seq(case, b, DT)
+        mx, mean = errors(out[b], ref_out)
+        print("  seq %d L=%d max_rel %.2e mean_rel %.2e" % (b, lens[b], mx, mean), flush=True)
+        assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
+    assert np.isfinite(out).all()

@@ -34,9 +34,10 @@ def asm(tmp_path_factory):
 
 def _kernels(lines):
     starts = [(i, m.group(1)) for i, l in enumerate(lines) for m in [re.match(r"^(_ZN3mla\d+decode_h\w+):", l)] if m]
-    assert len(starts) == 14, starts         # decode_h128v2 (bf16), decode_h128 x 6 quantised formats, decode_h16 x 7
+    assert len(starts) == 16, starts         # decode_h128v2 (bf16), decode_h128 x 7 quantised formats, decode_h16 x 8
     for st, name in starts:
-        en = next(i for i in range(st, len(lines)) if "s_endpgm" in lines[i])
+        # the whole function (a kernel may hold several s_endpgm)
+        en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
         yield name, lines[st:en]
 
 
