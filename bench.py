@@ -415,7 +415,13 @@ def main():
     cache_dtype = DTYPES[args.cache_dtype]
     dev = torch.device("cuda:0")
     cfg = api.config(case.H, cache_dtype, case.softmax_scale)
-    run = DecodeRunner(cfg, case.B, case.num_pages, dev)
+    # The step appends each sequence's newest token (position L - 1) again.  For
+    # the per-channel INT8 cache that position closes a 32-token block, and
+    # closing it again over the block's already-quantised rows would read codes
+    # as bf16: there the step's tokens go to one spare page per sequence (outside
+    # the block table), so every step does the same closing work on valid data.
+    spare = case.B if cache_dtype == 7 else 0
+    run = DecodeRunner(cfg, case.B, case.num_pages + spare, dev)
 
     def bits(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -442,6 +448,8 @@ def main():
             n_pend = 0
     new_c = bits(np.stack(last_c))
     new_r = bits(np.stack(last_r))
+    if spare:
+        last_s = [(case.num_pages + b) * 64 + int(s) % 64 for b, s in enumerate(last_s)]
     new_s = torch.from_numpy(np.array(last_s, np.int64)).to(dev)
     q_nope, q_pe = bits(case.q_nope), bits(case.q_pe)
     w_uk, w_uv = bits(case.w_uk), bits(case.w_uv)

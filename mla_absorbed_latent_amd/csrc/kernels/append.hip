@@ -363,60 +363,59 @@ constexpr int kI8cKeyCodes = 64 * 512, kI8cScales = kI8cKeyCodes + 64 * 64, kI8c
               kI8cOverflow = kI8cKeyScales + 64 * 8 * 4;
 constexpr int kTBlk = 32;
 
-// bf16 row pieces of a block's row rr: from the call's input when the call holds
-// that position at index j, else from the block's open storage.
-__device__ __forceinline__ u32x4 i8c_row_piece(const uint16_t* c_kv, const int64_t* slots, int n, int64_t i_close,
-                                               int64_t slot_close, int rr, const uint8_t* page, int blk, int lane) {
-  const int64_t j = i_close - (kTBlk - 1) + rr;
-  const bool in_call = j >= 0 && j < n && slots[j] == slot_close - (kTBlk - 1) + rr;
-  if (in_call) return ld16(c_kv + j * kDc + 8 * lane);
-  const uint8_t* src = lane < 32 ? page + (kTBlk * blk + rr) * 512 + 16 * lane : page + kI8cOverflow + rr * 512 + 16 * (lane - 32);
-  return ld16(src);
-}
-
-// Launch 1: one wave per input token; the wave of a token that closes its block
-// (position 31 within it) quantises the block, lane l owning latent channels
-// 8 l .. 8 l + 7: the maximum down each channel over the 32 rows, then each
-// row's codes (a row's codes overwrite its open storage only after the whole
-// wave has read that row).
+// Launch 1: one work-group per input token; the group of a token that closes its
+// block (position 31 within it) quantises the block, thread t owning latent
+// channels 2 t and 2 t + 1 (channels are independent: no reduction across
+// threads).  Each of the block's rows comes from the call's input when the call
+// holds that position (at index i_close - 31 + rr), else from the block's open
+// storage.  The 32 rows are loaded at once (one memory round trip), then each
+// channel's maximum and each row's codes are formed from registers; the codes
+// overwrite the open storage only after the whole group has read it.
 __global__ __launch_bounds__(256) void append_int8c_close(uint8_t* pool, int64_t num_pages, const uint16_t* c_kv,
                                                           const int64_t* slots, int n) {
-  const int64_t tok = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // uniform per wave
-  const int lane = threadIdx.x & 63;
-  if (tok >= n) return;
+  const int64_t tok = blockIdx.x;
+  const int t = threadIdx.x;
   const int64_t slot = slots[tok];
-  if (!slot_ok(slot, num_pages) || slot % kTBlk != kTBlk - 1) return;
+  if (!slot_ok(slot, num_pages) || slot % kTBlk != kTBlk - 1) return;   // uniform per group
   uint8_t* page = pool + (slot / kBlock) * (int64_t)kPageInt8c;
   const int blk = (int)((slot % kBlock) / kTBlk);
-  float amax[8];
+  const int ch = 2 * t;
+  // The slots of the call's 31 preceding indices, read unconditionally (index
+  // clamped) so that the reads issue together.
+  int64_t prev[kTBlk];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) amax[c] = 0.f;
+  for (int rr = 0; rr < kTBlk; ++rr) prev[rr] = slots[max(tok - (kTBlk - 1) + rr, (int64_t)0)];
+  uint32_t v[kTBlk];                       // channels ch, ch + 1 of row rr (bf16 pair)
+#pragma unroll
   for (int rr = 0; rr < kTBlk; ++rr) {
-    const u32x4 v = i8c_row_piece(c_kv, slots, n, tok, slot, rr, page, blk, lane);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      amax[2 * d] = fmaxf(amax[2 * d], fabsf(__uint_as_float(v[d] << 16)));
-      amax[2 * d + 1] = fmaxf(amax[2 * d + 1], fabsf(__uint_as_float(v[d] & 0xffff0000u)));
-    }
+    const int64_t j = tok - (kTBlk - 1) + rr;  // < n, as tok < n
+    const bool in_call = j >= 0 && prev[rr] == slot - (kTBlk - 1) + rr;
+    const uint8_t* open = ch < kDc / 2 ? page + (kTBlk * blk + rr) * 512 + 2 * ch
+                                       : page + kI8cOverflow + rr * 512 + 2 * (ch - kDc / 2);
+    const uint8_t* src = in_call ? reinterpret_cast<const uint8_t*>(c_kv + j * kDc + ch) : open;
+    v[rr] = *reinterpret_cast<const uint32_t*>(src);
   }
-  float scale[8];
+  float amax0 = 0.f, amax1 = 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) scale[c] = __fdiv_rn(amax[c], 127.0f);
   for (int rr = 0; rr < kTBlk; ++rr) {
-    const u32x4 v = i8c_row_piece(c_kv, slots, n, tok, slot, rr, page, blk, lane);
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float x = __uint_as_float(c & 1 ? (v[c >> 1] & 0xffff0000u) : (v[c >> 1] << 16));
-      float q = 0.f;
-      if (scale[c] != 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(x, scale[c])), -127.f), 127.f);
-      packed[c >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (c & 3));
-    }
-    *reinterpret_cast<u32x2*>(page + (kTBlk * blk + rr) * 512 + 8 * lane) = u32x2{packed[0], packed[1]};
+    amax0 = fmaxf(amax0, fabsf(__uint_as_float(v[rr] << 16)));
+    amax1 = fmaxf(amax1, fabsf(__uint_as_float(v[rr] & 0xffff0000u)));
   }
-  float* sc = reinterpret_cast<float*>(page + kI8cScales) + blk * kDc + 8 * lane;
+  const float s0 = __fdiv_rn(amax0, 127.0f), s1 = __fdiv_rn(amax1, 127.0f);
+  __syncthreads();                         // every row read before any code is written over it
+  auto code = [](float x, float sc) {
+    float q = 0.f;
+    if (sc != 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(x, sc)), -127.f), 127.f);
+    return (uint32_t)(int)q & 0xffu;
+  };
 #pragma unroll
-  for (int c = 0; c < 8; ++c) sc[c] = scale[c];
+  for (int rr = 0; rr < kTBlk; ++rr) {
+    const uint32_t c = code(__uint_as_float(v[rr] << 16), s0) | (code(__uint_as_float(v[rr] & 0xffff0000u), s1) << 8);
+    *reinterpret_cast<uint16_t*>(page + (kTBlk * blk + rr) * 512 + ch) = (uint16_t)c;
+  }
+  float* sc = reinterpret_cast<float*>(page + kI8cScales) + blk * kDc + ch;
+  sc[0] = s0;
+  sc[1] = s1;
 }
 
 // Launch 2 (after launch 1 on the stream): one wave per input token; lanes 0-7
@@ -459,9 +458,9 @@ hipError_t launch_append(int cache_dtype, void* pool, int64_t num_pages, const u
                        c_kv, k_pe, slots, n);
   } else if (cache_dtype == 7) {
     const int64_t work = (int64_t)n * 64;                  // one wave a token
-    const dim3 grid((unsigned)((work + 255) / 256));
-    hipLaunchKernelGGL(append_int8c_close, grid, dim3(256), 0, stream, p, num_pages, c_kv, slots, n);
-    hipLaunchKernelGGL(append_int8c_tok, grid, dim3(256), 0, stream, p, num_pages, c_kv, k_pe, slots, n);
+    hipLaunchKernelGGL(append_int8c_close, dim3((unsigned)n), dim3(256), 0, stream, p, num_pages, c_kv, slots, n);
+    hipLaunchKernelGGL(append_int8c_tok, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, p, num_pages,
+                       c_kv, k_pe, slots, n);
   } else if (cache_dtype == 4 || cache_dtype == 5) {
     const int64_t work = (int64_t)n * 64;                  // one wave a token
     hipLaunchKernelGGL(cache_dtype == 4 ? append_int8t : append_fp8t, dim3((unsigned)((work + 255) / 256)),
