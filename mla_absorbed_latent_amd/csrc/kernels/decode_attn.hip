@@ -1892,6 +1892,418 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 }
 
 // ===========================================================================
+// H = 16, FP8 (e4m3, per-token scale) cache on the FP8 matrix instructions
+// ===========================================================================
+// Both products run on v_mfma_scale_f32_16x16x128_f8f6f4 with the cache's own
+// e4m3 codes as one operand, so the staging waves copy raw page bytes into LDS
+// and dequantise nothing:
+//   scores  S^T[tokens][heads] = K[tokens][128 ch] . q~^T, four K-steps over the
+//           512 latent channels.  q~ goes in as two e4m3 terms with a power-of-
+//           two scale per head (hi = e4m3(q~ 2^-e), lo = e4m3((q~ 2^-e - hi) 2^4)),
+//           both terms into one accumulator through the instruction's block
+//           scales (2^e and 2^(e-4)); the token's fp32 scale multiplies the
+//           result row.  The RoPE key (per-8-group scales) is widened to fp16 in
+//           registers for two 16x16x32 fp16 products.
+//   values  O^T[features][heads] += V^T[features][128 tokens] . P'', with
+//           P' = P * (token scale) and P'' its two e4m3 terms under a power-of-
+//           two scale per 32-token block and head, passed as the block scales of
+//           the B operand; V^T comes from the raw tile by 8-bit transposed LDS
+//           reads (ds_read_b64_tr_b8).
+// The two-term split keeps each operand to about 2^-8 relative (the precision
+// contract's FP8 case); two FP8 products take the matrix core as long as one
+// fp16 product of the same shape, so what this gains is staging work and LDS
+// bytes, and with them a second 128-token tile in flight per CU.
+//
+// Instruction layout (16x16x128, 8-bit operands; established by in-bounds
+// probes on gfx950): lane l = 16 g + r holds row (or column) r; its byte j is
+// K = 64 (j / 16) + 16 g + j % 16; the block scale of K-block b (K 32 b .. +31)
+// of row r is the scale operand of lane 16 b + r; the result lane l holds rows
+// 4 g .. 4 g + 3 of column r.
+//
+// Work-group: waves 0-3 compute, waves 4-7 stage (as decode_h16).  128-token
+// tiles (two pages); compute wave w takes the scores of tokens 32 w .. 32 w + 31
+// (K-block w of the value product) and the value product of features
+// 128 w .. 128 w + 127 for all 16 heads, so the softmax maximum and P cross the
+// waves through LDS (three barriers per tile) and no merge is needed at the end.
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+typedef int int32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileF8 = 128;
+constexpr int kRowF8 = 576;                               // raw row: 512 latent codes, 64 RoPE-key codes
+constexpr int kPageF8 = kBlock * 612;                     // [64][576] codes | [64] f32 | [64][8] f32
+constexpr int kPgLatScale = 64 * 576, kPgKeyScale = kPgLatScale + 64 * 4;
+constexpr int kF8LatScale = kTileF8 * kRowF8;             // LDS tile: rows | [128] f32 | [128][8] f32
+constexpr int kF8KeyScale = kF8LatScale + kTileF8 * 4;
+constexpr int kBufF8 = kF8KeyScale + kTileF8 * 32;        // 78,336 B
+constexpr int kPexF8 = 2 * 16 * kTileF8;                  // P'' terms: [2][16 heads][128 tokens] bytes
+constexpr int kSegPagesF8 = 256;
+
+// Raw-row swizzle: 16-byte chunk c of row r sits at chunk c ^ f8_swz(r) (low two
+// bits), so that the score reads (16 consecutive rows, one chunk) and the
+// transposed reads (rows 16 g + j and 16 g + 16 + j for the two lane groups of
+// a pass, or their +64 copies) hit 16 different bank quads.
+__device__ __forceinline__ uint32_t f8_swz(int r) { return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1); }
+__device__ __forceinline__ uint32_t f8_off(int r, int c) { return r * kRowF8 + 16 * (c ^ f8_swz(r)); }
+// P'' exchange: head h's 128 bytes of term t, 16-byte chunk c at c ^ ((h >> 1) & 7).
+__device__ __forceinline__ uint32_t pex_off(int t, int h, int c) { return t * 2048 + h * 128 + 16 * (c ^ ((h >> 1) & 7)); }
+
+__device__ __forceinline__ floatx4 mfma_f8(int32x8 a, int32x8 b, floatx4 c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+// Power-of-two exponent that maps a positive maximum m into [128, 256): m 2^-e,
+// clamped to [-120, 120] so that the block scales 127 + e and 127 + e - 4 stay
+// valid E8M0 codes (a smaller maximum, e.g. subnormal, only lets its block's
+// values underflow: they are below 2^-113 of the largest).
+__device__ __forceinline__ int f8_exp(float m) {
+  const int e = m > 0.f ? (int)((__float_as_uint(m) >> 23) & 0xffu) - 127 - 7 : 0;
+  return min(max(e, -120), 120);
+}
+// Two e4m3 terms of v (|v| < 256): hi = e4m3(v), lo = e4m3((v - hi) 2^4), packed
+// four values per word.
+__device__ __forceinline__ void f8_split4(const float (&v)[4], uint32_t& hi, uint32_t& lo) {
+  uint32_t h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)h, true);
+  float r[4];
+  r[0] = (v[0] - __builtin_amdgcn_cvt_f32_fp8((int)h, 0)) * 16.f;
+  r[1] = (v[1] - __builtin_amdgcn_cvt_f32_fp8((int)h, 1)) * 16.f;
+  r[2] = (v[2] - __builtin_amdgcn_cvt_f32_fp8((int)h, 2)) * 16.f;
+  r[3] = (v[3] - __builtin_amdgcn_cvt_f32_fp8((int)h, 3)) * 16.f;
+  uint32_t l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+  l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], (int)l, true);
+  hi = h;
+  lo = l;
+}
+
+// Staging of one raw 128-token tile (threads kTid0 .. kTid0 + 255).  Load i of
+// thread t is 16-byte chunk t + 256 (i % 9) of page i / 9's code block (2,304
+// chunks: row = chunk / 36, column chunk % 36), so that consecutive lanes read
+// consecutive bytes; plus 16 bytes of the key scales and 16 bytes of the latent
+// scales (stored by t < 32 only; every thread loads, so that each wave issues
+// the same number of loads).  Rows past t_end and pages out of range read the
+// zero page.
+template <int kTid0>
+struct LoaderF8Raw {
+  static constexpr int kLoads = 20;
+  u32x4 c[18] = {};
+  u32x4 ks = {}, ls = {};
+
+  template <int I>
+  __device__ __forceinline__ void issue_one(const DecodeArgs& a, int64_t pgi, int t0, int t_end) {
+    const int q = ltid<kTid0>() + 256 * (I % 9), row = q / 36;
+    const uint8_t* src = page_base(a, pgi, pgi >= 0 && t0 + 64 * (I / 9) + row < t_end, kPageF8) + 16 * q;
+    asm_ld16_nt<0>(c[I], src);
+  }
+  __device__ __forceinline__ void issue(const DecodeArgs& a, int64_t p0, int64_t p1, int t0, int t_end) {
+    issue_one<0>(a, p0, t0, t_end);
+    issue_one<1>(a, p0, t0, t_end);
+    issue_one<2>(a, p0, t0, t_end);
+    issue_one<3>(a, p0, t0, t_end);
+    issue_one<4>(a, p0, t0, t_end);
+    issue_one<5>(a, p0, t0, t_end);
+    issue_one<6>(a, p0, t0, t_end);
+    issue_one<7>(a, p0, t0, t_end);
+    issue_one<8>(a, p0, t0, t_end);
+    issue_one<9>(a, p1, t0, t_end);
+    issue_one<10>(a, p1, t0, t_end);
+    issue_one<11>(a, p1, t0, t_end);
+    issue_one<12>(a, p1, t0, t_end);
+    issue_one<13>(a, p1, t0, t_end);
+    issue_one<14>(a, p1, t0, t_end);
+    issue_one<15>(a, p1, t0, t_end);
+    issue_one<16>(a, p1, t0, t_end);
+    issue_one<17>(a, p1, t0, t_end);
+    const int t = ltid<kTid0>();
+    const int64_t pk = t < 128 ? p0 : p1;
+    asm_ld16_nt<0>(ks, page_base(a, pk, pk >= 0, kPageF8) + kPgKeyScale + 16 * (t & 127));
+    const int64_t pl = (t & 31) < 16 ? p0 : p1;
+    asm_ld16_nt<0>(ls, page_base(a, pl, pl >= 0, kPageF8) + kPgLatScale + 16 * (t & 15));
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int i = 0; i < 18; ++i) settle(c[i]);
+    settle(ks);
+    settle(ls);
+  }
+  __device__ __forceinline__ void commit(char* buf) {
+    const int t = ltid<kTid0>();
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      const int q = t + 256 * (i % 9), row = q / 36;
+      *reinterpret_cast<u32x4*>(buf + f8_off(64 * (i / 9) + row, q - 36 * row)) = c[i];
+    }
+    *reinterpret_cast<u32x4*>(buf + kF8KeyScale + 2048 * (t >> 7) + 16 * (t & 127)) = ks;
+    if (t < 32) *reinterpret_cast<u32x4*>(buf + kF8LatScale + 256 * (t >> 4) + 16 * (t & 15)) = ls;
+  }
+};
+
+__device__ __forceinline__ void fill_ptab_n(const DecodeArgs& a, int b, int t0, int t1, int32_t* ptab) {
+  const int n = (t1 - t0 + kBlock - 1) / kBlock;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ptab[i] = (int32_t)page_of(a, b, t0 + i * kBlock);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_h16f8(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kBufF8];
+  __shared__ __attribute__((aligned(16))) char pex[kPexF8];
+  __shared__ float xmax[4][16];            // per wave and head: the tile maximum, then (end) the sum
+  __shared__ int xexp[4][16];              // per 32-token block and head: P'' exponent
+  __shared__ int32_t ptab[kSegPagesF8];
+  ItemRange it = item_range(a);
+  if (!it.ok) return;
+  if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
+  const bool stager = threadIdx.x >= 256;          // waves 4-7 (uniform per wave)
+  const int lane = threadIdx.x & 63;
+  const int w = (threadIdx.x >> 6) & 3;
+  const int r = lane & 15, g = lane >> 4;          // MFMA row/column r, lane group g
+
+  if (stager) {
+    for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPagesF8 * kBlock) {
+      const int seg1 = min(it.t_end, seg0 + kSegPagesF8 * kBlock);
+      __syncthreads();                     // earlier users of the buffers and the table are done
+      fill_ptab_n(a, it.b, seg0, seg1, ptab);
+      __syncthreads();
+      const int n_tiles = (seg1 - seg0 + kTileF8 - 1) / kTileF8;
+      const int n_pg = (seg1 - seg0 + kBlock - 1) / kBlock;
+      auto pg = [&](int i) -> int64_t { return i < n_pg ? ptab[i] : -1; };
+      LoaderF8Raw<256> ld0, ld1;
+      ld0.issue(a, pg(0), pg(1), seg0, seg1);
+      wait_vm<0>();
+      ld0.settle_all();
+      ld0.commit(lds);
+      ld1.issue(a, pg(2), pg(3), seg0 + kTileF8, seg1);
+      ld0.issue(a, pg(4), pg(5), seg0 + 2 * kTileF8, seg1);
+      auto stage_step = [&](int s, LoaderF8Raw<256>& ldn) {
+        __syncthreads();                   // X1: tile s in place, buffer (s + 1) % 2 free
+        const int64_t q0 = pg(2 * s + 6), q1 = pg(2 * s + 7);
+        wait_vm<LoaderF8Raw<256>::kLoads>();   // the other loader's tile stays in flight
+        ldn.settle_all();
+        ldn.commit(lds + ((s + 1) & 1) * kBufF8);
+        ldn.issue(a, q0, q1, seg0 + (s + 3) * kTileF8, seg1);
+        __syncthreads();                   // X2 (the compute waves' maximum exchange)
+        __syncthreads();                   // X3 (their P exchange)
+      };
+      for (int s = 0; s < n_tiles; s += 2) {
+        stage_step(s, ld1);
+        stage_step(s + 1, ld0);
+      }
+      wait_vm<0>();                        // the last (zero-page) tiles
+    }
+    __syncthreads();                       // the compute waves' final sum exchange
+    return;
+  }
+
+  // ---- compute waves: q~ as two e4m3 terms (lane: head r, channels of K-step s
+  // 128 s + 16 g + 0..15 and 128 s + 64 + 16 g + 0..15), the RoPE part in fp16
+  // (16x16x32 B operand: channels 512 + 8 g + 32 j .. +7).
+  int32x8 qh[4], ql[4];
+  half8 qr[2];
+  int eq;                                  // per-head exponent of q~
+  {
+    const uint16_t* qp = a.q_abs + ((int64_t)it.b * 16 + r) * kDk;
+    half8 x[4][4];                         // K-step s, piece 2 hh + k: channels 128 s + 64 hh + 16 g + 8 k .. +7
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[s][k] = __builtin_bit_cast(half8, ld16(qp + 128 * s + 64 * (k >> 1) + 16 * g + 8 * (k & 1)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) qr[j] = __builtin_bit_cast(half8, ld16(qp + kDc + 8 * g + 32 * j));
+    float m = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)x[s][k][e]));
+    m = wave_max_xor(m, 16);
+    m = wave_max_xor(m, 32);                // all 512 channels of head r
+    eq = f8_exp(m);
+    const float sc = __uint_as_float((uint32_t)(127 - eq) << 23);   // 2^-eq
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const half8& xs = x[s][d >> 1];
+        const int e0 = 4 * (d & 1);
+        const float x4[4] = {(float)xs[e0] * sc, (float)xs[e0 + 1] * sc, (float)xs[e0 + 2] * sc, (float)xs[e0 + 3] * sc};
+        uint32_t hi, lo;
+        f8_split4(x4, hi, lo);
+        qh[s][d] = (int)hi;
+        ql[s][d] = (int)lo;
+      }
+  }
+  wait_vm<0>();
+  const int sq_hi = 127 + eq, sq_lo = 127 + eq - 4;
+  floatx4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = floatx4{};
+  float m_run = -INFINITY, l_sum = 0.f;
+
+  for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPagesF8 * kBlock) {
+    const int seg1 = min(it.t_end, seg0 + kSegPagesF8 * kBlock);
+    __syncthreads();
+    fill_ptab_n(a, it.b, seg0, seg1, ptab);
+    __syncthreads();
+    const int n_tiles = (seg1 - seg0 + kTileF8 - 1) / kTileF8;
+    const int n_pg = (seg1 - seg0 + kBlock - 1) / kBlock;
+    for (int s = 0; s < n_tiles; ++s) {
+      __syncthreads();                     // X1
+      const char* buf = lds + (s & 1) * kBufF8;
+      const int t0 = seg0 + s * kTileF8;
+      // ---- scores of tokens 32 w + 16 rb + 0..15 (rows), all heads (columns)
+      float p[2][4];
+      float lat[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = 32 * w + 16 * rb + r;
+        floatx4 acc = floatx4{}, accr = floatx4{};
+        auto kread = [&](int s4) {
+          const u32x4 k0 = *reinterpret_cast<const u32x4*>(buf + f8_off(row, 8 * s4 + g));
+          const u32x4 k1 = *reinterpret_cast<const u32x4*>(buf + f8_off(row, 8 * s4 + 4 + g));
+          return int32x8{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3], (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+        };
+        int32x8 ka = kread(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          int32x8 kn = ka;
+          if (s4 + 1 < 4) kn = kread(s4 + 1);
+          acc = mfma_f8(ka, qh[s4], acc, 127, sq_hi);
+          acc = mfma_f8(ka, ql[s4], acc, 127, sq_lo);
+          ka = kn;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // RoPE key codes 8 g + 32 j .. +7 of the row (chunk 32 + 2 j + g / 2, half g % 2) and their group scale
+          const u32x2 kc = *reinterpret_cast<const u32x2*>(buf + f8_off(row, 32 + 2 * j + (g >> 1)) + 8 * (g & 1));
+          const float ksc = reinterpret_cast<const float*>(buf + kF8KeyScale)[row * 8 + g + 4 * j];
+          const _Float16 s256 = (_Float16)(ksc * 256.f);
+          const u32x2 lo = fp8x4_to_f16(kc[0], half2v{s256, s256}), hi = fp8x4_to_f16(kc[1], half2v{s256, s256});
+          const half8 kr = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          accr = mfma16x16x32(kr, qr[j], accr);
+        }
+        // result rows 32 w + 16 rb + 4 g + i
+        const floatx4 ls = *reinterpret_cast<const floatx4*>(buf + kF8LatScale + 4 * (32 * w + 16 * rb + 4 * g));
+        const bool page_ok = (2 * s + ((32 * w + 16 * rb) >> 6) < n_pg) &&
+                             ptab[min(2 * s + ((32 * w + 16 * rb) >> 6), n_pg - 1)] >= 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = t0 + 32 * w + 16 * rb + 4 * g + i;
+          const bool ok = page_ok && tt < seg1;
+          float v = (acc[i] * ls[i] + accr[i]) * a.scale_log2;
+          v = ok ? v : -INFINITY;
+          p[rb][i] = v;
+          lat[rb][i] = ok ? ls[i] : 0.f;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);           // this wave's 32 tokens, head r
+      if (g == 0) xmax[w][r] = mx;
+      __syncthreads();                     // X2
+      const float mt = fmaxf(fmaxf(xmax[0][r], xmax[1][r]), fmaxf(xmax[2][r], xmax[3][r]));
+      const bool need = mt > m_run + kTau;
+      if (__ballot(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        l_sum *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      // P, its sum, and P' = P * token scale as two e4m3 terms under this block's exponent
+      float pm = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(p[rb][i] - m_use);
+          l_sum += e;
+          p[rb][i] = e * lat[rb][i];
+          pm = fmaxf(pm, p[rb][i]);
+        }
+      pm = wave_max_xor(pm, 16);
+      pm = wave_max_xor(pm, 32);
+      const int ep = f8_exp(pm);
+      const float sp = __uint_as_float((uint32_t)(127 - ep) << 23);
+      if (g == 0) xexp[w][r] = ep;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float x4[4] = {p[rb][0] * sp, p[rb][1] * sp, p[rb][2] * sp, p[rb][3] * sp};
+        uint32_t hi, lo;
+        f8_split4(x4, hi, lo);
+        const int c = 2 * w + rb;          // token chunk of 32 w + 16 rb, byte 4 g
+        *reinterpret_cast<uint32_t*>(pex + pex_off(0, r, c) + 4 * g) = hi;
+        *reinterpret_cast<uint32_t*>(pex + pex_off(1, r, c) + 4 * g) = lo;
+      }
+      __syncthreads();                     // X3
+      // ---- values: B = P'' (lane: head r, tokens 16 g + 0..15 and 64 + 16 g + 0..15)
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(pex + pex_off(0, r, g));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(pex + pex_off(0, r, 4 + g));
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(pex + pex_off(1, r, g));
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(pex + pex_off(1, r, 4 + g));
+      const int32x8 ph = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+      const int32x8 pl = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      const int eb = xexp[g][r];           // block g = compute wave g's tokens
+      const int sp_hi = 127 + eb, sp_lo = 127 + eb - 4;
+      // A = V^T: lane 16 g + 2 j + h addresses row (token) base_q + j, byte 8 h of
+      // the feature chunk; the four reads take tokens 16 g + 0..7, + 8..15,
+      // 64 + 16 g + 0..7, + 8..15.  Row offsets are formed here from an opaque
+      // copy of the lane index, so that the compiler keeps four bases live, not
+      // thirty-two addresses.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int jj = (ln & 15) >> 1, hh = ln & 1, gq = ln >> 4;
+      uint32_t vbase[4], vswz[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 64 * (q >> 1) + 16 * gq + 8 * (q & 1) + jj;
+        vbase[q] = row * kRowF8 + 128 * w + 8 * hh;
+        vswz[q] = 16 * f8_swz(row);
+      }
+      auto vread = [&](int fb) {
+        int32x2 v4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v4[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) int32x2*)((lds_char*)buf + vbase[q] + ((16u * fb) ^ vswz[q])));
+        return int32x8{v4[0][0], v4[0][1], v4[1][0], v4[1][1], v4[2][0], v4[2][1], v4[3][0], v4[3][1]};
+      };
+      int32x8 va = vread(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) {
+        int32x8 vn = va;
+        if (fb + 1 < 8) vn = vread(fb + 1);     // the next block's operand, read under this block's products
+        o[fb] = mfma_f8(va, ph, o[fb], 127, sp_hi);
+        o[fb] = mfma_f8(va, pl, o[fb], 127, sp_lo);
+        va = vn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (n_tiles & 1) {                     // the staging waves' idle step
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    }
+  }
+
+  // ---- the heads' sums over the four waves' tokens, then o_part and lse
+  l_sum += __shfl_xor(l_sum, 16, 64);
+  l_sum += __shfl_xor(l_sum, 32, 64);
+  if (g == 0) xmax[w][r] = l_sum;
+  __syncthreads();
+  const float l = xmax[0][r] + xmax[1][r] + xmax[2][r] + xmax[3][r];
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* op = a.o_part + ((int64_t)it.out_row * 16 + r) * kDc + 128 * w + 4 * g;
+#pragma unroll
+  for (int fb = 0; fb < 8; ++fb)
+    *reinterpret_cast<half4*>(op + 16 * fb) = __builtin_convertvector(o[fb] * inv, half4);   // nearest even
+  if (w == 0 && g == 0) a.lse_part[(int64_t)it.out_row * 16 + r] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ===========================================================================
 // H = 128, bf16 cache: eight waves per work-group, two per SIMD
 // ===========================================================================
 // A single wave per SIMD (decode_h128 above) leaves the matrix cores idle
@@ -2301,7 +2713,6 @@ using H16Int8 = LoaderInt8Wide<kSwz16, 256>;
 using H16Int4 = LoaderInt4Wide<kSwz16, 256>;
 using H16Int4Sym = LoaderInt4Wide<kSwz16, 256, true>;
 using H16Int8Tok = LoaderInt8Wide<kSwz16, 256, true>;
-using H16Fp8Tok = LoaderInt8Wide<kSwz16, 256, true, true>;
 using H16Int4SymK4 = LoaderInt4Wide<kSwz16, 256, true, true>;
 using H16Int8c = LoaderInt8cWide<kSwz16, 256>;
 using H16Int8cOpen = LoaderInt8cOpenWide<kSwz16, 256>;
@@ -2326,7 +2737,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int num_heads, int cache_dtyp
     else if (cache_dtype == 2) hipLaunchKernelGGL(decode_h16<H16Int4>, grid, block16, 0, stream, a);
     else if (cache_dtype == 3) hipLaunchKernelGGL(decode_h16<H16Int4Sym>, grid, block16, 0, stream, a);
     else if (cache_dtype == 4) hipLaunchKernelGGL(decode_h16<H16Int8Tok>, grid, block16, 0, stream, a);
-    else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h16<H16Fp8Tok>, grid, block16, 0, stream, a);
+    else if (cache_dtype == 5) hipLaunchKernelGGL(decode_h16f8, grid, block16, 0, stream, a);
     else if (cache_dtype == 6) hipLaunchKernelGGL(decode_h16<H16Int4SymK4>, grid, block16, 0, stream, a);
     else if (cache_dtype == 7) hipLaunchKernelGGL((decode_h16<H16Int8c, H16Int8cOpen>), grid, block16, 0, stream, a);
     else return hipErrorInvalidValue;

@@ -72,15 +72,17 @@ def _h128_redo_taken(s):
     return bool(np.any(s[:, 32:].max(axis=1) > s[:, :32].max(axis=1) + 15.0))
 
 
-def _h16_rescale_taken(s):
-    """Some head of some compute wave (tokens 16 w .. 16 w + 15 of every 64-token
-    tile) sees its running maximum grow by more than 8 after a non-empty tile,
-    so its sums are rescaled by a factor other than 0."""
+def _h16_rescale_taken(s, cache_dtype=0):
+    """Some head's running maximum grows by more than 8 after a non-empty tile,
+    so its sums are rescaled by a factor other than 0.  The 16-head kernels keep
+    that maximum per compute wave over tokens 16 w .. 16 w + 15 of every 64-token
+    tile, except the FP8 one, whose waves share one maximum per 128-token tile."""
     H, L = s.shape
-    for w in range(4):
+    tile, part = (128, 128) if cache_dtype == 5 else (64, 16)
+    for w in range(tile // part):
         m = np.full(H, -np.inf)
-        for t0 in range(0, L, 64):
-            lo, hi = t0 + 16 * w, min(t0 + 16 * w + 16, L)
+        for t0 in range(0, L, tile):
+            lo, hi = t0 + part * w, min(t0 + part * w + part, L)
             if lo >= hi:
                 continue
             mx = s[:, lo:hi].max(axis=1)
@@ -131,7 +133,7 @@ def _early_max_case(H, case_id=61):
 def test_late_maximum(H, cache_dtype):
     case = _spread_case(H)
     scores = [_log2_scores(case, b, cache_dtype) for b in range(case.B)]
-    taken = _h128_redo_taken if H == 128 else _h16_rescale_taken
+    taken = _h128_redo_taken if H == 128 else (lambda s: _h16_rescale_taken(s, cache_dtype))
     assert any(taken(s) for s in scores), "case does not reach the branch"
     _note("late max H=%d dtype=%d spread %.1f log2" % (H, cache_dtype, float(np.ptp(scores[0]))))
     _check(case, cache_dtype, chunk=1000)      # one work item per sequence

@@ -69,6 +69,20 @@ def test_no_scratch_reads_in_tile_loops(asm):
             assert reloads == 0, (name, a, b, reloads)
 
 
+def test_no_scratch_reads_in_staging_loops(asm):
+    """The 16-head kernels' staging loops (no matrix instructions, so not covered
+    above) must not reload spills either: a reload waits behind the tile loads
+    the loop keeps in flight."""
+    checked = 0
+    for name, body in _kernels(asm):
+        if "decode_h16" not in name:
+            continue
+        for hdr, seg in _staging_loops(body):
+            assert not any("scratch_load" in x for x in seg), (name, hdr)
+            checked += 1
+    assert checked >= 9, checked
+
+
 def test_scratch_stays_small(asm):
     text = "\n".join(asm)
     for m in re.finditer(r"\.name:\s+(_ZN3mla\d+decode_h\S+)\s*\n(?:.*\n){0,80}?\s+\.private_segment_fixed_size:\s+(\d+)", text):
