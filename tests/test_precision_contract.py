@@ -20,7 +20,10 @@ times; split into two e4m3 terms (the value and the e4m3 rounding of its
 remainder, both products accumulated in fp32) both operands meet it.  Two FP8
 products take the matrix cores as long as one fp16 product of the same shape
 (twice the rate, twice the work), so FP8 matrix instructions can only save
-operand conversion and LDS traffic, not matrix time.
+operand conversion and LDS traffic, not matrix time.  The last test emulates
+the 16-head FP8 decode's own form of that split (power-of-two scales per head
+for q~ and per 32 tokens and head for P, the token scale folded into P, the
+cache's e4m3 codes as the other operand) on the quantised V2-Lite workload.
 """
 import numpy as np
 import pytest
@@ -123,4 +126,74 @@ def test_e4m3_operands_exceed_the_mean_relative_bound(v3_sequence):
 
 def test_two_term_e4m3_operands_meet_the_tolerance(v3_sequence):
     mx, mean = _emulate(v3_sequence, _two_term(_fp8(32)), _two_term(_fp8()))
+    assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
+
+
+def _pow2_split(x, axis):
+    """The FP8 decode's operand split: a power-of-two scale per slice along
+    `axis` (the slice maximum mapped into [128, 256)), two e4m3 terms with the
+    second scaled by 2^4; returns the value the matrix core multiplies."""
+    x = np.asarray(x, np.float32)
+    m = np.abs(x).max(axis=axis, keepdims=True)
+    e = np.where(m > 0, np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7, 0).clip(-120, 120)
+    s = np.float32(2.0) ** e.astype(np.float32)
+    y = (x / s).astype(np.float32)
+    hi = _e4m3(y)
+    lo = _e4m3((y - hi) * np.float32(16.0))
+    return ((hi.astype(np.float64) + lo.astype(np.float64) / 16.0) * s).astype(np.float64)
+
+
+def test_fp8_matrix_instruction_scheme_meets_the_tolerance():
+    """The 16-head FP8 decode's arithmetic on the per-token FP8 cache of the
+    quantised V2-Lite workload (one 16,384-token sequence): latent scores from
+    the e4m3 codes times q~ split in two e4m3 terms (power-of-two scale per head),
+    times the token's scale; RoPE key widened to fp16; softmax with the running
+    maximum moved when a 128-token tile exceeds it by more than 8; P times the
+    token scale split in two e4m3 terms (power-of-two scale per 32 tokens and
+    head) against the raw codes; fp16 partial, fp16 latent into W_UV, bf16
+    output.  Reference: the fp64 oracle over the same dequantised cache."""
+    from oracle import quant
+    case = mla_synth.small_decode(case_id=5, H=16, seq_lens=[16384], normalise=False, outliers=True)
+    c_bits, r_bits = case.seq_cache(0)
+    f = quant.encode_tokens(quant.CACHE_FP8_TOK, c_bits, r_bits)
+    c32, r32 = quant.dequant_fields(quant.CACHE_FP8_TOK, f)
+    qn = mla_ref.bf16_to_f64(case.q_nope[0])
+    qp = mla_ref.bf16_to_f64(case.q_pe[0])
+    w_uk = mla_ref.bf16_to_f64(case.w_uk)
+    w_uv = mla_ref.bf16_to_f64(case.w_uv)
+    ref, _, _ = mla_ref.absorbed_decode(qn, qp, c32.astype(np.float64), r32.astype(np.float64), w_uk, w_uv,
+                                        case.softmax_scale)
+
+    codes = f["codes"]
+    v_lat = quant.fp8_e4m3_decode(codes[:, :512]).astype(np.float64)          # raw e4m3 values
+    lat_s = f["c_scale"].reshape(-1).astype(np.float64)
+    r_val = _f16(_f16(quant.fp8_e4m3_decode(codes[:, 512:]) / 256.0)
+                 * _f16(np.repeat(f["r_scale"], 8, axis=1) * 256.0)).astype(np.float64)
+    q_abs = _f16(mla_ref.absorb_q(qn[None], w_uk)[0])                          # fp16 q~, as stored
+    q_eff = _pow2_split(q_abs, axis=1)
+    s = ((v_lat @ q_eff.T) * lat_s[:, None] + r_val @ _f16(qp).astype(np.float64).T).T   # [H, L]
+    s = (s * case.softmax_scale / np.log(2.0)).astype(np.float32)
+    H, L = s.shape
+    m = np.full(H, -np.inf, np.float32)
+    l_sum = np.zeros(H, np.float64)
+    o = np.zeros((H, 512))
+    for t0 in range(0, L, 128):
+        st = s[:, t0:t0 + 128]
+        mt = st.max(axis=1)
+        need = mt > m + 8.0
+        if np.any(need):
+            alpha = np.where(need, np.exp2(np.where(np.isfinite(m), m - np.where(need, mt, m), -np.inf)), 1.0)
+            o *= alpha[:, None]
+            l_sum *= alpha
+            m = np.where(need, mt, m)
+        p = np.exp2(st - m[:, None]).astype(np.float32)
+        l_sum += p.sum(axis=1, dtype=np.float32)
+        pp = (p * lat_s[None, t0:t0 + 128]).astype(np.float32)
+        blocks = pp.reshape(H, -1, 32)
+        p_eff = _pow2_split(blocks, axis=2).reshape(H, -1)
+        o += p_eff @ v_lat[t0:t0 + 128]
+    o_lat = _f16(o / l_sum[:, None]).astype(np.float64)
+    out = _bf16(np.einsum("hc,hdc->hd", o_lat, w_uv)).astype(np.float64)
+    d = np.abs(out - ref)
+    mx, mean = d.max() / np.abs(ref).max(), d.sum() / np.abs(ref).sum()
     assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
