@@ -489,18 +489,19 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     clock_after = clock_probe_ghz(torch, dev)
 
-    # ---- the dominant kernel alone: mla_decode_attn, events on its own stream
+    # ---- the dominant kernel alone: mla_decode_attn back to back, one pair of
+    # events on its launch stream around all of them (an event pair per launch
+    # would add its markers' gaps to every launch)
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     run.absorb(q_nope, q_pe, w_uk)
+    torch.cuda.synchronize()
+    ev0.record(stream)
     for i in range(args.steps):
         next_pool()
-        starts[i].record(stream)
         run.attend(block_table, seq_lens)
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    attn_ms = ev0.elapsed_time(ev1) / args.steps
     # combine alone (for t_attn = decode_attn + combine)
     ev0.record()
     for _ in range(args.steps):
