@@ -378,3 +378,23 @@ def test_int8_chan_page_layout_and_roundtrip():
     g = quant.page_fields_int8_chan(pg, 37)
     for k in ("codes", "blk_scale", "r_codes", "r_scale", "open"):
         assert np.array_equal(g[k], f[k]), k
+
+
+@pytest.mark.parametrize("n", [5, 32, 64])
+def test_int8_chan_page_roundtrip_open_first_half_or_none(n):
+    """An open block in the page's first half (n = 5: rows in code rows 0..4 and
+    overflow rows 0..4, no scales yet), one closed block and nothing open
+    (n = 32), both blocks closed (n = 64): the page reads back to the same fields."""
+    rng = np.random.default_rng(14 + n)
+    c = _draw(rng, (n, 512))
+    r = _draw(rng, (n, 64))
+    f = quant.encode_tokens(quant.CACHE_INT8_CHAN, c, r)
+    pg = quant.pack_page(quant.CACHE_INT8_CHAN, f)
+    nc = (n // 32) * 32
+    for rr in range(n - nc):
+        assert np.array_equal(pg[(nc + rr) * 512:(nc + rr + 1) * 512].view(np.uint16), c[nc + rr, :256])
+        assert np.array_equal(pg[43008 + rr * 512:43008 + (rr + 1) * 512].view(np.uint16), c[nc + rr, 256:])
+    assert not pg[36864 + 2048 * (nc // 32):36864 + 4096].any()      # no scales for blocks not closed
+    g = quant.page_fields_int8_chan(pg, n)
+    for k in ("codes", "blk_scale", "r_codes", "r_scale", "open"):
+        assert np.array_equal(g[k], f[k]), k
