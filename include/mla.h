@@ -329,6 +329,28 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
 /* n_tokens * (576 + H * 192) * 4 bytes: the fp32 projection results.        */
 size_t mla_layer_front_workspace_bytes(const mla_config* cfg, int32_t n_tokens);
 
+/* ------------------------------------------------------------------ layer front into the cache
+ * mla_layer_front_append: mla_layer_front followed by
+ * mla_cache_append(cfg, pool, num_pages, c_kv, k_pe, slot_mapping, n_tokens)
+ * (same arguments, definitions and results, bit for bit: the cache rows are
+ * written by the same row functions), with the append done by the launch that
+ * normalises and rotates each token, so that the rows go into the cache without
+ * a second pass over c_kv and k_pe: the fill path [Tutorial] §三 describes
+ * (the latent normalised and the key rotated before they are cached).  c_kv and
+ * k_pe are still written (mla_prefill_attn takes them).  The per-channel INT8
+ * format is appended after the front by mla_cache_append's own two launches
+ * (a block this call completes must be closed before the call's rows of the
+ * next block take the page's overflow rows).
+ *   pool, num_pages, slot_mapping  as for mla_cache_append (slots outside the
+ *                                  pool are skipped)
+ *   everything else                as for mla_layer_front
+ * n_tokens == 0 is a no-op; n_tokens < 0 or num_pages < 0 is MLA_ERR_VALUE.   */
+mla_status mla_layer_front_append(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
+                                  const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                  float* workspace, size_t workspace_bytes, uint16_t* q_nope, uint16_t* q_pe,
+                                  uint16_t* c_kv, uint16_t* k_pe, void* pool, int64_t num_pages,
+                                  const int64_t* slot_mapping, int32_t n_tokens, hipStream_t stream);
+
 /* ------------------------------------------------------------------ layer front, no allocation
  * mla_layer_front_noalloc: mla_layer_front (same arguments, definitions and
  * results, bit for bit) for callers that cannot allocate device memory --

@@ -47,6 +47,8 @@ SIGNATURES = {
                                               C.c_int32, _P]),
     "mla_layer_front": (C.c_int, [_CFG, _P, C.c_int32, _P, _P, _P, C.c_float, C.c_float, _P, C.c_size_t,
                                   _P, _P, _P, _P, C.c_int32, _P]),
+    "mla_layer_front_append": (C.c_int, [_CFG, _P, C.c_int32, _P, _P, _P, C.c_float, C.c_float, _P, C.c_size_t,
+                                         _P, _P, _P, _P, _P, C.c_int64, _P, C.c_int32, _P]),
     "mla_layer_front_workspace_bytes": (C.c_size_t, [_CFG, C.c_int32]),
     "mla_layer_front_noalloc": (C.c_int, [_CFG, _P, C.c_int32, _P, _P, _P, C.c_float, C.c_float,
                                           _P, _P, _P, _P, C.c_int32, _P]),

@@ -245,6 +245,34 @@ def layer_front(cfg: Config, x, w_q, w_dkv, positions, workspace, q_nope, q_pe, 
            "mla_layer_front")
 
 
+def layer_front_append(cfg: Config, x, w_q, w_dkv, positions, workspace, q_nope, q_pe, c_kv, k_pe, pool,
+                       slot_mapping, rms_eps: float = 1e-6, rope_base: float = 10000.0) -> None:
+    """layer_front, and each token's row written into its pool slot in the config's
+    cache format by the same launch (mla_layer_front_append)."""
+    T, hidden, H = int(x.shape[0]), int(x.shape[1]), cfg.num_heads
+    _need(x, "x", (T, hidden), 2)
+    _need(w_q, "w_q", (H * 192, hidden), 2)
+    _need(w_dkv, "w_dkv", (576, hidden), 2)
+    _need(positions, "positions", (T,), 4)
+    _need(q_nope, "q_nope", (T, H, 128), 2)
+    _need(q_pe, "q_pe", (T, H, 64), 2)
+    _need(c_kv, "c_kv", (T, 512), 2)
+    _need(k_pe, "k_pe", (T, 64), 2)
+    _need(slot_mapping, "slot_mapping", (T,), 8)
+    page = cache_page_bytes(cfg)
+    nbytes = pool.numel() * pool.element_size()
+    if nbytes % page:
+        raise ValueError("pool size %d is not a whole number of %d-byte pages" % (nbytes, page))
+    ws_bytes = int(workspace.numel()) * int(workspace.element_size())
+    _check(L.load().mla_layer_front_append(C.byref(cfg), _dev(x, "x"), hidden, _dev(w_q, "w_q"), _dev(w_dkv, "w_dkv"),
+                                           _dev(positions, "positions"), float(rms_eps), float(rope_base),
+                                           _dev(workspace, "workspace"), ws_bytes, _dev(q_nope, "q_nope"),
+                                           _dev(q_pe, "q_pe"), _dev(c_kv, "c_kv"), _dev(k_pe, "k_pe"),
+                                           _dev(pool, "pool"), nbytes // page, _dev(slot_mapping, "slot_mapping"), T,
+                                           _stream()),
+           "mla_layer_front_append")
+
+
 def layer_front_noalloc(cfg: Config, x, w_q, w_dkv, positions, q_nope, q_pe, c_kv, k_pe,
                         rms_eps: float = 1e-6, rope_base: float = 10000.0) -> None:
     """layer_front with the projections in the library's own scratch (mla_layer_front_noalloc)."""

@@ -250,6 +250,31 @@ mla_status mla_layer_front(const mla_config* cfg, const uint16_t* x, int32_t hid
                                           workspace, q_nope, q_pe, c_kv, k_pe, n_tokens, stream));
 }
 
+mla_status mla_layer_front_append(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
+                                  const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                  float* workspace, size_t workspace_bytes, uint16_t* q_nope, uint16_t* q_pe,
+                                  uint16_t* c_kv, uint16_t* k_pe, void* pool, int64_t num_pages,
+                                  const int64_t* slot_mapping, int32_t n_tokens, hipStream_t stream) {
+  mla_status s = mla_config_check(cfg);
+  if (s != MLA_OK) return s;
+  if (n_tokens < 0 || num_pages < 0 || hidden <= 0 || hidden % 8 != 0) return MLA_ERR_VALUE;
+  if (!(rms_eps > 0.f) || !std::isfinite(rms_eps) || !(rope_base > 1.f) || !std::isfinite(rope_base))
+    return MLA_ERR_VALUE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!x || !w_q || !w_dkv || !positions || !workspace || !q_nope || !q_pe || !c_kv || !k_pe || !pool ||
+      !slot_mapping)
+    return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_dkv) || !aligned16(positions) || !aligned16(workspace) ||
+      !aligned16(q_nope) || !aligned16(q_pe) || !aligned16(c_kv) || !aligned16(k_pe) || !aligned16(pool) ||
+      !aligned16(slot_mapping))
+    return MLA_ERR_ALIGN;
+  if (workspace_bytes < mla_layer_front_workspace_bytes(cfg, n_tokens)) return MLA_ERR_WORKSPACE;
+  if ((s = check_device()) != MLA_OK) return s;
+  return launched(mla::launch_layer_front_append(cfg->num_heads, x, hidden, w_q, w_dkv, positions, rms_eps, rope_base,
+                                                 workspace, q_nope, q_pe, c_kv, k_pe, cfg->cache_dtype, pool,
+                                                 num_pages, slot_mapping, n_tokens, stream));
+}
+
 mla_status mla_layer_front_noalloc(const mla_config* cfg, const uint16_t* x, int32_t hidden, const uint16_t* w_q,
                                    const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
                                    uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe,

@@ -23,6 +23,7 @@
 #include <atomic>
 #include <mutex>
 
+#include "append_row.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -175,13 +176,20 @@ __device__ __forceinline__ uint16_t bf16_of(double v) { return f32_to_bf16_rne((
 
 // One work-group (256 threads) per token t: the 32 rotation angles of its
 // position are evaluated once (double precision) into LDS and shared by the
-// RoPE key and the H query heads; wave 0 normalises the latent.
+// RoPE key and the H query heads; wave 0 normalises the latent.  With a pool
+// (formats 0-6), the group then writes the token's row into its cache slot in
+// the cache's format (the append kernels' own row functions, from an LDS copy of
+// the row); slots outside the pool are skipped, as by mla_cache_append.
 __global__ __launch_bounds__(256) void front_finish_kernel(const float* __restrict__ kv, const float* __restrict__ q,
                                                            const int32_t* __restrict__ pos, int H, float eps,
                                                            float base, uint16_t* __restrict__ q_nope,
                                                            uint16_t* __restrict__ q_pe, uint16_t* __restrict__ c_kv,
-                                                           uint16_t* __restrict__ k_pe) {
+                                                           uint16_t* __restrict__ k_pe, int cache_dtype,
+                                                           uint8_t* __restrict__ pool, int64_t num_pages,
+                                                           const int64_t* __restrict__ slots, int n_tokens) {
   __shared__ double cs[32][2];
+  __shared__ __attribute__((aligned(16))) uint16_t crow[kDc];
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kDr];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < 32) {
     // pair i of a 64-wide rotary vector turns by pos * base^(-2i/64)
@@ -201,7 +209,11 @@ __global__ __launch_bounds__(256) void front_finish_kernel(const float* __restri
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const double inv = 1.0 / sqrt(ss / kDc + (double)eps);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c_kv[(int64_t)t * kDc + 8 * tid + i] = bf16_of(v[i] * inv);
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t b = bf16_of(v[i] * inv);
+      c_kv[(int64_t)t * kDc + 8 * tid + i] = b;
+      crow[8 * tid + i] = b;
+    }
   }
   const float* q_tok = q + (int64_t)t * H * (kDn + kDr);
   for (int idx = tid; idx < H * kDn; idx += 256) {
@@ -216,9 +228,19 @@ __global__ __launch_bounds__(256) void front_finish_kernel(const float* __restri
     uint16_t* dst = h < H ? q_pe + ((int64_t)t * H + h) * kDr : k_pe + (int64_t)t * kDr;
     const double c = cs[i][0], sn = cs[i][1];
     const double xe = src[2 * i], xo = src[2 * i + 1];
-    dst[2 * i] = bf16_of(xe * c - xo * sn);
-    dst[2 * i + 1] = bf16_of(xe * sn + xo * c);
+    const uint16_t re = bf16_of(xe * c - xo * sn), ro = bf16_of(xe * sn + xo * c);
+    dst[2 * i] = re;
+    dst[2 * i + 1] = ro;
+    if (h == H) {
+      krow[2 * i] = re;
+      krow[2 * i + 1] = ro;
+    }
   }
+  if (pool == nullptr) return;             // uniform: no append requested
+  __syncthreads();                         // the row is complete in LDS
+  const int64_t slot = slots[t];
+  if (!slot_ok(slot, num_pages)) return;   // uniform per group
+  append_row_wg(cache_dtype, pool, slot, crow, krow, tid);
 }
 
 // x_out[t][n] = bf16(x_in[t][n] + y[t][n]) (fp32 sum, round to nearest even);
@@ -254,8 +276,32 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
   project(x, w_dkv, hidden, n_kv, n_tokens, kv, stream);
   project(x, w_q, hidden, n_q, n_tokens, q, stream);
   hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens), dim3(256), 0, stream, kv, q, positions,
-                     num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe);
+                     num_heads, rms_eps, rope_base, q_nope, q_pe, c_kv, k_pe, 0, nullptr, (int64_t)0, nullptr, 0);
   return hipGetLastError();
+}
+
+hipError_t launch_layer_front_append(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q,
+                                     const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                     float* workspace, uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv,
+                                     uint16_t* k_pe, int cache_dtype, void* pool, int64_t num_pages,
+                                     const int64_t* slots, int n_tokens, hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  const int n_kv = kDc + kDr, n_q = num_heads * (kDn + kDr);
+  float* kv = workspace;
+  float* q = workspace + (int64_t)n_tokens * n_kv;
+  project(x, w_dkv, hidden, n_kv, n_tokens, kv, stream);
+  project(x, w_q, hidden, n_q, n_tokens, q, stream);
+  // The per-channel INT8 format appends after the front, as mla_cache_append
+  // does: a call that closes a block and opens the next one on the same page
+  // must close first, since the new open rows take the overflow rows that the
+  // closing block's earlier rows still occupy.
+  const bool fuse = cache_dtype != 7;
+  hipLaunchKernelGGL(front_finish_kernel, dim3(n_tokens), dim3(256), 0, stream, kv, q, positions, num_heads, rms_eps,
+                     rope_base, q_nope, q_pe, c_kv, k_pe, cache_dtype, fuse ? static_cast<uint8_t*>(pool) : nullptr,
+                     num_pages, slots, n_tokens);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && !fuse) e = launch_append(cache_dtype, pool, num_pages, c_kv, k_pe, slots, n_tokens, stream);
+  return e;
 }
 
 // Device address of `scratch` on the current device, looked up once per device

@@ -37,6 +37,15 @@ hipError_t launch_layer_front(int num_heads, const uint16_t* x, int hidden, cons
                               uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv, uint16_t* k_pe, int n_tokens,
                               hipStream_t stream);
 
+// launch_layer_front, and each token's row written into its cache slot in the
+// format cache_dtype by the same launch (the per-channel INT8 format runs its
+// usual two append launches after the front instead).
+hipError_t launch_layer_front_append(int num_heads, const uint16_t* x, int hidden, const uint16_t* w_q,
+                                     const uint16_t* w_dkv, const int32_t* positions, float rms_eps, float rope_base,
+                                     float* workspace, uint16_t* q_nope, uint16_t* q_pe, uint16_t* c_kv,
+                                     uint16_t* k_pe, int cache_dtype, void* pool, int64_t num_pages,
+                                     const int64_t* slots, int n_tokens, hipStream_t stream);
+
 // launch_layer_front with the fp32 projections in the library's per-device
 // scratch (kFrontScratchBytes) instead of a caller workspace; allocates nothing.
 constexpr size_t kFrontScratchBytes = size_t(16) << 20;

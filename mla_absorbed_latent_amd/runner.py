@@ -115,11 +115,18 @@ class PrefillLayer:
         self.attn = torch.empty(T, H, 128, dtype=torch.bfloat16, device=dev)
         self.positions = torch.arange(T, dtype=torch.int32, device=dev)
 
-    def forward(self, x, w_q, w_dkv, w_uk, w_uv, w_o, x_out, rms_eps=1e-6, rope_base=10000.0):
+    def forward(self, x, w_q, w_dkv, w_uk, w_uv, w_o, x_out, rms_eps=1e-6, rope_base=10000.0, cache=None,
+                slots=None):
         """x_out = x + W_O . attention(front(x)); x_out may be x.  c_kv / k_pe
-        keep the layer's latent rows (what a decode step would append)."""
-        api.layer_front(self.cfg, x, w_q, w_dkv, self.positions, self.front_ws, self.q_nope, self.q_pe,
-                        self.c_kv, self.k_pe, rms_eps, rope_base)
+        keep the layer's latent rows.  With `cache` (a DecodeRunner of this layer)
+        and `slots` (int64 [T]) the rows also go into the cache, in its format, from
+        the front's own launch (mla_layer_front_append)."""
+        if cache is None:
+            api.layer_front(self.cfg, x, w_q, w_dkv, self.positions, self.front_ws, self.q_nope, self.q_pe,
+                            self.c_kv, self.k_pe, rms_eps, rope_base)
+        else:
+            api.layer_front_append(cache.cfg, x, w_q, w_dkv, self.positions, self.front_ws, self.q_nope, self.q_pe,
+                                   self.c_kv, self.k_pe, cache.pool, slots, rms_eps, rope_base)
         api.prefill_attn(self.cfg, self.q_nope, self.q_pe, self.c_kv, self.k_pe, w_uk, w_uv, self.attn_ws, self.attn)
         api.out_residual(self.cfg, self.attn, w_o, x, x_out, self.res_ws)
         return x_out

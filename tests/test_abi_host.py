@@ -245,6 +245,33 @@ def test_append_absorb_validation(lib):
     assert call(pool=None, n=0, q=None, b=0) == L.MLA_OK
 
 
+def test_layer_front_append_validation(lib):
+    """Host-side checks of the front with the cache append fused in: the front's
+    and the append's argument checks, before any HIP call."""
+    cfg = api.config(16, 1)
+    fake, odd = C.c_void_p(0x1000), C.c_void_p(0x1001)
+    ws = api.layer_front_workspace_bytes(cfg, 4)
+    f = lib.mla_layer_front_append
+
+    def call(x=fake, hidden=2048, eps=1e-6, base=1e4, wsb=ws, n=4, pool=fake, pages=8, slots=fake):
+        return f(C.byref(cfg), x, hidden, fake, fake, fake, eps, base, fake, wsb, fake, fake, fake, fake, pool, pages,
+                 slots, n, None)
+
+    assert call(hidden=2044) == L.MLA_ERR_VALUE
+    assert call(n=-1) == L.MLA_ERR_VALUE
+    assert call(pages=-1) == L.MLA_ERR_VALUE
+    assert call(eps=0.0) == L.MLA_ERR_VALUE
+    assert call(pool=None) == L.MLA_ERR_NULL
+    assert call(slots=None) == L.MLA_ERR_NULL
+    assert call(pool=odd) == L.MLA_ERR_ALIGN
+    assert call(slots=odd) == L.MLA_ERR_ALIGN
+    assert call(wsb=ws - 4) == L.MLA_ERR_WORKSPACE
+    assert call(pool=None, slots=None, x=None, n=0) == L.MLA_OK        # no-op
+    bad = api.config(16, 8)
+    assert f(C.byref(bad), fake, 2048, fake, fake, fake, 1e-6, 1e4, fake, ws, fake, fake, fake, fake, fake, 8, fake, 4,
+             None) == L.MLA_ERR_VALUE
+
+
 def test_layer_front_noalloc_validation(lib):
     """Host-side checks of the allocation-free front: the token count is bounded by
     the library's 16 MiB scratch (MLA_ERR_WORKSPACE beyond it), before any HIP call."""

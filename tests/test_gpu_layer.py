@@ -86,3 +86,47 @@ def test_v2lite_layer_end_to_end(fused):
         assert mx <= MAX_REL and mean <= MEAN_REL, (key, mx, mean)
     mx, mean = errors(of.cpu().numpy()[0], ref["out_absorbed"])
     assert mx <= MAX_REL and mean <= MEAN_REL, (mx, mean)
+
+
+@pytest.mark.parametrize("cache_dtype", [0, 1, 2, 3, 4, 5, 6, 7])
+def test_layer_front_append_matches_front_then_append(cache_dtype):
+    """mla_layer_front_append against mla_layer_front followed by
+    mla_cache_append: every output and every pool byte equal, over two calls
+    (positions 0..44, then 45..99: the second call finishes blocks the first one
+    opened and takes the matrix-core projection), pages shuffled, one slot
+    outside the pool (skipped by both)."""
+    H, T = 16, 100
+    case = mla_synth.v2lite_layer(T=T, H=H, hidden=2048, case_id=32)
+    cfg = api.config(H, cache_dtype, case.softmax_scale)
+    page = api.cache_page_bytes(cfg)
+    perm = [2, 0, 3, 1]
+    slots_all = np.array([perm[p // 64] * 64 + p % 64 for p in range(T)], np.int64)
+    slots_all[7] = 4 * 64 + 3                        # past the 4-page pool
+    pools = [torch.zeros(4 * page, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    x_all = to_dev_bits(case.x)
+    w_q, w_dkv = to_dev_bits(case.w_q), to_dev_bits(case.w_dkv)
+    print("front+append dtype=%d" % cache_dtype, flush=True)
+    for t0, t1 in ((0, 45), (45, T)):
+        n = t1 - t0
+        x = x_all[t0:t1].contiguous()
+        pos = torch.arange(t0, t1, dtype=torch.int32, device=DEV)
+        slots = torch.from_numpy(slots_all[t0:t1].copy()).to(DEV)
+        ws = torch.empty(api.layer_front_workspace_bytes(cfg, n) // 4, dtype=torch.float32, device=DEV)
+        outs = []
+        for k in range(2):
+            o = (torch.empty(n, H, 128, dtype=torch.bfloat16, device=DEV),
+                 torch.empty(n, H, 64, dtype=torch.bfloat16, device=DEV),
+                 torch.empty(n, 512, dtype=torch.bfloat16, device=DEV),
+                 torch.empty(n, 64, dtype=torch.bfloat16, device=DEV))
+            if k == 0:
+                api.layer_front(cfg, x, w_q, w_dkv, pos, ws, *o, rms_eps=case.rms_eps, rope_base=case.rope_base)
+                api.cache_append(cfg, pools[0], o[2], o[3], slots)
+            else:
+                api.layer_front_append(cfg, x, w_q, w_dkv, pos, ws, *o, pools[1], slots, rms_eps=case.rms_eps,
+                                       rope_base=case.rope_base)
+            outs.append(o)
+        torch.cuda.synchronize()
+        for a, b in zip(*outs):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(pools[0], pools[1]), (t0, int((pools[0] != pools[1]).sum()))
+    assert bool(pools[1].any())

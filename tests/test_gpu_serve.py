@@ -1,9 +1,9 @@
 """A prompt followed by one decode step through a stack of three V2-Lite layers,
 wholly on the GPU, against the stack oracle.
 
-Per layer: the prompt (T = 48 tokens) runs the prompt path (mla_layer_front ->
-mla_prefill_attn -> mla_out_residual) and its latent rows are appended to the
-layer's paged cache; the next token then runs the decode path at position T
+Per layer: the prompt (T = 48 tokens) runs the prompt path
+(mla_layer_front_append, which also writes its latent rows into the layer's
+paged cache -> mla_prefill_attn -> mla_out_residual); the next token then runs the decode path at position T
 (mla_layer_front for one token -> mla_cache_append -> mla_absorb_q ->
 mla_decode_attn -> merge + W_UV -> mla_out_residual).  Attention is causal, so
 the oracle stack over T + 1 tokens gives both: rows 0..T-1 for the prompt and
@@ -58,9 +58,9 @@ def test_prompt_then_decode_through_three_layers(cache_dtype):
     for l, case in enumerate(layers):
         w = [to_dev_bits(a) for a in (case.w_q, case.w_dkv, case.w_uk, case.w_uv, case.w_o)]
         run = DecodeRunner(cfg, 1, pages, DEV)
-        # prompt: prefill path; its latent rows go to this layer's cache
-        prompt.forward(x_p, *w, x_p)
-        run.append(prompt.c_kv, prompt.k_pe, torch.arange(T, dtype=torch.int64, device=DEV))
+        # prompt: prefill path; its latent rows go to this layer's cache from the
+        # front's own launch (mla_layer_front_append)
+        prompt.forward(x_p, *w, x_p, cache=run, slots=torch.arange(T, dtype=torch.int64, device=DEV))
         # decode: one token at position T through the absorbed path
         api.layer_front(cfg, x_d, w[0], w[1], pos, fws, qn, qp, c1, r1)
         run.plan([T + 1])
