@@ -38,13 +38,15 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 
 // Grid (ceil(Lp / 128), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
 // work-group computes 128 positions x the 128 output features of head h as a
-// tiled GEMM over the 512 latent channels: chunks of 64 channels of the latent
-// rows and of the weight rows go straight into LDS (double-buffered, 16-byte
-// chunk c of row r at c ^ (r & 7)), and wave (wm, wn) computes 64 positions x 64
-// features from them (4 x 4 tiles of 16 x 16).  Both operands are rows of 64
-// channels with the same fragment layout, so the weight is the A operand for
-// K_nope (D[feature][position]: four consecutive features per lane and store)
-// and the B operand for V^T (D[position][feature]: four consecutive positions).
+// tiled GEMM over the 512 latent channels, in 16 stages of 32 channels: a
+// stage's latent rows and weight rows (64 B each) go straight into LDS, four
+// stage buffers deep, so that three stages are in flight while one is used
+// (16-byte chunk c of row r at c ^ ((r >> 2) & 3): the 16 rows a fragment read
+// touches then fill the 64 banks once).  Wave (wm, wn) computes 64 positions x
+// 64 features (4 x 4 tiles of 16 x 16).  Both operands are rows of channels
+// with the same fragment layout, so the weight is the A operand for K_nope
+// (D[feature][position]: four consecutive features per lane and store) and the
+// B operand for V^T (D[position][feature]: four consecutive positions).
 // V^T keeps each 32-key block's positions in the order 0-3, 16-19, 4-7, 20-23,
 // 8-11, 24-27, 12-15, 28-31: the eight keys that lane group g of the value
 // product takes in a k-step (32 ks + 4 g .. +3 and 32 ks + 16 + 4 g .. +3) are
@@ -56,42 +58,52 @@ __device__ __forceinline__ int vt_pos(int j) {
 }
 
 constexpr int kXT = 128;                  // positions per work-group
-constexpr int kXChunk = 64;               // channels per LDS chunk
-constexpr int kXRow = kXChunk * 2;        // 128 B
-constexpr int kXBuf = 2 * kXT * kXRow;    // latent + weight tiles, 32 KB
+constexpr int kXChunk = 32;               // channels per stage
+constexpr int kXRow = kXChunk * 2;        // 64 B
+constexpr int kXBuf = 2 * kXT * kXRow;    // latent + weight rows of a stage, 16 KB
+constexpr int kXStages = 4;               // stage buffers
+constexpr int kXLoads = kXBuf / 1024 / 4; // 1 KB direct loads per wave per stage
 
-__global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
-                                                        const uint16_t* __restrict__ w_uk,
-                                                        const uint16_t* __restrict__ w_uv, int L, int Lp,
-                                                        uint16_t* __restrict__ k_nope, uint16_t* __restrict__ v_t) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kXBuf];
+// s_waitcnt with only vmcnt constrained (gfx9 encoding).
+template <int kN>
+__device__ __forceinline__ void x_wait_vm() {
+  __builtin_amdgcn_s_waitcnt((kN & 15) | (7 << 4) | (15 << 8) | ((kN >> 4) << 14));
+}
+
+template <bool is_v>
+__device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ w_in,
+                                               int L, int Lp, uint16_t* __restrict__ k_nope,
+                                               uint16_t* __restrict__ v_t, char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;          // positions 64 wm.., features 64 wn..
-  const int h = blockIdx.y, is_v = blockIdx.z;
+  const int h = blockIdx.y;
   const int j0 = blockIdx.x * kXT;
-  const uint16_t* w = (is_v ? w_uv : w_uk) + (int64_t)h * kDn * kDc;
+  const uint16_t* w = w_in + (int64_t)h * kDn * kDc;
 
-  // staging: rows 0..127 latent, 128..255 weight, 8 chunks of 16 B per row,
+  // Staging: rows 0..127 latent, 128..255 weight, 4 chunks of 16 B per row,
   // straight into LDS (global_load_lds_dwordx4: lane i of a wave instruction
-  // fills bytes 16 i .. of a 1 KB segment): 32 segments, wave w issues w + 4 i.
-  // Each lane loads the chunk that belongs at its slot (chunk ch ^ (row & 7)).
-  // Positions past L load position L - 1: finite values, masked in attention.
-  auto issue = [&](int kc, int buf) {
-    char* base = lds + buf * kXBuf;
+  // fills bytes 16 i .. of a 1 KB segment): 16 segments, wave w issues w + 4 i.
+  // Each lane loads the chunk that belongs at its slot.  Positions past L load
+  // position L - 1: finite values, masked in attention.
+  const uint16_t* src0[kXLoads];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 3, ch = (P & 7) ^ (row & 7);
-      const int k = kc * kXChunk + 8 * ch;
-      const uint16_t* src;
-      if (row < kXT) {
-        const int j = j0 + row;
-        src = c_kv + (int64_t)(j < L ? j : L - 1) * kDc + k;
-      } else {
-        src = w + (int64_t)(row - kXT) * kDc + k;
-      }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(base + 1024 * seg), 16, 0, 0);
+  for (int i = 0; i < kXLoads; ++i) {
+    const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 2, ch = (P & 3) ^ ((row >> 2) & 3);
+    if (row < kXT) {
+      const int j = j0 + row;
+      src0[i] = c_kv + (int64_t)(j < L ? j : L - 1) * kDc + 8 * ch;
+    } else {
+      src0[i] = w + (int64_t)(row - kXT) * kDc + 8 * ch;
     }
+  }
+  auto issue = [&](int kc) {
+    char* base = lds + (kc % kXStages) * kXBuf;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i)
+      __builtin_amdgcn_global_load_lds(src0[i] + kc * kXChunk,
+                                       (__attribute__((address_space(3))) void*)(base + 1024 * (wave + 4 * i)), 16,
+                                       0, 0);
   };
 
   floatx4 acc[4][4];
@@ -101,34 +113,41 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kChunks = kDc / kXChunk;
-  issue(0, 0);
+  static_assert(kChunks >= kXStages, "the prologue fills kXStages - 1 stages");
+#pragma unroll
+  for (int kc = 0; kc < kXStages - 1; ++kc) issue(kc);
+  // Stages fully unrolled, so that every wait count and buffer is a constant.
+  // The barrier is a bare s_barrier after this wave's own waits: the workgroup
+  // fence of __syncthreads would wait for every load in flight, the later
+  // stages' included.
+#pragma unroll
   for (int kc = 0; kc < kChunks; ++kc) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                       // chunk kc in LDS; chunk kc - 1 read by every wave
-    if (kc + 1 < kChunks) issue(kc + 1, (kc + 1) & 1);
-    const char* buf = lds + (kc & 1) * kXBuf;
+    // stage kc's loads retire; the (up to two) later stages stay in flight
+    if (kc + 2 < kChunks) x_wait_vm<2 * kXLoads>();
+    else if (kc + 1 < kChunks) x_wait_vm<kXLoads>();
+    else x_wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage kc in LDS; stage kc - 1 read
+    if (kc + kXStages - 1 < kChunks) issue(kc + kXStages - 1);
+    const char* buf = lds + (kc % kXStages) * kXBuf;
+    u32x4 pf[4], wf[4];
 #pragma unroll
-    for (int ks = 0; ks < kXChunk / 32; ++ks) {
-      u32x4 pf[4], wf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pr = 64 * wm + 16 * t + li, wr = kXT + 64 * wn + 16 * t + li;
-        pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * ((4 * ks + g) ^ (pr & 7)));
-        wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * ((4 * ks + g) ^ (wr & 7)));
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          // a: position tile, b: feature tile
-          if (!is_v)
-            acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[b]), __builtin_bit_cast(bf16x8, pf[a]),
-                                          acc[a][b]);
-          else
-            acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf[a]), __builtin_bit_cast(bf16x8, wf[b]),
-                                          acc[a][b]);
-        }
+    for (int t = 0; t < 4; ++t) {
+      const int pr = 64 * wm + 16 * t + li, wr = kXT + 64 * wn + 16 * t + li;
+      pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * (g ^ ((pr >> 2) & 3)));
+      wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * (g ^ ((wr >> 2) & 3)));
     }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // a: position tile, b: feature tile
+        if constexpr (!is_v)
+          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[b]), __builtin_bit_cast(bf16x8, pf[a]),
+                                        acc[a][b]);
+        else
+          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf[a]), __builtin_bit_cast(bf16x8, wf[b]),
+                                        acc[a][b]);
+      }
   }
 
 #pragma unroll
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const u32x2 o = {pack_f16(acc[a][b][0], acc[a][b][1]), pack_f16(acc[a][b][2], acc[a][b][3])};
-      if (!is_v) {
+      if constexpr (!is_v) {
         // D[feature 64 wn + 16 b + 4 g + r][position 64 wm + 16 a + li]
         const int j = j0 + 64 * wm + 16 * a + li;
         if (j < Lp) *reinterpret_cast<u32x2*>(k_nope + ((int64_t)h * Lp + j) * kDn + 64 * wn + 16 * b + 4 * g) = o;
@@ -148,6 +167,15 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restri
           *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 64 * wn + 16 * b + li) * Lp + vt_pos(j)) = o;
       }
     }
+}
+
+__global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
+                                                        const uint16_t* __restrict__ w_uk,
+                                                        const uint16_t* __restrict__ w_uv, int L, int Lp,
+                                                        uint16_t* __restrict__ k_nope, uint16_t* __restrict__ v_t) {
+  __shared__ __attribute__((aligned(16))) char lds[kXStages * kXBuf];
+  if (blockIdx.z == 0) expand_kv_body<false>(c_kv, w_uk, L, Lp, k_nope, v_t, lds);
+  else expand_kv_body<true>(c_kv, w_uv, L, Lp, k_nope, v_t, lds);
 }
 
 // Grid (ceil(T / kQB), H), kWaves waves.  Wave w owns queries
