@@ -252,36 +252,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int ks = 0; ks < 2; ++ks) qf[u][4 + ks] = ld16(qp + 32 * ks);
   }
 
-  // This lane's part of a tile: K segments wave, wave + 8, wave + 16 (LDS slot
-  // P = 64 segment + lane = 24 key + (chunk ^ (key & 7))), V^T segments wave,
-  // wave + 8 (P = 8 dim + (chunk ^ (dim & 7))).  Offsets are 32-bit, from
-  // per-head bases (a head's K_nope or V^T spans Lp * 128 < 2^31 elements).
+  // This lane's part of a tile: K segments wave + 4 n (LDS slot P = 64 segment
+  // + lane = 24 key + (chunk ^ (key & 7))), V^T segments wave + 4 n (P = 8 dim +
+  // (chunk ^ (dim & 7))).  Each load's source for block 0 is formed here and
+  // advanced by a fixed stride per block; pad keys (j >= L: only their k_pe
+  // part, K_nope is padded) read row L - 1 instead.
   const uint16_t* k_nope_h = k_nope + (int64_t)h * Lp * kDn;
   const uint16_t* v_t_h = v_t + (int64_t)h * kDn * Lp;
-  int kslot[kKSeg], voff[kVSeg];
+  const char* ksrc[kKSeg];
+  int kstride[kKSeg], kkey[kKSeg];
+  const char* kpe_last[kKSeg];
 #pragma unroll
   for (int n = 0; n < kKSeg; ++n) {
-    const int P = 64 * (wave + kWaves * n) + lane, key = P / 24;
-    kslot[n] = key | (((P % 24) ^ (key & 7)) << 8);         // key | chunk << 8
+    const int P = 64 * (wave + kWaves * n) + lane, key = P / 24, ch = (P % 24) ^ (key & 7);
+    kkey[n] = ch < 16 ? -1 : key;             // k_pe chunks check for pad keys
+    ksrc[n] = ch < 16 ? reinterpret_cast<const char*>(k_nope_h + key * kDn + 8 * ch)
+                      : reinterpret_cast<const char*>(k_pe + key * kDr + 8 * (ch - 16));
+    kstride[n] = ch < 16 ? 64 * kDn * 2 : 64 * kDr * 2;
+    kpe_last[n] = reinterpret_cast<const char*>(k_pe + (int64_t)(L - 1) * kDr + 8 * (ch < 16 ? 0 : ch - 16));
   }
+  const char* vsrc[kVSeg];
 #pragma unroll
   for (int n = 0; n < kVSeg; ++n) {
     const int P = 64 * (wave + kWaves * n) + lane, d = P >> 3, ch = (P & 7) ^ (d & 7);
-    voff[n] = d * Lp + 8 * ch;
+    vsrc[n] = reinterpret_cast<const char*>(v_t_h + d * Lp + 8 * ch);
   }
-  auto issue = [&](int kb, int buf) {
+  // Load m (0 .. kKSeg + kVSeg - 1) of block kb into buffer buf.
+  auto issue_one = [&](int m, int kb, int buf) {
     char* base = lds + buf * kBufBytes;
-#pragma unroll
-    for (int n = 0; n < kKSeg; ++n) {
-      const int j = kb * 64 + (kslot[n] & 255), ch = kslot[n] >> 8;
-      const uint16_t* src = ch < 16 ? k_nope_h + (j * kDn + 8 * ch)
-                                    : k_pe + ((j < L ? j : L - 1) * kDr + 8 * (ch - 16));   // pad keys: row L-1
+    if (m < kKSeg) {
+      const int n = m;
+      const char* src = ksrc[n] + (int64_t)kb * kstride[n];
+      if (kkey[n] >= 0 && kb * 64 + kkey[n] >= L) src = kpe_last[n];
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * (wave + kWaves * n)), 16, 0, 0);
+    } else {
+      const int n = m - kKSeg;
+      __builtin_amdgcn_global_load_lds(vsrc[n] + kb * 128, (lds_void*)(base + kKBytes + 1024 * (wave + kWaves * n)),
+                                       16, 0, 0);
     }
+  };
+  auto issue = [&](int kb, int buf) {
 #pragma unroll
-    for (int n = 0; n < kVSeg; ++n)
-      __builtin_amdgcn_global_load_lds(v_t_h + (voff[n] + kb * 64),
-                                       (lds_void*)(base + kKBytes + 1024 * (wave + kWaves * n)), 16, 0, 0);
+    for (int m = 0; m < kKSeg + kVSeg; ++m) issue_one(m, kb, buf);
   };
 
   floatx4 o[kU][8];
@@ -298,29 +310,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int kb = 0; kb < n_blocks; ++kb) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                                   // tile kb in LDS; block kb - 1 done by every wave
-    if (kb + 1 < n_blocks) issue(kb + 1, (kb + 1) & 1);
+    // The last block re-loads itself into the idle buffer (never read) rather
+    // than branching around the loads.
+    const int kb_next = kb + 1 < n_blocks ? kb + 1 : kb;
     const char* kt_lds = lds + (kb & 1) * kBufBytes;
     const char* vt_lds = kt_lds + kKBytes;
 
+    // Score products; the next block's loads are spread between them (one
+    // after every other K fragment), so that the CU's load queue drains while
+    // the matrix cores work instead of stalling every wave at the block start.
+    // K fragment idx = 6 kt + ks (key tile kt, k-step ks) is read one step
+    // ahead of its products.
+    auto kfrag = [&](int idx) {
+      const int kt = idx / 6, ks = idx % 6, key = 16 * kt + li;
+      return *reinterpret_cast<const u32x4*>(kt_lds + key * 384 + 16 * ((4 * ks + g) ^ (key & 7)));
+    };
     floatx4 s[kU][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int u = 0; u < kU; ++u) s[u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int key = 16 * kt + li;
-      const char* krow = kt_lds + key * 384;
+    u32x4 a_cur = kfrag(0);
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * ks + g) ^ (key & 7)));
+    for (int idx = 0; idx < 24; ++idx) {
+      const int kt = idx / 6, ks = idx % 6;
+      const u32x4 a = a_cur;
+      if (idx + 1 < 24) a_cur = kfrag(idx + 1);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if (ks < 4)
-            s[u][kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[u][ks]), s[u][kt]);
-          else
-            s[u][kt] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u][ks]),
-                                         s[u][kt]);
-        }
+      for (int u = 0; u < kU; ++u) {
+        if (ks < 4)
+          s[u][kt] = mfma16x16x32(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, qf[u][ks]), s[u][kt]);
+        else
+          s[u][kt] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u][ks]),
+                                       s[u][kt]);
       }
+      constexpr int kLoads = kKSeg + kVSeg;
+      if ((idx & 1) && (idx >> 1) < kLoads) issue_one(idx >> 1, kb_next, (kb + 1) & 1);
     }
     // keys after the query (and pad keys) masked; only blocks that reach past
     // the work-group's first query can hold such keys
@@ -382,6 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
   }
 
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last block's idle re-load has landed
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     float l = l_run[u];
