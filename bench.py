@@ -319,12 +319,31 @@ def measured_peaks(torch, dev):
         t, _ = timed(mm)
         res[name] = flop / t / 1e12
         res[name + "_clock"] = clock_probe_ghz(torch, dev)
+    # per-CU intake from L2: one 512-thread work-group per CU, each on its own
+    # 64 KB slice (16 MB in all: resident in the 8 x 4 MB L2s)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    slices = torch.ones(cus * 16384, dtype=torch.float32, device=dev)
+    sink = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+    cyc = torch.empty(cus, dtype=torch.int64, device=dev)
+    cu_read = {}
+    for name, dma in (("plain", 0), ("lds_dma", 1)):
+        for it in (50, 2000):        # warm-up, then measured
+            err = lib.mla_bench_cu_read(C.c_void_p(slices.data_ptr()), cus, it, dma, C.c_void_p(sink.data_ptr()),
+                                        C.c_void_p(cyc.data_ptr()), stream)
+            if err:
+                raise RuntimeError("mla_bench_cu_read: hipError %d" % err)
+        torch.cuda.synchronize()
+        cu_read[name] = round(2000 * 65536 / float(cyc.double().mean()), 1)
+    del slices, sink, cyc
     return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "hbm_read_gbs_median": round(nbytes / t_read_med / 1e9, 1),
             "mfma_f16_tflops": round(res["f16"], 1), "mfma_bf16_tflops": round(res["bf16"], 1),
+            "l2_read_bytes_per_cu_cycle": cu_read,
             "clock_ghz_after": {"read": read_clock, "mfma_f16": res["f16_clock"], "mfma_bf16": res["bf16_clock"]},
             "how": "mla_bench_stream_read over 4 GiB (16-byte non-temporal loads, 8192 work-groups); "
                    "mla_bench_mfma_loop: 512 work-groups x 4 waves x 8 independent 32x32x16 chains x 4000; "
-                   "best of 5 after one warm-up"}
+                   "best of 5 after one warm-up; mla_bench_cu_read: one 512-thread work-group per CU re-reading "
+                   "its own L2-resident 64 KB slice 2000 times, plain or direct-to-LDS 16-byte loads, "
+                   "shader cycles from s_memtime"}
 
 
 def settle(torch, step, min_s=1.0, max_s=6.0, chunk=20):

@@ -30,6 +30,18 @@ int32_t mla_bench_stream_read(const void* buf, int64_t bytes, uint32_t* out, int
  * per thread to out[0 .. 256 * blocks - 1].                                  */
 int32_t mla_bench_mfma_loop(int32_t bf16, int32_t iters, int32_t blocks, float* out, hipStream_t stream);
 
+/* Per-CU read rate from L2: `blocks` work-groups of 512 threads (size it to one
+ * per CU), work-group b reading bytes 65536 b .. 65536 b + 65535 of buf
+ * `iters` times, with 16-byte loads into registers (dma == 0, eight in
+ * flight per thread) or with direct-to-LDS 16-byte loads (dma != 0).  With
+ * blocks x 64 KB within the L2s the slices stay resident after the first
+ * pass.  Writes cycles[b] = shader-clock cycles of work-group b's loop (so
+ * iters x 65536 / cycles[b] is bytes per cycle for that CU) and one 32-bit
+ * value per wave to out[0 .. 8 * blocks - 1] (kept so nothing is elided).
+ * buf: 65536 * blocks bytes, 16-byte aligned.                               */
+int32_t mla_bench_cu_read(const void* buf, int32_t blocks, int32_t iters, int32_t dma, uint32_t* out,
+                          uint64_t* cycles, hipStream_t stream);
+
 /* Shader clock: one wave spins `spins` dependent integer steps between two
  * reads of the shader-clock counter and of the constant 100 MHz counter;
  * writes out[0] = shader cycles, out[1] = 100 MHz ticks, out[2] = a value of

@@ -62,6 +62,7 @@ SIGNATURES = {
     "mla_bench_stream_read": (C.c_int32, [_P, C.c_int64, _P, C.c_int32, _P]),
     "mla_bench_mfma_loop": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, _P, _P]),
     "mla_bench_clock_probe": (C.c_int32, [C.c_int32, _P, _P]),
+    "mla_bench_cu_read": (C.c_int32, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P]),
     "mla_last_hip_error": (C.c_int32, []),
 }
 

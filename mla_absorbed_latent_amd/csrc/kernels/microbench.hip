@@ -6,6 +6,10 @@
 //     read bandwidth; one sum per work-group is written so nothing is elided);
 //   * mfma_loop: independent chains of v_mfma_f32_32x32x16_{f16,bf16} on
 //     register operands (matrix-core throughput with no memory traffic);
+//   * cu_read: one 512-thread work-group per CU reads its own 64 KB slice over
+//     and over (L2-resident when the slices fit), with plain 16-byte loads or
+//     with direct-to-LDS loads, timing itself with the shader-clock counter:
+//     the bytes a CU takes in per cycle from L2 on either path;
 //   * clock_probe: one wave reads the shader-clock counter (s_memtime) and the
 //     constant 100 MHz counter (s_memrealtime) around a fixed spin, giving the
 //     shader clock over that interval.
@@ -72,6 +76,48 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Work-group b reads slice b (4,096 chunks of 16 B) iters times.  Plain: each
+// thread keeps eight 16-byte loads in flight (its chunks t + 512 k, rotated by
+// 64 per pass so that no load is hoisted out of the loop) and folds them into a
+// sum.  Direct-to-LDS: wave w copies 1 KB segments w + 8 k of the slice into
+// the work-group's 64 KB of LDS, waiting each second pass until one pass's
+// loads are left in flight.  cycles[b] = shader cycles of the loop.
+__global__ __launch_bounds__(512, 1) void cu_read_kernel(const u32x4* __restrict__ buf, int iters, int dma,
+                                                         uint32_t* __restrict__ out, uint64_t* __restrict__ cycles) {
+  __shared__ __attribute__((aligned(1024))) char lds[65536];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const u32x4* p = buf + (int64_t)blockIdx.x * 4096;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if (dma) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int seg = wave + 8 * k;
+        __builtin_amdgcn_global_load_lds(p + 64 * seg + lane, (__attribute__((address_space(3))) void*)(lds + 1024 * seg),
+                                         16, 0, 0);
+      }
+      if (it & 1) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));   // vmcnt(8)
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));                              // vmcnt(0)
+  } else {
+    for (int it = 0; it < iters; ++it) {
+      u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + ((512 * k + (int)threadIdx.x + 64 * it) & 4095));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += v[k];
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  __syncthreads();
+  acc[0] += *reinterpret_cast<const uint32_t*>(lds + 4 * threadIdx.x);
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  if (lane == 0) out[(int64_t)blockIdx.x * 8 + wave] = x;
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
 __global__ __launch_bounds__(64) void clock_probe_kernel(int spins, uint64_t* __restrict__ out) {
   const uint64_t c0 = __builtin_amdgcn_s_memtime();
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
@@ -116,6 +162,16 @@ int32_t mla_bench_mfma_loop(int32_t bf16, int32_t iters, int32_t blocks, float* 
   if (e != hipSuccess) return (int32_t)e;
   if (bf16) hipLaunchKernelGGL(mla::mfma_loop_kernel<true>, dim3(blocks), dim3(256), 0, stream, iters, out);
   else hipLaunchKernelGGL(mla::mfma_loop_kernel<false>, dim3(blocks), dim3(256), 0, stream, iters, out);
+  return (int32_t)hipGetLastError();
+}
+
+int32_t mla_bench_cu_read(const void* buf, int32_t blocks, int32_t iters, int32_t dma, uint32_t* out,
+                          uint64_t* cycles, hipStream_t stream) {
+  if (!buf || !out || !cycles || blocks <= 0 || iters <= 0 || ((uintptr_t)buf & 15)) return (int32_t)hipErrorInvalidValue;
+  hipError_t e = mla::check_gfx950();
+  if (e != hipSuccess) return (int32_t)e;
+  hipLaunchKernelGGL(mla::cu_read_kernel, dim3(blocks), dim3(512), 0, stream, static_cast<const mla::u32x4*>(buf),
+                     iters, dma ? 1 : 0, out, cycles);
   return (int32_t)hipGetLastError();
 }
 
