@@ -834,6 +834,29 @@ struct LoaderBf16Wide {
       for (int k = 0; k < 9; ++k)
         *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = bf16x8_to_f16x8(r[9 * p + k]);
   }
+  // commit() and then issue() of the next tile, interleaved: each chunk's
+  // registers are reloaded right after they are stored, so that the loads
+  // leave while the rest of the tile is converted (a wave that issues them in
+  // one burst stalls while the CU's load queue is full).
+  template <int I>
+  __device__ __forceinline__ void chunk(char* dst, const uint8_t* src0, const uint8_t* src1) {
+    constexpr int p = I / 9, k = I % 9;
+    *reinterpret_cast<u32x4*>(dst + 32 * p * kRowLds + 128 * k) = bf16x8_to_f16x8(r[I]);
+    __builtin_amdgcn_sched_barrier(0);     // the reload may not overtake the conversion of the same registers
+    asm_ld16_nt<128 * k>(r[I], p == 0 ? src0 : src1);
+    if constexpr (I + 1 < 18) chunk<I + 1>(dst, src0, src1);
+  }
+  __device__ __forceinline__ void commit_issue(char* lds_buf, const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = ltid<kTid0>() >> 3;
+    const uint8_t* src[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = page >= 0 && t0 + 32 * p + tok < t_end;
+      src[p] = page_base(a, page, ok, kBlock * kRowBytesBf16) + ((t0 % kBlock) + 32 * p + tok) * kRowBytesBf16 +
+               16 * (ltid<kTid0>() & 7);
+    }
+    chunk<0>(lds_buf + swz<kSwz>(tok, ltid<kTid0>() & 7), src[0], src[1]);
+  }
 };
 
 // INT8 (page: [64][576] codes | [64][16] f32 latent scales | [64][8] f32 key
@@ -920,6 +943,27 @@ struct LoaderInt8Wide {
     commit_piece<6>(d0, d1, upper);
     commit_piece<7>(d0, d1, upper);
     commit_piece<8>(d0, d1, upper);
+  }
+  // commit() and then issue() of the next tile, interleaved (as LoaderBf16Wide):
+  // each piece's codes are reloaded right after it is converted and stored; the
+  // scales, which every piece uses, last.  The loads keep issue()'s order.
+  template <int I>
+  __device__ __forceinline__ void piece(char* d0, char* d1, bool upper, const uint8_t* codes) {
+    commit_piece<I>(d0, d1, upper);
+    __builtin_amdgcn_sched_barrier(0);     // the reload may not overtake the conversion of the same registers
+    asm_ld16_nt<64 * I>(c[I], codes);
+    if constexpr (I + 1 < 9) piece<I + 1>(d0, d1, upper, codes);
+  }
+  __device__ __forceinline__ void commit_issue(char* lds_buf, const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int tok = wide_tok<kTid0>(), c4 = ltid<kTid0>() & 3;
+    const bool ok = page >= 0 && t0 + tok < t_end;
+    const int row = (t0 % kBlock) + tok;
+    const uint8_t* pg = page_base(a, page, ok, kPage);
+    piece<0>(lds_buf + swz<kSwz>(tok, 2 * c4), lds_buf + swz<kSwz>(tok, 2 * c4 + 1), c4 >= 2, pg + row * 576 + 16 * c4);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kTok1) asm_ld4<0>(st, pg + 64 * 576 + row * 4);
+    else asm_ld16<0>(sv, pg + 64 * 576 + row * 64 + 16 * c4);
+    asm_ld8<0>(ks, pg + kKeyScales + row * 32 + 8 * c4);
   }
 };
 
@@ -1642,6 +1686,20 @@ constexpr int kQ16Reg = 10, kQ16Lds = kDk / 32 - kQ16Reg;
 // compute waves work on tile s, and then issue the loads of tile s + 3.  Each
 // SIMD runs one wave of each kind and interleaves them, so the staging work and
 // the compute overlap, and every tile's loads have two tile steps to arrive.
+// A staging step's store of one tile and load of the next: interleaved by the
+// loader when it provides commit_issue, else one after the other.
+template <class L>
+__device__ __forceinline__ auto stage_commit_issue(L& ld, char* buf, const DecodeArgs& a, int64_t page, int t0,
+                                                   int t_end, int) -> decltype(ld.commit_issue(buf, a, page, t0, t_end)) {
+  return ld.commit_issue(buf, a, page, t0, t_end);
+}
+template <class L>
+__device__ __forceinline__ void stage_commit_issue(L& ld, char* buf, const DecodeArgs& a, int64_t page, int t0,
+                                                   int t_end, long) {
+  ld.commit(buf);
+  ld.issue(a, page, t0, t_end);
+}
+
 // Staging waves of decode_h16: the same segment loop and barriers as the compute
 // waves.  Stage (s + 1) % 2 holds tile s + 1 (written at step s, then reloaded
 // with tile s + 3); the other holds tile s + 2.
@@ -1674,8 +1732,7 @@ __device__ __forceinline__ void h16_stage(const DecodeArgs& a, int b, int t_begi
       const int next_page = s + 3 < n_tiles ? ptab[s + 3] : -1;
       wait_vm<Loader::kLoads>();           // the other loader's tile stays in flight
       ldn.settle_all();
-      ldn.commit(lds + ((s + 1) & 1) * kBuf16);
-      ldn.issue(a, next_page, seg0 + (s + 3) * kTile16, seg1);
+      stage_commit_issue(ldn, lds + ((s + 1) & 1) * kBuf16, a, next_page, seg0 + (s + 3) * kTile16, seg1, 0);
     };
     // Pairs of steps (an odd tile count gets one idle step, matched by an extra
     // barrier in the compute waves).
