@@ -1134,6 +1134,54 @@ struct LoaderInt8cWide {
     *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
     *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
   }
+  // commit() and then issue() of the next tile, interleaved (as LoaderInt8Wide):
+  // the channel scales are taken into registers first, each code row is
+  // reloaded right after it is stored, then the scales and the RoPE key.  The
+  // loads keep issue()'s order.
+  template <int M>
+  __device__ __forceinline__ void row(char* lds_buf, const half2v (&s2)[8], const DecodeArgs& a, int64_t page, int t0,
+                                      int t_end) {
+    const int lt = ltid<kTid0>(), p = lt & 31, tok0 = 8 * (lt >> 5);
+    const half2v bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    uint32_t h[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t u = c[M][d] ^ 0x80808080u;
+      const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+      h[2 * d] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, lo) + bias) * s2[2 * d]);
+      h[2 * d + 1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, hi) + bias) * s2[2 * d + 1]);
+    }
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok0 + M, 2 * p)) = u32x4{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok0 + M, 2 * p + 1)) = u32x4{h[4], h[5], h[6], h[7]};
+    __builtin_amdgcn_sched_barrier(0);     // the reload may not overtake the conversion of the same registers
+    asm_ld16_nt<0>(c[M], page_base(a, page, page >= 0 && t0 + tok0 + M < t_end, kPageInt8c) + (tok0 + M) * 512 + 16 * p);
+    if constexpr (M + 1 < 8) row<M + 1>(lds_buf, s2, a, page, t0, t_end);
+  }
+  __device__ __forceinline__ void commit_issue(char* lds_buf, const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int lt = ltid<kTid0>(), p = lt & 31, tg = lt >> 5;
+    half2v s2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s2[j] = half2v{(_Float16)sv[j >> 1][2 * (j & 1)], (_Float16)sv[j >> 1][2 * (j & 1) + 1]};
+    row<0>(lds_buf, s2, a, page, t0, t_end);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* sc = page_base(a, page, page >= 0 && t0 + 32 * (tg >> 2) < t_end, kPageInt8c) + kI8cScales +
+                        (tg >> 2) * 2048 + 64 * p;
+    asm_ld16<0>(sv[0], sc);
+    asm_ld16<16>(sv[1], sc);
+    asm_ld16<32>(sv[2], sc);
+    asm_ld16<48>(sv[3], sc);
+    const int ktok = lt >> 2, kq = lt & 3;
+    const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
+    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(ktok, 64 + 2 * kq + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* kp = page_base(a, page, page >= 0 && t0 + ktok < t_end, kPageInt8c);
+    asm_ld16_nt<0>(kc, kp + kI8cKeyCodes + ktok * 64 + 16 * kq);
+    asm_ld8<0>(ks, kp + kI8cKeyScales + ktok * 32 + 8 * kq);
+  }
 };
 
 // The open block of the per-channel INT8 format: latent rows in bf16, channels
@@ -1192,6 +1240,30 @@ struct LoaderInt8cOpenWide {
     const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
     *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
     *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4 + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+  }
+  // commit() and then issue() of the next tile, interleaved (as LoaderBf16Wide).
+  template <int I>
+  __device__ __forceinline__ void chunk(char* lds_buf, const uint8_t* src) {
+    const int tok = ltid<kTid0>() >> 2, c4 = ltid<kTid0>() & 3;
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 16 * c4 + I)) = bf16x8_to_f16x8(v[I]);
+    __builtin_amdgcn_sched_barrier(0);     // the reload may not overtake the conversion of the same registers
+    asm_ld16_nt<16 * I>(v[I], src);
+    if constexpr (I + 1 < 16) chunk<I + 1>(lds_buf, src);
+  }
+  __device__ __forceinline__ void commit_issue(char* lds_buf, const DecodeArgs& a, int64_t page, int t0, int t_end) {
+    const int lt = ltid<kTid0>(), tok = lt >> 2, c4 = lt & 3;
+    const bool ok = page >= 0 && t0 + tok < t_end && t0 + tok >= t_lo;
+    const uint8_t* pg = page_base(a, page, ok, kPageInt8c);
+    chunk<0>(lds_buf, pg + (c4 < 2 ? tok * 512 + 256 * c4 : kI8cOverflow + (tok % 32) * 512 + 256 * (c4 - 2)));
+    __builtin_amdgcn_sched_barrier(0);
+    const _Float16 k0 = (_Float16)ks[0], k1 = (_Float16)ks[1];
+    const u32x2 a0 = int8x4_to_f16_perm(kc[0], half2v{k0, k0}), a1 = int8x4_to_f16_perm(kc[1], half2v{k0, k0});
+    const u32x2 b0 = int8x4_to_f16_perm(kc[2], half2v{k1, k1}), b1 = int8x4_to_f16_perm(kc[3], half2v{k1, k1});
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *reinterpret_cast<u32x4*>(lds_buf + swz_chunk<kSwz>(tok, 64 + 2 * c4 + 1)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+    __builtin_amdgcn_sched_barrier(0);
+    asm_ld16_nt<0>(kc, pg + kI8cKeyCodes + tok * 64 + 16 * c4);
+    asm_ld8<0>(ks, pg + kI8cKeyScales + tok * 32 + 8 * c4);
   }
 };
 
