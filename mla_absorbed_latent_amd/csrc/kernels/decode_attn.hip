@@ -2640,12 +2640,15 @@ struct ValuesV2 {
 struct SegV2 {
   int seg0, seg1, n_tiles;
 };
-__device__ __forceinline__ SegV2 v2_segment(const DecodeArgs& a, const ItemRange& it, int seg0, int32_t* ptab) {
+// filled: the table already holds this segment (the kernel's prologue fills
+// the first one); the two barriers are passed either way.
+__device__ __forceinline__ SegV2 v2_segment(const DecodeArgs& a, const ItemRange& it, int seg0, int32_t* ptab,
+                                            bool filled = false) {
   SegV2 sg;
   sg.seg0 = seg0;
   sg.seg1 = seg0 + min(it.t_end - seg0, kSegPages * kBlock);
   __syncthreads();                         // earlier users of the buffers and the table are done
-  fill_ptab(a, it.b, sg.seg0, sg.seg1, ptab);
+  if (!filled) fill_ptab(a, it.b, sg.seg0, sg.seg1, ptab);
   __syncthreads();
   sg.n_tiles = (sg.seg1 - sg.seg0 + kTile128 - 1) / kTile128;
   return sg;
@@ -2664,7 +2667,7 @@ __device__ __forceinline__ void v2_score_pass(const DecodeArgs& a, const ItemRan
                                               float& l_sum, bool& overflow) {
   const char* qimg = qtail + qtail2_off(w, 0, 32 * L.g + L.hl);
   for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
-    const SegV2 sg = v2_segment(a, it, seg0, ptab);
+    const SegV2 sg = v2_segment(a, it, seg0, ptab, kMode == 0 && seg0 == it.t_begin);
     StageA sa;
     sa.begin(a, v2_page(sg, ptab, 0), sg.seg0, sg.seg1);
     sa.load_all();
@@ -2707,7 +2710,7 @@ __device__ __forceinline__ void v2_value_pass(const DecodeArgs& a, const ItemRan
                                               const char* pbuf, int32_t* ptab, const H128Lane& L, int w,
                                               floatx16 (&ob)[12]) {
   for (int seg0 = it.t_begin; seg0 < it.t_end; seg0 += kSegPages * kBlock) {
-    const SegV2 sg = v2_segment(a, it, seg0, ptab);
+    const SegV2 sg = v2_segment(a, it, seg0, ptab, kMode == 0 && seg0 == it.t_begin);
     StageB sb;
     sb.begin(a, v2_page(sg, ptab, 0), sg.seg0, sg.seg1);
     sb.load_all();
@@ -2764,18 +2767,32 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
   const int lane = threadIdx.x & 63, hl = lane & 31, g = lane >> 5;
   const H128Lane L = h128_lane();
 
-  // Q^T k-steps from kQReg2 on, all heads, to LDS: thread -> head tid / 4 and the
-  // 16-byte chunks c = tid % 4 + 4 i of its row's tail (chunk c is k-step
-  // kQReg2 + c / 2, lane group c % 2).
-  {
+  // Prologue, as one memory round trip: the Q^T k-steps from kQReg2 on (all
+  // heads, to LDS: thread -> head tid / 4 and the 16-byte chunks c = tid % 4 + 4 i
+  // of its row's tail; chunk c is k-step kQReg2 + c / 2, lane group c % 2), the
+  // score waves' Q^T registers (loaded just before this, in their branch), and
+  // the page table of the item's first segment (the first segment of pass 0
+  // then skips its fill) are all requested before any of them is used.
+  auto prologue = [&]() {
     const int hr = threadIdx.x >> 2;
     const uint16_t* qr = a.q_abs + ((int64_t)it.b * 128 + hr) * kDk + 16 * kQReg2;
+    u32x4 qt[2 * kQTail2 / 4];
+#pragma unroll
+    for (int i = 0; i < 2 * kQTail2 / 4; ++i) qt[i] = ld16(qr + 8 * ((threadIdx.x & 3) + 4 * i));
+    const int seg1 = it.t_begin + min(it.t_end - it.t_begin, kSegPages * kBlock);
+    const int n0 = (seg1 - it.t_begin + kBlock - 1) / kBlock;          // <= kSegPages = 2 x 512
+    const int i0 = threadIdx.x, i1 = threadIdx.x + 512;
+    const int32_t p0 = i0 < n0 ? (int32_t)page_of(a, it.b, it.t_begin + i0 * kBlock) : -1;
+    const int32_t p1 = i1 < n0 ? (int32_t)page_of(a, it.b, it.t_begin + i1 * kBlock) : -1;
 #pragma unroll
     for (int i = 0; i < 2 * kQTail2 / 4; ++i) {
       const int c = (threadIdx.x & 3) + 4 * i;
-      *reinterpret_cast<u32x4*>(qtail + qtail2_off(hr >> 5, c >> 1, (hr & 31) + 32 * (c & 1))) = ld16(qr + 8 * c);
+      *reinterpret_cast<u32x4*>(qtail + qtail2_off(hr >> 5, c >> 1, (hr & 31) + 32 * (c & 1))) = qt[i];
     }
-  }
+    if (i0 < n0) ptab[i0] = p0;
+    if (i1 < n0) ptab[i1] = p1;
+  };
+  static_assert(kSegPages <= 2 * 512, "the prologue fills the first segment's table with two entries per thread");
   float m_ref = -INFINITY, l_sum = 0.f;
   bool overflow = false;
   float* red = reinterpret_cast<float*>(pbuf);
@@ -2785,6 +2802,7 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
     const uint16_t* qp = a.q_abs + ((int64_t)it.b * 128 + 32 * w + hl) * kDk + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kQReg2; ++ks) q[ks] = __builtin_bit_cast(half8, ld16(qp + 16 * ks));
+    prologue();
     wait_vm<0>();                          // the Q loads retire before the tile loop's loads are issued
     floatx16 oa[4];
 #pragma unroll
@@ -2813,6 +2831,7 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
     if (g == 0)
       a.lse_part[(int64_t)it.out_row * 128 + 32 * w + hl] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    prologue();
     wait_vm<0>();
     floatx16 ob[12];
 #pragma unroll
