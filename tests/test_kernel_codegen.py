@@ -106,6 +106,27 @@ def test_prompt_path_kernels_use_no_scratch(src, tmp_path):
         assert int(size) == 0, (name, size)
 
 
+def test_expansion_keeps_stages_in_flight(tmp_path):
+    """The K/V expansion keeps three 32-channel stages of direct-to-LDS loads in
+    flight: each stage waits only until the two later stages' loads (4 a wave
+    each) are left, before a bare s_barrier.  A workgroup fence (as in
+    __syncthreads) would add vmcnt(0) before every barrier and drain the
+    pipeline with every parity test still passing; so each of the two stage
+    sequences (the K_nope and the V^T instance) must wait vmcnt(8) 14 times,
+    then vmcnt(4) and vmcnt(0), and nothing else."""
+    out = str(tmp_path / "prefill.s")
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I" + KDIR, "-I" + os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-o", out, os.path.join(KDIR, "prefill.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    lines = open(out).read().split("\n")
+    st = next(i for i, l in enumerate(lines) if "expand_kv_kernel" in l and re.match(r"^_Z\S+:", l))
+    en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
+    waits = [int(m.group(1)) for l in lines[st:en] for m in [_WAIT_VM.search(l)] if m]
+    assert waits == ([8] * 14 + [4, 0]) * 2, waits
+    assert sum("s_barrier" in l for l in lines[st:en]) == 32
+
+
 _VMEM = re.compile(r"^\s*(global_load|global_store|buffer_load|buffer_store|global_atomic)\w*\s+(v\[(\d+):(\d+)\]|v(\d+))")
 _WAIT_VM = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
 _VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
