@@ -2536,15 +2536,25 @@ struct ScoresV2 {
   }
 };
 
-// Scores and softmax of one tile for a score wave (modes as h128_scores).
+// Maximum over lanes l and l ^ 32, within the VALU: v_permlane32_swap of x with
+// itself gives the lower half-wave in both halves of its first result and the
+// upper half-wave in both halves of its second.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+
+// Scores and softmax of one tile for a score wave (modes as h128_scores).  The
+// maximum is taken over the unscaled scores and scaled once (scale_log2 > 0, so
+// it is the maximum of the scaled scores), and the scale goes into the
+// exponent's argument as one fused multiply-add.
 template <int kMode>
 __device__ __forceinline__ void v2_scores(const char* buf, const char* qtail, const H128Lane& L,
                                           const half8 (&q)[kQReg2], float& m_ref, float& l_sum,
                                           bool& overflow, int t0, int t_end, bool page_ok, float scale_log2,
                                           half8 (&p)[2]) {
   floatx16 sacc = ScoresV2<3>{buf, qtail, L, q}.run();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sacc[r] *= scale_log2;
   if (!page_ok || t0 + kTile128 > t_end) {          // partial tile: mask the missing rows
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -2555,7 +2565,7 @@ __device__ __forceinline__ void v2_scores(const char* buf, const char* qtail, co
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-  mx = wave_max_xor(mx, 32);               // lanes l and l^32 hold the same head
+  mx = max_xor32(mx) * scale_log2;         // lanes l and l^32 hold the same head
   if (kMode == 1) {
     m_ref = fmaxf(m_ref, mx);
     return;
@@ -2568,7 +2578,7 @@ __device__ __forceinline__ void v2_scores(const char* buf, const char* qtail, co
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float e = __builtin_amdgcn_exp2f(sacc[r] - m_use);
+    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_use));
     psum += e;
     p[r >> 3][r & 7] = (_Float16)e;
   }
@@ -2734,30 +2744,45 @@ __device__ __forceinline__ void v2_value_pass(const DecodeArgs& a, const ItemRan
   }
 }
 
-// O^T accumulators (feature block base fb0 + f, head group hg) normalised by
-// 1 / l of each head and stored as fp16 rows of o_part, straight from the
-// accumulator layout (lane: head 32 hg + hl, features 8 (r / 4) + 4 g + r % 4).
+// The epilogue stages the normalised O^T of all 128 heads in LDS as fp16 rows
+// (head h: 1 KB at 1024 h, its 16-byte chunk c at 16 (c ^ (h & 15)) so that the
+// accumulators' writes spread over the banks), then the work-group stores whole
+// rows of o_part: store k of wave v writes row 8 k + v, one 16-byte chunk a lane.
+constexpr int kORows = 128 * 1024;
 template <int kN>
-__device__ __forceinline__ void v2_store(const DecodeArgs& a, const ItemRange& it, const floatx16 (&o)[kN],
-                                         int feat0, const float (&inv)[4], int hl, int g) {
+__device__ __forceinline__ void v2_stage_o(char* orow, const floatx16 (&o)[kN], int feat0, const float (&inv)[4],
+                                           int hl, int g) {
 #pragma unroll
   for (int i = 0; i < kN; ++i) {
-    const int f = i / 4, hg = i % 4;
-    uint16_t* op = a.o_part + ((int64_t)it.out_row * 128 + 32 * hg + hl) * kDc + feat0 + 32 * f + 4 * g;
+    const int f = i / 4, hg = i % 4, h = 32 * hg + hl;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const floatx4 x = floatx4{o[i][4 * rr], o[i][4 * rr + 1], o[i][4 * rr + 2], o[i][4 * rr + 3]} * inv[hg];
-      *reinterpret_cast<half4*>(op + 8 * rr) = __builtin_convertvector(x, half4);   // round to nearest even
+      const int c = (feat0 + 32 * f + 8 * rr) >> 3;
+      *reinterpret_cast<half4*>(orow + 1024 * h + 16 * (c ^ (h & 15)) + 8 * g) =
+          __builtin_convertvector(x, half4);   // round to nearest even
     }
+  }
+}
+__device__ __forceinline__ void v2_store_rows(const DecodeArgs& a, const ItemRange& it, const char* orow) {
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
+  uint16_t* dst = a.o_part + (int64_t)it.out_row * 128 * kDc;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int h = 8 * k + v;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(orow + 1024 * h + 16 * (lane ^ (h & 15)));
+    *reinterpret_cast<u32x4*>(dst + h * kDc + 8 * lane) = x;
   }
 }
 
 __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds0[kBuf128];
-  __shared__ __attribute__((aligned(16))) char lds1[kBuf128];
-  __shared__ __attribute__((aligned(16))) char pbuf[kPBuf];
-  __shared__ __attribute__((aligned(16))) char qtail[kQTail2Bytes];
-  __shared__ int32_t ptab[kSegPages];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBuf128 + kPBuf + kQTail2Bytes + 4 * kSegPages];
+  char* const lds0 = smem;
+  char* const lds1 = smem + kBuf128;
+  char* const pbuf = smem + 2 * kBuf128;
+  char* const qtail = pbuf + kPBuf;
+  int32_t* const ptab = reinterpret_cast<int32_t*>(qtail + kQTail2Bytes);
+  static_assert(kORows <= 2 * kBuf128 + kPBuf + kQTail2Bytes, "the O rows fit below the page table");
   ItemRange it = item_range(a);
   if (!it.ok) return;
   if (a.num_pages <= 0) it.t_end = it.t_begin;     // no page can be valid (the loaders need page 0)
@@ -2795,7 +2820,7 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
   static_assert(kSegPages <= 2 * 512, "the prologue fills the first segment's table with two entries per thread");
   float m_ref = -INFINITY, l_sum = 0.f;
   bool overflow = false;
-  float* red = reinterpret_cast<float*>(pbuf);
+  float* red = reinterpret_cast<float*>(ptab);      // the table is not read after the passes
   if (scorer) {
     // Q^T as the B operand: lane holds q_abs[b][32w + hl][16 ks + 8 g .. +7] for the first kQReg2 k-steps.
     half8 q[kQReg2];
@@ -2827,7 +2852,7 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
       const float l = red[32 * hg + hl];
       inv[hg] = l > 0.f ? 1.f / l : 0.f;
     }
-    v2_store(a, it, oa, 128 * w, inv, hl, g);
+    v2_stage_o(smem, oa, 128 * w, inv, hl, g);
     if (g == 0)
       a.lse_part[(int64_t)it.out_row * 128 + 32 * w + hl] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
@@ -2851,8 +2876,10 @@ __global__ __launch_bounds__(512, 1) void decode_h128v2(DecodeArgs a) {
       const float l = red[32 * hg + hl];
       inv[hg] = l > 0.f ? 1.f / l : 0.f;
     }
-    v2_store(a, it, ob, 128 * w + 32, inv, hl, g);
+    v2_stage_o(smem, ob, 128 * w + 32, inv, hl, g);
   }
+  __syncthreads();                         // every O row staged
+  v2_store_rows(a, it, smem);
 }
 
 // ---------------------------------------------------------------------------
