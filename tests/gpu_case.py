@@ -66,6 +66,21 @@ def run_step(run: DecodeRunner, dev: dict, seq_lens, chunk_pages: int = 0, num_c
     return out
 
 
+def lse_bound(case: mla_synth.DecodeCase, b: int):
+    """Per-head bound on |lse - lse_ref| for sequence b of a bf16 cache: the scores
+    differ from the oracle's by the fp16 rounding of the absorbed query (at most
+    2^-11 relative per element) and by fp32 accumulation, both within
+    scale * 2^-10 * sum_c |q~_hc| |k_tc| for every token t, and a log-sum-exp moves
+    by no more than its largest argument does."""
+    c_bits, r_bits = case.seq_cache(b)
+    if c_bits.shape[0] == 0:
+        return np.zeros(case.H)
+    keys = np.abs(np.concatenate([mla_ref.bf16_to_f64(c_bits), mla_ref.bf16_to_f64(r_bits)], axis=1))
+    q = np.concatenate([mla_ref.absorb_q(mla_ref.bf16_to_f64(case.q_nope[b])[None], mla_ref.bf16_to_f64(case.w_uk))[0],
+                        mla_ref.bf16_to_f64(case.q_pe[b])], axis=1)
+    return case.softmax_scale * 2.0 ** -10 * (np.abs(q) @ keys.T).max(axis=1)
+
+
 def oracle_seq(case: mla_synth.DecodeCase, b: int, cache_dtype: int = 0):
     """fp64 oracle for sequence b: (out [H,128], lse [H], o_lat [H,512])."""
     c_bits, r_bits = case.seq_cache(b)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import mla_synth
-from gpu_case import (DEV, MAX_REL, MEAN_REL, errors, oracle_seq, run_step, to_dev_bits, upload)
+from gpu_case import (DEV, MAX_REL, MEAN_REL, errors, lse_bound, oracle_seq, run_step, to_dev_bits, upload)
 from mla_absorbed_latent_amd import api
 from oracle import mla_ref, quant
 
@@ -87,7 +87,11 @@ def test_decode_small(H, lens, chunk, paging):
         assert mx <= MAX_REL and mean <= MEAN_REL, (b, mx, mean)
         mx, mean = errors(o_lat[b], ref_olat)
         assert mx <= MAX_REL and mean <= MEAN_REL, ("o_lat", b, mx, mean)
-        assert np.max(np.abs(lse[b] - ref_lse)) <= 1e-2 * max(1.0, np.max(np.abs(ref_lse)))
+        if not np.isfinite(ref_lse).all():     # an empty sequence: -inf for every head
+            assert np.all(np.isneginf(lse[b])) and np.all(np.isneginf(ref_lse))
+            continue
+        tol = lse_bound(case, b) + 1e-5 * np.maximum(1.0, np.abs(ref_lse))
+        assert np.all(np.abs(lse[b] - ref_lse) <= tol), ("lse", b, np.max(np.abs(lse[b] - ref_lse) / tol))
 
 
 QUANT_DECODE_READY = True
@@ -157,7 +161,8 @@ def test_empty_sequence_and_invalid_pages(H):
     out = run_step(run, dev, lens, chunk_pages=1).float().cpu().numpy()
     assert np.all(out[0] == 0) and np.all(np.isneginf(run.lse[0].cpu().numpy()))
     ref1, _, _ = oracle_seq(case, 1)
-    assert errors(out[1], ref1)[1] <= MEAN_REL
+    mx, mean = errors(out[1], ref1)
+    assert mx <= MAX_REL and mean <= MEAN_REL
     # sequence 2 with only tokens 0..63 and 128..129 visible
     c_bits, r_bits = case.seq_cache(2)
     keep = np.r_[0:64, 128:130]
