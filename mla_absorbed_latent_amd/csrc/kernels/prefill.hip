@@ -28,6 +28,17 @@ __device__ __forceinline__ floatx4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48, within the VALU: each
+// v_permlane*_swap of x with itself gives, in its two results, the two lanes
+// of every pair (l, l ^ 16) or (l, l ^ 32).
+__device__ __forceinline__ float max_xor16_32(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1])));
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -330,12 +341,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int u = 0; u < kU; ++u) s[u][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    u32x4 a_cur = kfrag(0);
+    constexpr int kKPf = 3;                            // K fragments read ahead of their products
+    u32x4 a_pf[kKPf];
+#pragma unroll
+    for (int d = 0; d < kKPf; ++d) a_pf[d] = kfrag(d);
 #pragma unroll
     for (int idx = 0; idx < 24; ++idx) {
       const int kt = idx / 6, ks = idx % 6;
-      const u32x4 a = a_cur;
-      if (idx + 1 < 24) a_cur = kfrag(idx + 1);
+      const u32x4 a = a_pf[idx % kKPf];
+      if (idx + kKPf < 24) a_pf[idx % kKPf] = kfrag(idx + kKPf);
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         if (ks < 4)
@@ -367,8 +381,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mb = fmaxf(mb, s[u][kt][r]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      mb = max_xor16_32(mb);
       const float m_new = fmaxf(m_run[u], mb);       // finite: key 0 is in every query's range
       const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * scale_log2);
       m_run[u] = m_new;
@@ -395,16 +408,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                           pack_f16(s[u][2 * ks + 1][0], s[u][2 * ks + 1][1]),
                           pack_f16(s[u][2 * ks + 1][2], s[u][2 * ks + 1][3])};
     }
+    // V^T fragment idx = 8 ks + mt, read kVPf products ahead.
+    constexpr int kVPf = 2;
+    auto vfrag = [&](int idx) {
+      const int ks = idx / 8, d = 16 * (idx % 8) + li;
+      return *reinterpret_cast<const u32x4*>(vt_lds + d * 128 + 16 * ((4 * ks + g) ^ (d & 7)));
+    };
+    u32x4 v_pf[kVPf];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int d = 0; d < kVPf; ++d) v_pf[d] = vfrag(d);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int d = 16 * mt + li;
-        const half8 av = __builtin_bit_cast(
-            half8, *reinterpret_cast<const u32x4*>(vt_lds + d * 128 + 16 * ((4 * ks + g) ^ (d & 7))));
+    for (int idx = 0; idx < 16; ++idx) {
+      const int ks = idx / 8, mt = idx % 8;
+      const half8 av = __builtin_bit_cast(half8, v_pf[idx % kVPf]);
+      if (idx + kVPf < 16) v_pf[idx % kVPf] = vfrag(idx + kVPf);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
-      }
+      for (int u = 0; u < kU; ++u) o[u][mt] = mfma16x16x32(av, __builtin_bit_cast(half8, pb[u][ks]), o[u][mt]);
+    }
   }
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last block's idle re-load has landed
