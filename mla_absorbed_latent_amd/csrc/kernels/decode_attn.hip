@@ -1777,11 +1777,11 @@ __device__ __forceinline__ void stage_commit_issue(L& ld, char* buf, const Decod
 // with tile s + 3); the other holds tile s + 2.
 template <class Loader>
 __device__ __forceinline__ void h16_stage(const DecodeArgs& a, int b, int t_begin, int t_end, int t_lo, char* lds,
-                                          int32_t* ptab) {
+                                          int32_t* ptab, bool filled = false) {
   for (int seg0 = t_begin; seg0 < t_end; seg0 += kSegPages * kBlock) {
     const int seg1 = min(t_end, seg0 + kSegPages * kBlock);
     __syncthreads();                       // earlier users of the buffers and the table are done
-    fill_ptab(a, b, seg0, seg1, ptab);
+    if (!(filled && seg0 == t_begin)) fill_ptab(a, b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
     // Every step commits and issues unconditionally (tiles past the end load
@@ -1834,10 +1834,26 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
 
   // Q^T k-steps past kQ16Reg go to LDS (all threads), the rest to the compute
   // waves' VGPRs below.
-  for (int i = threadIdx.x; i < kQ16Lds * 64; i += blockDim.x) {
-    const int j = i >> 6, l = i & 63;
-    const uint16_t* src = a.q_abs + ((int64_t)it.b * 16 + (l & 15)) * kDk + 32 * (kQ16Reg + j) + 8 * (l >> 4);
-    *reinterpret_cast<u32x4*>(qt16 + 16 * i) = ld16(src);
+  // With one pass, the page table of its first segment is requested together
+  // with the Q^T tail (one memory round trip instead of two); that segment then
+  // skips its fill.
+  static_assert(kQ16Lds * 64 == 512 && kSegPages <= 2 * 512, "one Q^T chunk and two table entries per thread");
+  {
+    const int l = threadIdx.x & 63;
+    const u32x4 qv = ld16(a.q_abs + ((int64_t)it.b * 16 + (l & 15)) * kDk + 32 * (kQ16Reg + (threadIdx.x >> 6)) +
+                          8 * (l >> 4));
+    if constexpr (!kSplit) {
+      const int seg1 = it.t_begin + min(it.t_end - it.t_begin, kSegPages * kBlock);
+      const int n0 = (seg1 - it.t_begin + kBlock - 1) / kBlock;
+      const int i0 = threadIdx.x, i1 = threadIdx.x + 512;
+      const int32_t p0 = i0 < n0 ? (int32_t)page_of(a, it.b, it.t_begin + i0 * kBlock) : -1;
+      const int32_t p1 = i1 < n0 ? (int32_t)page_of(a, it.b, it.t_begin + i1 * kBlock) : -1;
+      *reinterpret_cast<u32x4*>(qt16 + 16 * threadIdx.x) = qv;
+      if (i0 < n0) ptab[i0] = p0;
+      if (i1 < n0) ptab[i1] = p1;
+    } else {
+      *reinterpret_cast<u32x4*>(qt16 + 16 * threadIdx.x) = qv;
+    }
   }
   if (stager) {
     wait_vm<0>();
@@ -1846,7 +1862,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
       h16_stage<Loader>(a, it.b, it.t_begin, sp.closed_end, it.t_begin, lds, ptab);
       h16_stage<OpenLoader>(a, it.b, sp.open_begin, it.t_end, sp.open_lo, lds, ptab);
     } else {
-      h16_stage<Loader>(a, it.b, it.t_begin, it.t_end, it.t_begin, lds, ptab);
+      h16_stage<Loader>(a, it.b, it.t_begin, it.t_end, it.t_begin, lds, ptab, true);
     }
     __syncthreads();                       // the two barriers of the compute waves' merge
     __syncthreads();
@@ -1880,11 +1896,11 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   for (int t4 = 0; t4 < 4; ++t4) pv_off[t4] = swz<kSwz16>(pv_row, 2 * t4 + ((hl & 3) >> 1)) + 8 * (hl & 1);
 
   // Tokens [t_begin, t_end) of the item; rows below t_lo are masked.
-  auto pass = [&](int t_begin, int t_end, int t_lo) {
+  auto pass = [&](int t_begin, int t_end, int t_lo, bool filled) {
   for (int seg0 = t_begin; seg0 < t_end; seg0 += kSegPages * kBlock) {
     const int seg1 = min(t_end, seg0 + kSegPages * kBlock);
     __syncthreads();                       // earlier users of the buffers and the table are done
-    fill_ptab(a, it.b, seg0, seg1, ptab);
+    if (!(filled && seg0 == t_begin)) fill_ptab(a, it.b, seg0, seg1, ptab);
     __syncthreads();
     const int n_tiles = (seg1 - seg0 + kTile16 - 1) / kTile16;
     // One barrier per tile, as in h16_stage: at the barrier of step s, tile s is
@@ -1961,10 +1977,10 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   };
   if constexpr (kSplit) {
     const Int8cSplit sp = int8c_split<kTile16>(a, it);
-    pass(it.t_begin, sp.closed_end, it.t_begin);
-    pass(sp.open_begin, it.t_end, sp.open_lo);
+    pass(it.t_begin, sp.closed_end, it.t_begin, false);
+    pass(sp.open_begin, it.t_end, sp.open_lo, false);
   } else {
-    pass(it.t_begin, it.t_end, it.t_begin);
+    pass(it.t_begin, it.t_end, it.t_begin, true);
   }
 
   // ---- merge the four waves (each saw a quarter of every page) ----
