@@ -1988,15 +1988,18 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   l_w += __shfl_xor(l_w, 16, 64);
   l_w += __shfl_xor(l_w, 32, 64);
   __syncthreads();                                   // all waves done with the tiles
-  float* red = reinterpret_cast<float*>(lds);        // [4][16][512] O, then [4][16] m, [4][16] l
-  float* red_m = red + 4 * 16 * kDc;
+  // [4 waves][16 heads] rows of O padded to kRed floats (the 16-byte pad puts
+  // the 16 heads a store instruction writes on distinct banks), then [4][16] m,
+  // [4][16] l.
+  constexpr int kRed = kDc + 4;
+  static_assert((4 * 16 * kRed + 128) * 4 <= 2 * kBuf16, "the merge fits in the tile buffers");
+  float* red = reinterpret_cast<float*>(lds);
+  float* red_m = red + 4 * 16 * kRed;
   float* red_l = red_m + 64;
   {
 #pragma unroll
-    for (int tile = 0; tile < 32; ++tile) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[(wave * 16 + hl) * kDc + 16 * tile + 4 * grp + r] = o[tile][r];
-    }
+    for (int tile = 0; tile < 32; ++tile)       // features 16 tile + 4 grp .. +3 of head hl
+      *reinterpret_cast<floatx4*>(red + (wave * 16 + hl) * kRed + 16 * tile + 4 * grp) = o[tile];
     if (grp == 0) {
       red_m[wave * 16 + hl] = m_run;
       red_l[wave * 16 + hl] = l_w;
@@ -2004,8 +2007,8 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
   }
   __syncthreads();
   {
-    // 16 threads per head; thread i writes 16-byte chunks i + 16 k of the head's
-    // row, so a store instruction covers 256 contiguous bytes of four rows.
+    // 16 threads per head; thread i takes features 4 i + 64 j .. +3 (j < 8), so
+    // that each read and store instruction covers contiguous bytes of four rows.
     const int head = threadIdx.x >> 4;               // 0..15
     const int ci = threadIdx.x & 15;
     float mw[4], m = -INFINITY;
@@ -2020,16 +2023,12 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* op = a.o_part + ((int64_t)it.out_row * 16 + head) * kDc;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int f = 8 * ci + 128 * k;
-      floatx4 v0 = floatx4{}, v1 = floatx4{};
+    for (int j = 0; j < 8; ++j) {
+      const int f = 4 * ci + 64 * j;
+      floatx4 v = floatx4{};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        v0 += ew[w] * *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f);
-        v1 += ew[w] * *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kDc + f + 4);
-      }
-      const half4 h0 = __builtin_convertvector(v0 * inv, half4), h1 = __builtin_convertvector(v1 * inv, half4);
-      *reinterpret_cast<half8*>(op + f) = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);   // nearest even
+      for (int w = 0; w < 4; ++w) v += ew[w] * *reinterpret_cast<const floatx4*>(red + (w * 16 + head) * kRed + f);
+      *reinterpret_cast<half4*>(op + f) = __builtin_convertvector(v * inv, half4);   // nearest even
     }
     if ((threadIdx.x & 15) == 0)
       a.lse_part[(int64_t)it.out_row * 16 + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
