@@ -1393,7 +1393,7 @@ __device__ __forceinline__ void h128_scores(const char* buf, const char* qtail, 
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-  mx = wave_max_xor(mx, 32);               // lanes l and l^32 hold the same head
+  mx = max_xor32(mx);                      // lanes l and l^32 hold the same head
   if (kMode == 1) {
     m_ref = fmaxf(m_ref, mx);
     return;
@@ -1792,10 +1792,10 @@ __device__ __forceinline__ void h16_stage(const DecodeArgs& a, int b, int t_begi
     ld0.set_lo(t_lo);
     ld1.set_lo(t_lo);
     ld0.issue(a, ptab[0], seg0, seg1);
-    wait_vm<0>();
+    ld1.issue(a, n_tiles > 1 ? ptab[1] : -1, seg0 + kTile16, seg1);
+    wait_vm<Loader::kLoads>();             // tile 0; tile 1 stays in flight
     ld0.settle_all();
     ld0.commit(lds);
-    ld1.issue(a, n_tiles > 1 ? ptab[1] : -1, seg0 + kTile16, seg1);
     ld0.issue(a, n_tiles > 2 ? ptab[2] : -1, seg0 + 2 * kTile16, seg1);
     auto stage_step = [&](int s, Loader& ldn) {
       __syncthreads();
@@ -1945,8 +1945,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16(DecodeArgs a) {
         sacc[r] = v;
         mx = fmaxf(mx, v);
       }
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
+      mx = max_xor16_32(mx);
       const bool need = mx > m_run + kTau;
       if (__ballot(need)) {
         const float m_new = need ? mx : m_run;
@@ -2341,8 +2340,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16f8(DecodeArgs a) {
           mx = fmaxf(mx, v);
         }
       }
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);           // this wave's 32 tokens, head r
+      mx = max_xor16_32(mx);               // this wave's 32 tokens, head r
       if (g == 0) xmax[w][r] = mx;
       __syncthreads();                     // X2
       const float mt = fmaxf(fmaxf(xmax[0][r], xmax[1][r]), fmaxf(xmax[2][r], xmax[3][r]));
@@ -2367,8 +2365,7 @@ __global__ __launch_bounds__(512, 1) void decode_h16f8(DecodeArgs a) {
           p[rb][i] = e * lat[rb][i];
           pm = fmaxf(pm, p[rb][i]);
         }
-      pm = wave_max_xor(pm, 16);
-      pm = wave_max_xor(pm, 32);
+      pm = max_xor16_32(pm);
       const int ep = f8_exp(pm);
       const float sp = __uint_as_float((uint32_t)(127 - ep) << 23);
       if (g == 0) xexp[w][r] = ep;
@@ -2550,15 +2547,6 @@ struct ScoresV2 {
     return sacc;
   }
 };
-
-// Maximum over lanes l and l ^ 32, within the VALU: v_permlane32_swap of x with
-// itself gives the lower half-wave in both halves of its first result and the
-// upper half-wave in both halves of its second.
-__device__ __forceinline__ float max_xor32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
-}
 
 // Scores and softmax of one tile for a score wave (modes as h128_scores).  The
 // maximum is taken over the unscaled scores and scaled once (scale_log2 > 0, so

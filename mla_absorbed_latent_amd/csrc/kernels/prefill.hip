@@ -28,17 +28,6 @@ __device__ __forceinline__ floatx4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, floatx4
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48, within the VALU: each
-// v_permlane*_swap of x with itself gives, in its two results, the two lanes
-// of every pair (l, l ^ 16) or (l, l ^ 32).
-__device__ __forceinline__ float max_xor16_32(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  u = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1])));
-  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
-}
-
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
