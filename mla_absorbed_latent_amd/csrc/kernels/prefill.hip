@@ -39,8 +39,9 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // Grid (ceil(Lp / 128), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
 // work-group computes 128 positions x the 128 output features of head h as a
 // tiled GEMM over the 512 latent channels, in 16 stages of 32 channels: a
-// stage's latent rows and weight rows (64 B each) go straight into LDS, four
-// stage buffers deep, so that three stages are in flight while one is used
+// stage's latent rows and weight rows (64 B each) go straight into LDS, three
+// stage buffers deep, so that two stages are in flight while one is used (48 KB
+// of LDS: three work-groups fit a CU)
 // (16-byte chunk c of row r at c ^ ((r >> 2) & 3): the 16 rows a fragment read
 // touches then fill the 64 banks once).  Wave (wm, wn) computes 64 positions x
 // 64 features (4 x 4 tiles of 16 x 16).  Both operands are rows of channels
@@ -61,7 +62,7 @@ constexpr int kXT = 128;                  // positions per work-group
 constexpr int kXChunk = 32;               // channels per stage
 constexpr int kXRow = kXChunk * 2;        // 64 B
 constexpr int kXBuf = 2 * kXT * kXRow;    // latent + weight rows of a stage, 16 KB
-constexpr int kXStages = 4;               // stage buffers
+constexpr int kXStages = 3;               // stage buffers
 constexpr int kXLoads = kXBuf / 1024 / 4; // 1 KB direct loads per wave per stage
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding).
@@ -122,9 +123,9 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
   // stages' included.
 #pragma unroll
   for (int kc = 0; kc < kChunks; ++kc) {
-    // stage kc's loads retire; the (up to two) later stages stay in flight
-    if (kc + 2 < kChunks) x_wait_vm<2 * kXLoads>();
-    else if (kc + 1 < kChunks) x_wait_vm<kXLoads>();
+    // stage kc's loads retire; the later stage (if any) stays in flight
+    static_assert(kXStages == 3, "one later stage in flight at each wait");
+    if (kc + 1 < kChunks) x_wait_vm<kXLoads>();
     else x_wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage kc in LDS; stage kc - 1 read
     if (kc + kXStages - 1 < kChunks) issue(kc + kXStages - 1);
@@ -150,6 +151,17 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
       }
   }
 
+  // The fp16 result tile goes out through LDS as whole rows (128 rows of
+  // 256 B: positions for K_nope, features for V^T, whose positions are in the
+  // order of vt_pos): stored straight from the accumulators, each lane wrote
+  // 8-byte pieces of 16 different rows, and those partial-line writes took
+  // most of the kernel's time.  16-byte chunk c of tile row r sits at
+  // c ^ (r & 15), so the 16 rows a store instruction touches hit distinct banks.
+  static_assert(kXT * 256 <= kXStages * kXBuf, "the output tile fits in the stage buffers");
+  __syncthreads();                                   // every wave is done with the stage buffers
+  auto tile_off = [](int r, int col) {               // col: element (fp16) index within the row
+    return r * 256 + 16 * ((col >> 3) ^ (r & 15)) + 2 * (col & 7);
+  };
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -157,16 +169,26 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
       const u32x2 o = {pack_f16(acc[a][b][0], acc[a][b][1]), pack_f16(acc[a][b][2], acc[a][b][3])};
       if constexpr (!is_v) {
         // D[feature 64 wn + 16 b + 4 g + r][position 64 wm + 16 a + li]
-        const int j = j0 + 64 * wm + 16 * a + li;
-        if (j < Lp) *reinterpret_cast<u32x2*>(k_nope + ((int64_t)h * Lp + j) * kDn + 64 * wn + 16 * b + 4 * g) = o;
+        *reinterpret_cast<u32x2*>(lds + tile_off(64 * wm + 16 * a + li, 64 * wn + 16 * b + 4 * g)) = o;
       } else {
         // D[position 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]; the four
         // positions go to their place in the key order of vt_pos
-        const int j = j0 + 64 * wm + 16 * a + 4 * g;
-        if (j < Lp)
-          *reinterpret_cast<u32x2*>(v_t + ((int64_t)h * kDn + 64 * wn + 16 * b + li) * Lp + vt_pos(j)) = o;
+        *reinterpret_cast<u32x2*>(lds + tile_off(64 * wn + 16 * b + li, vt_pos(64 * wm + 16 * a + 4 * g))) = o;
       }
     }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int r = 16 * pass + (tid >> 4), c = tid & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 256 + 16 * (c ^ (r & 15)));
+    if constexpr (!is_v) {
+      const int j = j0 + r;
+      if (j < Lp) *reinterpret_cast<u32x4*>(k_nope + ((int64_t)h * Lp + j) * kDn + 8 * c) = v;
+    } else {
+      const int j = j0 + 8 * c;                      // positions j .. j + 7 in stored order
+      if (j < Lp) *reinterpret_cast<u32x4*>(v_t + ((int64_t)h * kDn + r) * Lp + j) = v;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
