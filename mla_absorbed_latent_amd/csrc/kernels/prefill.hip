@@ -41,9 +41,14 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // tiled GEMM over the 512 latent channels, in 16 stages of 32 channels: a
 // stage's latent rows and weight rows (64 B each) go straight into LDS, three
 // stage buffers deep, so that two stages are in flight while one is used (48 KB
-// of LDS: three work-groups fit a CU)
-// (16-byte chunk c of row r at c ^ ((r >> 2) & 3): the 16 rows a fragment read
-// touches then fill the 64 banks once).  Wave (wm, wn) computes 64 positions x
+// of LDS: three work-groups fit a CU).  16-byte chunk c of row r sits at
+// c ^ ((r >> 1) & 2).  A 16-byte LDS read serves 16 lanes per cycle, lanes
+// 0-7 with 16-23 (and 8-15 with 24-31, and so on: the lanes whose bit 3 is
+// equal), so that the 8 rows and two chunk columns (g, g ^ 1) of such a lane
+// set must fill the 64 banks once: rows r and r + 4 share their banks and
+// differ in bit 1 of the chunk (the swizzle c ^ ((r >> 2) & 3) made them
+// collide, twice the cycles per fragment read; the prefill attention's
+// layouts already met this).  Wave (wm, wn) computes 64 positions x
 // 64 features (4 x 4 tiles of 16 x 16).  Both operands are rows of channels
 // with the same fragment layout, so the weight is the A operand for K_nope
 // (D[feature][position]: four consecutive features per lane and store) and the
@@ -90,7 +95,7 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
   const uint16_t* src0[kXLoads];
 #pragma unroll
   for (int i = 0; i < kXLoads; ++i) {
-    const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 2, ch = (P & 3) ^ ((row >> 2) & 3);
+    const int seg = wave + 4 * i, P = 64 * seg + lane, row = P >> 2, ch = (P & 3) ^ ((row >> 1) & 2);
     if (row < kXT) {
       const int j = j0 + row;
       src0[i] = c_kv + (int64_t)(j < L ? j : L - 1) * kDc + 8 * ch;
@@ -134,8 +139,8 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int pr = 64 * wm + 16 * t + li, wr = kXT + 64 * wn + 16 * t + li;
-      pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * (g ^ ((pr >> 2) & 3)));
-      wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * (g ^ ((wr >> 2) & 3)));
+      pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * (g ^ ((pr >> 1) & 2)));
+      wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * (g ^ ((wr >> 1) & 2)));
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
