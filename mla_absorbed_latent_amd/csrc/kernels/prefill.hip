@@ -239,25 +239,15 @@ constexpr int kBufBytes = kKBytes + kVBytes;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(const uint16_t* __restrict__ q_nope,
-                                                                const uint16_t* __restrict__ q_pe,
-                                                                const uint16_t* __restrict__ k_pe,
-                                                                const uint16_t* __restrict__ k_nope,
-                                                                const uint16_t* __restrict__ v_t, int T, int L,
-                                                                int Lp, int H, float scale_log2,
-                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
+// One query block qb of head h (the work of one work-group; see the kernel).
+__device__ __forceinline__ void prefill_qblock(const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+                                               const uint16_t* __restrict__ k_pe,
+                                               const uint16_t* __restrict__ k_nope,
+                                               const uint16_t* __restrict__ v_t, int T, int L, int Lp, int H,
+                                               float scale_log2, uint16_t* __restrict__ out,
+                                               float* __restrict__ lse, char* lds, int h, int qb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  // Work-groups are dealt to the 8 XCDs round robin by linear id.  With H a
-  // multiple of 8 (16 or 128), the k-th work-group of XCD x takes head
-  // x + 8 (k / nqb) and query block nqb - 1 - k % nqb: all query blocks of a
-  // head run on one XCD (its K/V stays in that L2), longest causal ranges first.
-  const int nqb = gridDim.x;
-  const int wg_id = blockIdx.x + nqb * blockIdx.y;
-  const int xcd = wg_id & 7, k_on_xcd = wg_id >> 3;
-  const int h = xcd + 8 * (k_on_xcd / nqb);
-  const int qb = nqb - 1 - k_on_xcd % nqb;
   const int p_first = L - T + qb * kQB;
   const int p_last = L - T + min(qb * kQB + kQB - 1, T - 1);
   const int n_blocks = p_last / 64 + 1;
@@ -464,7 +454,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+// Work-groups are dealt to the 8 XCDs round robin by linear id.  With H a
+// multiple of 8 (16 or 128), the k-th work-group of XCD x takes head
+// x + 8 (k / units) and unit k % units of it: all query blocks of a head run
+// on one XCD (its K/V stays in that L2).  Unit u is query block nqb - 1 - u
+// (longest causal ranges first), or, with kPairs (nqb even), query blocks
+// nqb - 1 - u and then u: every work-group then has the same number of key
+// blocks.  Pairs serve launches whose work-groups all fit the CUs at once
+// (16-head prompts), where the longest causal range would otherwise set the
+// time while the CUs of the short ones idle.
+template <bool kPairs>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
+    const uint16_t* __restrict__ k_nope, const uint16_t* __restrict__ v_t, int T, int L, int Lp, int H,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
+  const int units = gridDim.x;
+  const int nqb = kPairs ? 2 * units : units;
+  const int wg_id = blockIdx.x + units * blockIdx.y;
+  const int xcd = wg_id & 7, k_on_xcd = wg_id >> 3;
+  const int h = xcd + 8 * (k_on_xcd / units);
+  const int unit = k_on_xcd % units;
+  prefill_qblock(q_nope, q_pe, k_pe, k_nope, v_t, T, L, Lp, H, scale_log2, out, lse, lds, h, nqb - 1 - unit);
+  if constexpr (kPairs) {
+    __syncthreads();                       // every wave is done with the first block's tiles
+    prefill_qblock(q_nope, q_pe, k_pe, k_nope, v_t, T, L, Lp, H, scale_log2, out, lse, lds, h, unit);
+  }
+}
+
 }  // namespace
+
+constexpr int kNumCUs = 256;             // compute units of a gfx950 card (8 XCDs x 32)
 
 int64_t prefill_padded_len(int seq_len) { return ((int64_t)seq_len + 63) / 64 * 64; }
 
@@ -479,10 +499,17 @@ hipError_t launch_prefill_attn(int num_heads, float softmax_scale, const uint16_
   hipLaunchKernelGGL(expand_kv_kernel, dim3((unsigned)((Lp + kXT - 1) / kXT), num_heads, 2), dim3(256), 0, stream,
                      c_kv, w_uk,
                      w_uv, seq_len, (int)Lp, k_nope, v_t);
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((n_queries + kQB - 1) / kQB, num_heads), dim3(kThreads), 0, stream,
-                     q_nope,
-                     q_pe, k_pe, k_nope, v_t, n_queries, seq_len, (int)Lp, num_heads,
-                     softmax_scale * 1.4426950408889634f, out, lse);
+  // Pair the query blocks when the whole grid fits the CUs at once (two
+  // work-groups per CU): a CU then holds one long and one short causal range.
+  const int nqb = (n_queries + kQB - 1) / kQB;
+  const bool pairs = nqb % 2 == 0 && (int64_t)nqb * num_heads <= 2 * kNumCUs;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (pairs)
+    hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(nqb / 2, num_heads), dim3(kThreads), 0, stream, q_nope, q_pe,
+                       k_pe, k_nope, v_t, n_queries, seq_len, (int)Lp, num_heads, scale_log2, out, lse);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(nqb, num_heads), dim3(kThreads), 0, stream, q_nope, q_pe,
+                       k_pe, k_nope, v_t, n_queries, seq_len, (int)Lp, num_heads, scale_log2, out, lse);
   return hipGetLastError();
 }
 

@@ -45,8 +45,11 @@ def _check(got, ref, got_lse, ref_lse, what):
 
 
 @pytest.mark.parametrize("T,L,H", [(1, 1, 16), (26, 26, 16), (64, 64, 16), (100, 300, 16), (5, 1000, 16),
-                                   (77, 77, 128), (130, 200, 128), (1, 65, 128)])
+                                   (300, 300, 16), (512, 600, 16), (77, 77, 128), (130, 200, 128), (1, 65, 128)])
 def test_prefill_small(T, L, H):
+    """Every row against the oracle.  T = 512 (four query blocks) and T = 130 at
+    128 heads take the paired schedule (a work-group runs query blocks
+    nqb - 1 - u and u), T = 300 (three blocks) the one-block-per-work-group one."""
     case = mla_synth.prefill_chunk(T, L, H, case_id=43)
     print("prefill T=%d L=%d H=%d" % (T, L, H), flush=True)
     out, lse = _run(case)
