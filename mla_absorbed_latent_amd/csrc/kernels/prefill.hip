@@ -36,20 +36,21 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
-// Grid (ceil(Lp / 128), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
-// work-group computes 128 positions x the 128 output features of head h as a
+// Grid (ceil(Lp / 256), H, 2); z = 0 writes K_nope, z = 1 writes V^T.  A
+// work-group computes 256 positions x the 128 output features of head h as a
 // tiled GEMM over the 512 latent channels, in 16 stages of 32 channels: a
 // stage's latent rows and weight rows (64 B each) go straight into LDS, three
-// stage buffers deep, so that two stages are in flight while one is used (48 KB
-// of LDS: three work-groups fit a CU).  16-byte chunk c of row r sits at
+// stage buffers deep, so that two stages are in flight while one is used (72 KB
+// of LDS: two work-groups fit a CU).  16-byte chunk c of row r sits at
 // c ^ ((r >> 1) & 2).  A 16-byte LDS read serves 16 lanes per cycle, lanes
 // 0-7 with 16-23 (and 8-15 with 24-31, and so on: the lanes whose bit 3 is
 // equal), so that the 8 rows and two chunk columns (g, g ^ 1) of such a lane
 // set must fill the 64 banks once: rows r and r + 4 share their banks and
 // differ in bit 1 of the chunk (the swizzle c ^ ((r >> 2) & 3) made them
 // collide, twice the cycles per fragment read; the prefill attention's
-// layouts already met this).  Wave (wm, wn) computes 64 positions x
-// 64 features (4 x 4 tiles of 16 x 16).  Both operands are rows of channels
+// layouts already met this).  Wave (wm, wn) computes 128 positions x
+// 64 features (8 x 4 tiles of 16 x 16: 12 fragment reads feed 32 products;
+// with 64 x 64 per wave, 8 fed 16).  Both operands are rows of channels
 // with the same fragment layout, so the weight is the A operand for K_nope
 // (D[feature][position]: four consecutive features per lane and store) and the
 // B operand for V^T (D[position][feature]: four consecutive positions).
@@ -63,12 +64,15 @@ __device__ __forceinline__ int vt_pos(int j) {
   return (j & ~31) + 4 * (q < 4 ? 2 * q : 2 * (q - 4) + 1);
 }
 
-constexpr int kXT = 128;                  // positions per work-group
+constexpr int kXT = 256;                  // positions per work-group
+constexpr int kXF = 128;                  // output features per work-group (one head's K_nope or V)
 constexpr int kXChunk = 32;               // channels per stage
 constexpr int kXRow = kXChunk * 2;        // 64 B
-constexpr int kXBuf = 2 * kXT * kXRow;    // latent + weight rows of a stage, 16 KB
+constexpr int kXBuf = (kXT + kXF) * kXRow;  // latent + weight rows of a stage, 24 KB
 constexpr int kXStages = 3;               // stage buffers
 constexpr int kXLoads = kXBuf / 1024 / 4; // 1 KB direct loads per wave per stage
+constexpr int kXPT = kXT / 2 / 16;        // 16-position tiles per wave (8)
+constexpr int kXFT = kXF / 2 / 16;        // 16-feature tiles per wave (4)
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding).
 template <int kN>
@@ -82,14 +86,14 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
                                                uint16_t* __restrict__ v_t, char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;          // positions 64 wm.., features 64 wn..
+  const int wm = wave >> 1, wn = wave & 1;          // positions 128 wm.., features 64 wn..
   const int h = blockIdx.y;
   const int j0 = blockIdx.x * kXT;
   const uint16_t* w = w_in + (int64_t)h * kDn * kDc;
 
-  // Staging: rows 0..127 latent, 128..255 weight, 4 chunks of 16 B per row,
+  // Staging: rows 0..255 latent, 256..383 weight, 4 chunks of 16 B per row,
   // straight into LDS (global_load_lds_dwordx4: lane i of a wave instruction
-  // fills bytes 16 i .. of a 1 KB segment): 16 segments, wave w issues w + 4 i.
+  // fills bytes 16 i .. of a 1 KB segment): 24 segments, wave w issues w + 4 i.
   // Each lane loads the chunk that belongs at its slot.  Positions past L load
   // position L - 1: finite values, masked in attention.
   const uint16_t* src0[kXLoads];
@@ -112,11 +116,11 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
                                        0, 0);
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[kXPT][kXFT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kXPT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kXFT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kChunks = kDc / kXChunk;
   static_assert(kChunks >= kXStages, "the prologue fills kXStages - 1 stages");
@@ -135,57 +139,63 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage kc in LDS; stage kc - 1 read
     if (kc + kXStages - 1 < kChunks) issue(kc + kXStages - 1);
     const char* buf = lds + (kc % kXStages) * kXBuf;
-    u32x4 pf[4], wf[4];
+    u32x4 wf[kXFT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int pr = 64 * wm + 16 * t + li, wr = kXT + 64 * wn + 16 * t + li;
-      pf[t] = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * (g ^ ((pr >> 1) & 2)));
+    for (int t = 0; t < kXFT; ++t) {
+      const int wr = kXT + 64 * wn + 16 * t + li;
       wf[t] = *reinterpret_cast<const u32x4*>(buf + wr * kXRow + 16 * (g ^ ((wr >> 1) & 2)));
     }
+    // Each position fragment feeds kXFT products.
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kXPT; ++a) {
+      const int pr = 128 * wm + 16 * a + li;
+      const u32x4 pf = *reinterpret_cast<const u32x4*>(buf + pr * kXRow + 16 * (g ^ ((pr >> 1) & 2)));
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < kXFT; ++b) {
         // a: position tile, b: feature tile
         if constexpr (!is_v)
-          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[b]), __builtin_bit_cast(bf16x8, pf[a]),
+          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[b]), __builtin_bit_cast(bf16x8, pf),
                                         acc[a][b]);
         else
-          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf[a]), __builtin_bit_cast(bf16x8, wf[b]),
+          acc[a][b] = mfma16x16x32_bf16(__builtin_bit_cast(bf16x8, pf), __builtin_bit_cast(bf16x8, wf[b]),
                                         acc[a][b]);
       }
+    }
   }
 
-  // The fp16 result tile goes out through LDS as whole rows (128 rows of
-  // 256 B: positions for K_nope, features for V^T, whose positions are in the
-  // order of vt_pos): stored straight from the accumulators, each lane wrote
-  // 8-byte pieces of 16 different rows, and those partial-line writes took
-  // most of the kernel's time.  16-byte chunk c of tile row r sits at
-  // c ^ (r & 15), so the 16 rows a store instruction touches hit distinct banks.
-  static_assert(kXT * 256 <= kXStages * kXBuf, "the output tile fits in the stage buffers");
+  // The fp16 result tile goes out through LDS as whole rows: for K_nope 256
+  // position rows of 256 B, for V^T 128 feature rows of 512 B (positions in the
+  // order of vt_pos).  Stored straight from the accumulators, each lane would
+  // write 8-byte pieces of 16 different rows.  16-byte chunk c of tile row r
+  // sits at c ^ (r & 15), so the 16 rows a store instruction touches hit
+  // distinct banks.
+  constexpr int kOutRow = is_v ? 2 * kXT : 2 * kXF;  // bytes per tile row
+  static_assert(kXT * kXF * 2 <= kXStages * kXBuf, "the output tile fits in the stage buffers");
   __syncthreads();                                   // every wave is done with the stage buffers
   auto tile_off = [](int r, int col) {               // col: element (fp16) index within the row
-    return r * 256 + 16 * ((col >> 3) ^ (r & 15)) + 2 * (col & 7);
+    return r * kOutRow + 16 * ((col >> 3) ^ (r & 15)) + 2 * (col & 7);
   };
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kXPT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < kXFT; ++b) {
       const u32x2 o = {pack_f16(acc[a][b][0], acc[a][b][1]), pack_f16(acc[a][b][2], acc[a][b][3])};
       if constexpr (!is_v) {
-        // D[feature 64 wn + 16 b + 4 g + r][position 64 wm + 16 a + li]
-        *reinterpret_cast<u32x2*>(lds + tile_off(64 * wm + 16 * a + li, 64 * wn + 16 * b + 4 * g)) = o;
+        // D[feature 64 wn + 16 b + 4 g + r][position 128 wm + 16 a + li]
+        *reinterpret_cast<u32x2*>(lds + tile_off(128 * wm + 16 * a + li, 64 * wn + 16 * b + 4 * g)) = o;
       } else {
-        // D[position 64 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]; the four
+        // D[position 128 wm + 16 a + 4 g + r][feature 64 wn + 16 b + li]; the four
         // positions go to their place in the key order of vt_pos
-        *reinterpret_cast<u32x2*>(lds + tile_off(64 * wn + 16 * b + li, vt_pos(64 * wm + 16 * a + 4 * g))) = o;
+        *reinterpret_cast<u32x2*>(lds + tile_off(64 * wn + 16 * b + li, vt_pos(128 * wm + 16 * a + 4 * g))) = o;
       }
     }
   __syncthreads();
+  constexpr int kChunksPerRow = kOutRow / 16;        // 16 (K_nope) or 32 (V^T)
+  constexpr int kRowsPerPass = 256 / kChunksPerRow;
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int r = 16 * pass + (tid >> 4), c = tid & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 256 + 16 * (c ^ (r & 15)));
+  for (int pass = 0; pass < kXT * kXF * 2 / (256 * 16); ++pass) {
+    const int r = kRowsPerPass * pass + tid / kChunksPerRow, c = tid % kChunksPerRow;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kOutRow + 16 * (c ^ (r & 15)));
     if constexpr (!is_v) {
       const int j = j0 + r;
       if (j < Lp) *reinterpret_cast<u32x4*>(k_nope + ((int64_t)h * Lp + j) * kDn + 8 * c) = v;
@@ -196,7 +206,7 @@ __device__ __forceinline__ void expand_kv_body(const uint16_t* __restrict__ c_kv
   }
 }
 
-__global__ __launch_bounds__(256) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void expand_kv_kernel(const uint16_t* __restrict__ c_kv,
                                                         const uint16_t* __restrict__ w_uk,
                                                         const uint16_t* __restrict__ w_uv, int L, int Lp,
                                                         uint16_t* __restrict__ k_nope, uint16_t* __restrict__ v_t) {

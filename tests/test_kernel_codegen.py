@@ -108,11 +108,11 @@ def test_prompt_path_kernels_use_no_scratch(src, tmp_path):
 
 def test_expansion_keeps_stages_in_flight(tmp_path):
     """The K/V expansion keeps two 32-channel stages of direct-to-LDS loads in
-    flight: each stage waits only until the later stage's loads (4 a wave) are
+    flight: each stage waits only until the later stage's loads (6 a wave) are
     left, before a bare s_barrier.  A workgroup fence (as in __syncthreads)
     would add vmcnt(0) before every barrier and drain the pipeline with every
     parity test still passing; so each of the two stage sequences (the K_nope
-    and the V^T instance) must wait vmcnt(4) 15 times, then vmcnt(0), and
+    and the V^T instance) must wait vmcnt(6) 15 times, then vmcnt(0), and
     nothing else; its barriers are the 16 stages' and the two around the
     output tile staged in LDS."""
     out = str(tmp_path / "prefill.s")
@@ -124,7 +124,7 @@ def test_expansion_keeps_stages_in_flight(tmp_path):
     st = next(i for i, l in enumerate(lines) if "expand_kv_kernel" in l and re.match(r"^_Z\S+:", l))
     en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
     waits = [int(m.group(1)) for l in lines[st:en] for m in [_WAIT_VM.search(l)] if m]
-    assert waits == ([4] * 15 + [0]) * 2, waits
+    assert waits == ([6] * 15 + [0]) * 2, waits
     assert sum("s_barrier" in l for l in lines[st:en]) == (16 + 2) * 2
 
 
