@@ -15,7 +15,9 @@
 //     masked) from c_kv and W_UK / W_UV, a tiled bf16 MFMA GEMM;
 //   prefill_attn_kernel: flash attention per (128 queries, head): 4 waves of
 //     32 queries, S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16
-//     (each LDS fragment feeds two products), streaming softmax in fp32.
+//     (each LDS fragment feeds two products), streaming softmax in fp32; a
+//     work-group takes one query block, or two paired ones (a long and a
+//     short causal range) when the whole grid fits the CUs at once.
 // The operands of the attention products are fp16 (bf16 inputs widen exactly);
 // P is rounded to fp16, its fp32 sum taken before rounding.
 #include "common.h"
